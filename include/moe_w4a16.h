@@ -1,0 +1,174 @@
+/*
+ * moe_w4a16.h -- C ABI of the W4A16 routed-expert MoE layer for one MI355X (gfx950).
+ *
+ * The layer (Horizon RunMap pages):
+ *   - routed experts stored as INT4 "qpacked" weights, 256-value blocks with
+ *     one FP16 scale each; FP16 activations; no persistent expanded FP16/BF16
+ *     expert ("Horizon RunMap - architecture", table "Representation and
+ *     computation"; "horizonrunmap.com/en", section "08 / Precision &
+ *     quality": weights are converted inside the kernel as computation needs
+ *     them, with FP32 accumulation stages and explicit rounding);
+ *   - routing chooses the experts of each token at each routed layer
+ *     ("horizonrunmap.com/en", section "06 / Follow a token", step "Select
+ *     experts"); routing and other non-routed parts stay outside INT4, with
+ *     FP16 weights (section "08", paragraph "Other components");
+ *   - a resident expert is not necessarily routed, and a missing expert row
+ *     is copied host-to-device only ("Horizon RunMap - architecture",
+ *     sections "Immutable authority and miss lifecycle" and "Regimes and
+ *     executor boundaries").
+ * The pages give no formula for the router or the expert FFN.  This library
+ * implements: top-k softmax routing over FP16 router logits, a SwiGLU expert
+ * (gate, up, SiLU(gate) * up, down) and the weighted sum of the k expert
+ * outputs.
+ *
+ * Conventions for every call
+ *   - Pointers named *_dev are device pointers (hipMalloc'd or torch CUDA
+ *     tensors); the caller owns them.  FP16 tensors are passed as void*.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
+ *     only enqueue kernels on it: they are asynchronous, never synchronize,
+ *     and never allocate.
+ *   - Return value: MOE_OK or an MOE_ERR_* code.  Arguments are validated on
+ *     the host before anything is enqueued; on error nothing is enqueued and
+ *     moe_last_error() returns a message (thread-local).
+ *   - Shapes: E <= 64 experts, 1 <= k <= min(E, 8), H and I multiples of 128,
+ *     T >= 0 (T = 0 enqueues nothing and returns MOE_OK).
+ *
+ * qpacked v1 weight layout of one matrix with R rows (output features) and K
+ * columns (reduction index), R % 16 == 0, K % 128 == 0.  A weight is
+ * (code - 8) * scale; the pages fix no zero point, so codes 0..15 stand for
+ * -8..7.
+ *   nibble plane (R*K/2 bytes): 1024-byte tiles.  Tile (rg, kt) holds rows
+ *     16rg .. 16rg+15, columns 128kt .. 128kt+127, at byte
+ *     (rg*(K/128) + kt)*1024.  Within a tile, the 16-byte chunk number
+ *     16g + r holds row 16rg + r, columns 128kt + 32g .. 128kt + 32g + 31;
+ *     byte i of the chunk holds column 2i in bits 0-3 and column 2i+1 in
+ *     bits 4-7 (relative to the chunk's first column).
+ *   scale plane (R*ceil(K/256) FP16): the scale of row 16rg + r for block b
+ *     (columns 256b .. min(256b+256, K)-1; the last block of a row may hold
+ *     only 128 columns) is element (rg*ceil(K/256) + b)*16 + r.
+ * Expert row: the unit that lives in one device slot and is uploaded on a
+ *   miss.  Sections, each starting on a 256-byte boundary, in this order:
+ *   gate nibbles [I][H], up nibbles [I][H], down nibbles [H][I], gate
+ *   scales, up scales, down scales.
+ *
+ * Pair numbering: token t's j-th selected expert (j = 0..k-1, descending
+ * logit) is pair p = t*k + j.  Grouping sorts pairs by expert (stable: within
+ * an expert, ascending p); pos = pair_pos[p] is a pair's place in that order
+ * and sorted_pairs[pos] = p.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,     /* null pointer, bad shape, misaligned pointer */
+    MOE_ERR_UNSUPPORTED = 2,     /* shape outside the supported envelope */
+    MOE_ERR_WORKSPACE = 3,       /* workspace missing or too small */
+    MOE_ERR_CAPACITY = 4,        /* expert table: not enough spare rows / staging at create */
+    MOE_ERR_HIP = 5,             /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_FAULTED = 6,         /* expert table faulted by a failure after publication */
+    MOE_ERR_ABSENT_EXPERT = 7,   /* a routed expert has no published device row */
+};
+
+#define MOE_MAX_EXPERTS 64
+#define MOE_MAX_TOPK 8
+
+/* Library version (major*10000 + minor*100 + patch). */
+int moe_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Size in bytes of one qpacked v1 expert row for hidden size H and expert
+ * intermediate size I (0 if H or I is not a positive multiple of 128).
+ * off6, if not NULL, receives the byte offsets of the six sections
+ * (gate_q, up_q, down_q, gate_s, up_s, down_s). */
+size_t moe_expert_row_bytes(int H, int I, size_t *off6);
+
+/* ------------------------------------------------------------ routing
+ * moe_route: router logits, top-k softmax and token-to-expert grouping, one
+ * kernel launch.
+ *   logit[t][e] = RN32( exact sum_h x[t][h] * w_router[h][e] ) (+ bias[e])
+ *     The dot product of FP16 values is accumulated exactly (in integer
+ *     units of 2^-48) and rounded once to FP32, so the selected experts do
+ *     not depend on summation order.  bias, if given, is added in FP32.
+ *   topk_ids[t][j]: the k largest logits, descending, ties to the lower
+ *     expert index.  topk_w[t][j] = softmax over those k logits (FP32; the
+ *     weights of a token sum to 1).
+ *   expert_offsets[E+1]: exclusive prefix sum of the per-expert pair counts.
+ *   sorted_pairs[T*k], pair_pos[T*k]: the stable grouping described above.
+ *   active_list[E]: experts with at least one pair, ascending; entries past
+ *     *n_active_dev are set to -1.  n_active_dev[0]: their number.
+ *   logits_dev: FP32 [T][E] copy of the logits (bias included), or NULL.
+ * Inputs:  x_dev FP16 [T][H] row-major; w_router_dev FP16 [H][E] row-major;
+ *          bias_dev FP32 [E] or NULL.
+ * ws_dev: workspace of moe_route_workspace_size(T, H, E) bytes, 256-byte
+ *   aligned, ZERO-FILLED BEFORE ITS FIRST USE (it holds completion counters
+ *   that every call leaves at zero again).  One workspace must not be used
+ *   by two calls that can overlap.  Returns 0 for unsupported shapes.
+ * Limits: T <= 65536, H <= 4096 (bounds the exact integer accumulators). */
+size_t moe_route_workspace_size(int T, int H, int E);
+int moe_route(const void *x_dev, const void *w_router_dev, const float *bias_dev,
+              int T, int H, int E, int k,
+              float *logits_dev, int32_t *topk_ids_dev, float *topk_w_dev,
+              int32_t *expert_offsets_dev, int32_t *sorted_pairs_dev, int32_t *pair_pos_dev,
+              int32_t *active_list_dev, int32_t *n_active_dev,
+              void *ws_dev, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------ expert FFN
+ * Expert rows are addressed as rows_dev + slot_map_dev[e] * row_stride
+ * (slot_map_dev NULL means slot e for expert e).  row_stride >=
+ * moe_expert_row_bytes(H, I) and a multiple of 256; rows_dev 256-byte
+ * aligned.  A routed expert whose slot is negative is an absent expert: its
+ * pairs get zero output and *status_dev (if not NULL) is set to
+ * MOE_ERR_ABSENT_EXPERT (the library never clears it; the caller zeroes it).
+ * expert_offsets / sorted_pairs / active_list / n_active are moe_route's
+ * outputs for the same T, E, k.
+ *
+ * moe_w4a16_gateup: for every pair p = (t, j) routed to expert e, in grouped
+ *   order pos = pair_pos[p]:
+ *     g = Wg[e] x[t], u = Wu[e] x[t]            (FP32 accumulation)
+ *     h[pos][i] = RN16( silu(g_i) * u_i ),  silu(g) = g / (1 + exp(-g))
+ *   h_dev: FP16 [T*k][I] workspace (16-byte aligned).
+ * moe_w4a16_down: pair_out[pos][r] = sum_i Wd[e][r][i] * h[pos][i] (FP32).
+ *   pair_out_dev: FP32 [T*k][H].
+ * moe_w4a16_expert_ffn: gateup then down on the same stream.
+ * Weights are read as INT4 codes and converted to FP16 in registers; the
+ * per-block FP16 scale is applied to the FP32 partial sum of each block, so
+ * no expanded weight matrix is ever stored. */
+int moe_w4a16_gateup(const void *x_dev, int T, int H, int I, int E, int k,
+                     const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                     const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
+                     const int32_t *active_list_dev, const int32_t *n_active_dev,
+                     void *h_dev, int32_t *status_dev, void *stream);
+int moe_w4a16_down(int T, int H, int I, int E, int k,
+                   const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                   const int32_t *expert_offsets_dev, const int32_t *active_list_dev,
+                   const int32_t *n_active_dev, const void *h_dev, float *pair_out_dev,
+                   int32_t *status_dev, void *stream);
+int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
+                         const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                         const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
+                         const int32_t *active_list_dev, const int32_t *n_active_dev,
+                         void *h_dev, float *pair_out_dev, int32_t *status_dev, void *stream);
+
+/* ------------------------------------------------------------ combine
+ * y[t][c] = RN16( sum_{j=0..k-1} topk_w[t][j] * pair_out[pair_pos[t*k+j]][c]
+ *                 (+ shared_gate[t] * shared_out[t][c]) ), FP32, j ascending.
+ * shared_out_dev (FP32 [T][H]) and shared_gate_dev (FP32 [T]) are both NULL
+ * or both given.  y_dev: FP16 [T][H]. */
+int moe_combine(const float *pair_out_dev, const int32_t *pair_pos_dev, const float *topk_w_dev,
+                const float *shared_out_dev, const float *shared_gate_dev,
+                int T, int H, int k, void *y_dev, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_W4A16_H */

@@ -1,0 +1,48 @@
+"""Shared helpers of the parity tests (no arithmetic of the layer itself)."""
+import numpy as np
+
+# Layer-output tolerance: |got - want| <= REL * max(|want|, floor), floor = 2^-4 * max_c |want[t, c]|.
+# The relative bound 2e-3 applies after FP16 rounding of the output.  The floor
+# exists because the SwiGLU output h is rounded to FP16 before the down
+# projection: FP32 and fp64 evaluations of the same h round differently when
+# the value sits next to an FP16 rounding midpoint (about 1 element in 300),
+# and each such 1-ulp flip moves every output of that pair by |w_d| * ulp(h)
+# in absolute terms.  Outputs that are small through cancellation then see a
+# large relative change.  An FP32 model of the kernel arithmetic needs a floor
+# of up to 2^-5.8 * max|y_t| on the Qwen-shaped layer (2^-7 on OLMoE), so
+# 2^-4 leaves a margin of about 3.5x.  Normwise errors are reported as well.
+REL = 2e-3
+FLOOR = 2.0 ** -4
+
+
+def f16_to_f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.float16)
+    return a.astype(np.float64)
+
+
+def rowwise_violations(got, want, rel=REL, floor=FLOOR):
+    """Boolean mask of elements outside the tolerance, rows = tokens (or pairs)."""
+    g, w = f16_to_f64(got), f16_to_f64(want)
+    m = np.abs(w).max(axis=-1, keepdims=True)
+    return np.abs(g - w) > rel * np.maximum(np.abs(w), m * floor)
+
+
+def assert_close_rows(got, want, what, rel=REL, floor=FLOOR):
+    bad = rowwise_violations(got, want, rel, floor)
+    if bad.any():
+        g, w = f16_to_f64(got), f16_to_f64(want)
+        idx = np.argwhere(bad)[:5].tolist()
+        raise AssertionError(f"{what}: {int(bad.sum())} elements outside tolerance, e.g. "
+                             + ", ".join(f"{tuple(i)}: got {g[tuple(i)]:.6g} want {w[tuple(i)]:.6g}" for i in idx))
+
+
+def error_report(got, want):
+    """(max relative error without floor over |want|>0, max normwise error per row)."""
+    g, w = f16_to_f64(got), f16_to_f64(want)
+    nz = np.abs(w) > 0
+    rel = float(np.max(np.abs(g - w)[nz] / np.abs(w)[nz])) if nz.any() else 0.0
+    m = np.abs(w).max(axis=-1, keepdims=True)
+    norm = float(np.max(np.abs(g - w).max(axis=-1, keepdims=True) / np.where(m > 0, m, 1)))
+    return rel, norm

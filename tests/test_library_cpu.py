@@ -1,0 +1,79 @@
+"""CPU checks of the HIP library: it loads, exports every declared symbol, and
+its host-side validation rejects bad arguments before touching a GPU."""
+import os
+import re
+
+import pytest
+
+from w4a16_routed_expert_amd import binding as B
+from w4a16_routed_expert_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = declared_functions()
+    assert len(decl) >= 9
+    for name in decl:
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+    assert sorted(B.EXPORTS) == decl
+
+
+def test_row_layout_matches_the_generator(lib):
+    for H, I in ((256, 512), (2048, 1024), (2048, 1408), (128, 128)):
+        rb, off = B.moe_expert_row_bytes(H, I)
+        lay = synth.expert_row_layout(H, I)
+        assert rb == lay["row_bytes"]
+        assert off == {k: v for k, v in lay.items() if k != "row_bytes"}
+    assert B.moe_expert_row_bytes(2048, 1000)[0] == 0
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    assert B.moe_route_workspace_size(1, 2048, 64) > 0
+    assert B.moe_route_workspace_size(32, 2048, 64) > B.moe_route_workspace_size(1, 2048, 64)
+    assert B.moe_route_workspace_size(4, 2048, 65) == 0          # unsupported shapes report 0
+    assert B.moe_route_workspace_size(4, 5000, 64) == 0
+
+
+def test_host_validation_rejects_bad_arguments(lib):
+    F = 0x1000  # never dereferenced: validation fails first
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(F, F, None, 4, 256, 65, 2, None, F, F, F, F, F, F, F, F, 1 << 20, stream=0)
+    assert ei.value.code == B.MOE_ERR_UNSUPPORTED
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(F, F, None, 4, 256, 8, 9, None, F, F, F, F, F, F, F, F, 1 << 20, stream=0)
+    assert ei.value.code == B.MOE_ERR_UNSUPPORTED
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(None, F, None, 4, 256, 8, 2, None, F, F, F, F, F, F, F, F, 1 << 20, stream=0)
+    assert ei.value.code == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(F, F, None, 4, 256, 8, 2, None, F, F, F, F, F, F, F, 0x1000, 16, stream=0)
+    assert ei.value.code == B.MOE_ERR_WORKSPACE
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(F, F, None, 4, 200, 8, 2, None, F, F, F, F, F, F, F, F, 1 << 20, stream=0)
+    assert ei.value.code == B.MOE_ERR_UNSUPPORTED
+    with pytest.raises(B.MoeError) as ei:     # row stride not a multiple of 256
+        B.moe_w4a16_expert_ffn(F, 4, 256, 512, 8, 2, F, 199_680 + 16, None, F, F, F, F, F, F, stream=0)
+    assert ei.value.code == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoeError) as ei:     # I not a multiple of 128
+        B.moe_w4a16_expert_ffn(F, 4, 256, 500, 8, 2, F, 1 << 20, None, F, F, F, F, F, F, stream=0)
+    assert ei.value.code == B.MOE_ERR_UNSUPPORTED
+    with pytest.raises(B.MoeError) as ei:     # only one of the shared-expert pointers
+        B.moe_combine(F, F, F, F, None, 4, 256, 2, F, stream=0)
+    assert ei.value.code == B.MOE_ERR_INVALID_ARG
+    assert "shared" in B.moe_last_error()

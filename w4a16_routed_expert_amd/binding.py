@@ -1,0 +1,152 @@
+"""Thin ctypes binding of libmoe_w4a16.so (include/moe_w4a16.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the library.  Functions carry the C names; tensors are torch CUDA tensors (or
+raw device addresses as ints), `stream` a torch.cuda.Stream, a raw hipStream_t
+address, or None for torch's current stream.  A non-zero status raises
+MoeError with the library's message.  If the library is not built, loading it
+raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_w4a16.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_CAPACITY = 4
+MOE_ERR_HIP = 5
+MOE_ERR_FAULTED = 6
+MOE_ERR_ABSENT_EXPERT = 7
+
+# Every symbol the header declares (checked by the CPU test suite).
+EXPORTS = (
+    "moe_version", "moe_last_error", "moe_expert_row_bytes",
+    "moe_route_workspace_size", "moe_route",
+    "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
+    "moe_combine",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[moe status {code}] {msg}")
+        self.code = code
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+    L = ctypes.CDLL(path)
+    L.moe_version.restype = _i
+    L.moe_version.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_expert_row_bytes.restype = _sz
+    L.moe_expert_row_bytes.argtypes = [_i, _i, ctypes.POINTER(_sz)]
+    L.moe_route_workspace_size.restype = _sz
+    L.moe_route_workspace_size.argtypes = [_i, _i, _i]
+    L.moe_route.restype = _i
+    L.moe_route.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.moe_w4a16_gateup.restype = _i
+    L.moe_w4a16_gateup.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.moe_w4a16_down.restype = _i
+    L.moe_w4a16_down.argtypes = [_i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.moe_w4a16_expert_ffn.restype = _i
+    L.moe_w4a16_expert_ffn.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp]
+    L.moe_combine.restype = _i
+    L.moe_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]
+    _lib = L
+    return L
+
+
+def _p(t):
+    """Device address of a tensor (or an int address, or None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _s(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoeError(rc, load().moe_last_error().decode())
+
+
+# ------------------------------------------------------------------ queries
+def moe_version() -> int:
+    return load().moe_version()
+
+
+def moe_last_error() -> str:
+    return load().moe_last_error().decode()
+
+
+def moe_expert_row_bytes(H: int, I: int):
+    """(row_bytes, dict of the six section offsets)."""
+    off = (_sz * 6)()
+    rb = load().moe_expert_row_bytes(H, I, off)
+    names = ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")
+    return int(rb), {n: int(off[i]) for i, n in enumerate(names)}
+
+
+def moe_route_workspace_size(T: int, H: int, E: int) -> int:
+    return int(load().moe_route_workspace_size(T, H, E))
+
+
+# ------------------------------------------------------------------ compute
+def moe_route(x, w_router, bias, T, H, E, k, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, pair_pos,
+              active_list, n_active, ws, ws_bytes, stream=None):
+    _check(load().moe_route(_p(x), _p(w_router), _p(bias), T, H, E, k, _p(logits), _p(topk_ids), _p(topk_w),
+                            _p(expert_offsets), _p(sorted_pairs), _p(pair_pos), _p(active_list), _p(n_active),
+                            _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_w4a16_gateup(x, T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, sorted_pairs, active_list,
+                     n_active, h, status=None, stream=None):
+    _check(load().moe_w4a16_gateup(_p(x), T, H, I, E, k, _p(rows), row_stride, _p(slot_map), _p(expert_offsets),
+                                   _p(sorted_pairs), _p(active_list), _p(n_active), _p(h), _p(status), _s(stream)))
+
+
+def moe_w4a16_down(T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, active_list, n_active, h, pair_out,
+                   status=None, stream=None):
+    _check(load().moe_w4a16_down(T, H, I, E, k, _p(rows), row_stride, _p(slot_map), _p(expert_offsets),
+                                 _p(active_list), _p(n_active), _p(h), _p(pair_out), _p(status), _s(stream)))
+
+
+def moe_w4a16_expert_ffn(x, T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, sorted_pairs, active_list,
+                         n_active, h, pair_out, status=None, stream=None):
+    _check(load().moe_w4a16_expert_ffn(_p(x), T, H, I, E, k, _p(rows), row_stride, _p(slot_map),
+                                       _p(expert_offsets), _p(sorted_pairs), _p(active_list), _p(n_active), _p(h),
+                                       _p(pair_out), _p(status), _s(stream)))
+
+
+def moe_combine(pair_out, pair_pos, topk_w, shared_out, shared_gate, T, H, k, y, stream=None):
+    _check(load().moe_combine(_p(pair_out), _p(pair_pos), _p(topk_w), _p(shared_out), _p(shared_gate), T, H, k,
+                              _p(y), _s(stream)))

@@ -1,0 +1,81 @@
+"""Device-buffer plumbing around the C ABI: one routed-expert layer.
+
+RoutedExpertLayer owns the torch device buffers the C calls write into and
+runs route -> expert FFN -> combine on one stream.  It does no arithmetic of
+its own: torch provides memory and streams, the HIP library does the work.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class RoutedExpertLayer:
+    """W4A16 routed-expert layer over qpacked expert rows that already sit in HBM.
+
+    rows: uint8 CUDA tensor [n_slots, row_stride] (256-byte aligned rows).
+    router: float16 CUDA tensor [H, E].  bias: float32 CUDA tensor [E] or None.
+    slot_map: int32 CUDA tensor [E] (slot of each expert, -1 = absent) or None
+    (expert e in slot e).
+    """
+
+    def __init__(self, H: int, I: int, E: int, k: int, rows: torch.Tensor, router: torch.Tensor,
+                 bias: torch.Tensor | None = None, slot_map: torch.Tensor | None = None, max_T: int = 64,
+                 device: str | torch.device = "cuda:0"):
+        self.H, self.I, self.E, self.k = H, I, E, k
+        self.row_bytes, self.offsets6 = B.moe_expert_row_bytes(H, I)
+        if rows.dtype != torch.uint8 or rows.dim() != 2 or rows.shape[1] < self.row_bytes:
+            raise ValueError("rows must be uint8 [n_slots, >= row_bytes]")
+        self.rows, self.router, self.bias, self.slot_map = rows, router, bias, slot_map
+        self.row_stride = rows.stride(0)
+        self.device = torch.device(device)
+        self.max_T = 0
+        self._alloc(max_T)
+
+    def _alloc(self, T: int):
+        d, E, k, H, I = self.device, self.E, self.k, self.H, self.I
+        n = max(T * k, 1)
+        self.max_T = T
+        self.logits = torch.empty((max(T, 1), E), dtype=torch.float32, device=d)
+        self.topk_ids = torch.empty((max(T, 1), k), dtype=torch.int32, device=d)
+        self.topk_w = torch.empty((max(T, 1), k), dtype=torch.float32, device=d)
+        self.expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=d)
+        self.sorted_pairs = torch.empty(n, dtype=torch.int32, device=d)
+        self.pair_pos = torch.empty(n, dtype=torch.int32, device=d)
+        self.active_list = torch.empty(E, dtype=torch.int32, device=d)
+        self.n_active = torch.empty(1, dtype=torch.int32, device=d)
+        self.ws_bytes = B.moe_route_workspace_size(T, H, E)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=d)      # zero before first use
+        self.h = torch.empty((n, I), dtype=torch.float16, device=d)
+        self.pair_out = torch.empty((n, H), dtype=torch.float32, device=d)
+        self.status = torch.zeros(1, dtype=torch.int32, device=d)
+
+    def route(self, x: torch.Tensor, stream=None):
+        T = x.shape[0]
+        if T > self.max_T:
+            self._alloc(T)
+        B.moe_route(x, self.router, self.bias, T, self.H, self.E, self.k, self.logits, self.topk_ids, self.topk_w,
+                    self.expert_offsets, self.sorted_pairs, self.pair_pos, self.active_list, self.n_active, self.ws,
+                    self.ws_bytes, stream)
+
+    def ffn(self, x: torch.Tensor, stream=None, rows=None):
+        T = x.shape[0]
+        B.moe_w4a16_expert_ffn(x, T, self.H, self.I, self.E, self.k, self.rows if rows is None else rows,
+                               self.row_stride, self.slot_map, self.expert_offsets, self.sorted_pairs,
+                               self.active_list, self.n_active, self.h, self.pair_out, self.status, stream)
+
+    def combine(self, T: int, y: torch.Tensor, shared_out=None, shared_gate=None, stream=None):
+        B.moe_combine(self.pair_out, self.pair_pos, self.topk_w, shared_out, shared_gate, T, self.H, self.k, y,
+                      stream)
+
+    def forward(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None, rows=None,
+                shared_out=None, shared_gate=None) -> torch.Tensor:
+        """y = layer(x); x float16 [T, H] on the device."""
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.H), dtype=torch.float16, device=self.device)
+        self.route(x, stream)
+        self.ffn(x, stream, rows)
+        self.combine(T, y, shared_out, shared_gate, stream)
+        return y
