@@ -93,12 +93,14 @@ const char *moe_last_error(void);
 size_t moe_expert_row_bytes(int H, int I, size_t *off6);
 
 /* ------------------------------------------------------------ routing
- * moe_route: router logits, top-k softmax and token-to-expert grouping, one
- * kernel launch.
+ * moe_route: router logits, top-k softmax and token-to-expert grouping (two
+ * kernel launches: logits, then one block for top-k and the grouping).
  *   logit[t][e] = RN32( exact sum_h x[t][h] * w_router[h][e] ) (+ bias[e])
- *     The dot product of FP16 values is accumulated exactly (in integer
- *     units of 2^-48) and rounded once to FP32, so the selected experts do
- *     not depend on summation order.  bias, if given, is added in FP32.
+ *     The correctly rounded FP32 value of the exact dot product of FP16
+ *     values, so the selected experts do not depend on summation order.  The
+ *     kernel sums the (exact) products in fp64 and recomputes a logit with
+ *     integer arithmetic only when an error bound cannot exclude that the
+ *     exact value rounds differently.  bias, if given, is added in FP32.
  *   topk_ids[t][j]: the k largest logits, descending, ties to the lower
  *     expert index.  topk_w[t][j] = softmax over those k logits (FP32; the
  *     weights of a token sum to 1).
@@ -109,11 +111,12 @@ size_t moe_expert_row_bytes(int H, int I, size_t *off6);
  *   logits_dev: FP32 [T][E] copy of the logits (bias included), or NULL.
  * Inputs:  x_dev FP16 [T][H] row-major; w_router_dev FP16 [H][E] row-major;
  *          bias_dev FP32 [E] or NULL.
- * ws_dev: workspace of moe_route_workspace_size(T, H, E) bytes, 256-byte
- *   aligned, ZERO-FILLED BEFORE ITS FIRST USE (it holds completion counters
- *   that every call leaves at zero again).  One workspace must not be used
- *   by two calls that can overlap.  Returns 0 for unsupported shapes.
- * Limits: T <= 65536, H <= 4096 (bounds the exact integer accumulators). */
+ * ws_dev / ws_bytes: workspace of moe_route_workspace_size(T, H, E) bytes
+ *   (16-byte aligned) that holds the logits between the two kernels; it may
+ *   be NULL when logits_dev is given.  It needs no initialization.  One
+ *   workspace must not be used by two calls that can overlap.
+ * Limits: T <= 65536, H <= 4096 (bounds the exact integer accumulators);
+ *   x_dev 8-byte aligned. */
 size_t moe_route_workspace_size(int T, int H, int E);
 int moe_route(const void *x_dev, const void *w_router_dev, const float *bias_dev,
               int T, int H, int E, int k,
@@ -121,6 +124,17 @@ int moe_route(const void *x_dev, const void *w_router_dev, const float *bias_dev
               int32_t *expert_offsets_dev, int32_t *sorted_pairs_dev, int32_t *pair_pos_dev,
               int32_t *active_list_dev, int32_t *n_active_dev,
               void *ws_dev, size_t ws_bytes, void *stream);
+
+/* moe_route_exact: same outputs as moe_route, every logit computed with the
+ * integer path (slow; for checking the fast path and for callers that want
+ * no floating-point shortcut at all).  Results are bit-identical to
+ * moe_route's. */
+int moe_route_exact(const void *x_dev, const void *w_router_dev, const float *bias_dev,
+                    int T, int H, int E, int k,
+                    float *logits_dev, int32_t *topk_ids_dev, float *topk_w_dev,
+                    int32_t *expert_offsets_dev, int32_t *sorted_pairs_dev, int32_t *pair_pos_dev,
+                    int32_t *active_list_dev, int32_t *n_active_dev,
+                    void *ws_dev, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------ expert FFN
  * Expert rows are addressed as rows_dev + slot_map_dev[e] * row_stride

@@ -43,11 +43,9 @@ def test_row_layout_matches_the_generator(lib):
     assert B.moe_expert_row_bytes(2048, 1000)[0] == 0
 
 
-def test_workspace_size_grows_with_tokens(lib):
-    assert B.moe_route_workspace_size(1, 2048, 64) > 0
-    assert B.moe_route_workspace_size(32, 2048, 64) > B.moe_route_workspace_size(1, 2048, 64)
+def test_route_workspace_holds_the_logits(lib):
+    assert B.moe_route_workspace_size(32, 2048, 64) >= 32 * 64 * 4
     assert B.moe_route_workspace_size(4, 2048, 65) == 0          # unsupported shapes report 0
-    assert B.moe_route_workspace_size(4, 5000, 64) == 0
 
 
 def test_host_validation_rejects_bad_arguments(lib):
@@ -62,8 +60,8 @@ def test_host_validation_rejects_bad_arguments(lib):
         B.moe_route(None, F, None, 4, 256, 8, 2, None, F, F, F, F, F, F, F, F, 1 << 20, stream=0)
     assert ei.value.code == B.MOE_ERR_INVALID_ARG
     with pytest.raises(B.MoeError) as ei:
-        B.moe_route(F, F, None, 4, 256, 8, 2, None, F, F, F, F, F, F, F, 0x1000, 16, stream=0)
-    assert ei.value.code == B.MOE_ERR_WORKSPACE
+        B.moe_route(F, F, None, 4, 8192, 8, 2, None, F, F, F, F, F, F, F, None, 0, stream=0)
+    assert ei.value.code == B.MOE_ERR_UNSUPPORTED
     with pytest.raises(B.MoeError) as ei:
         B.moe_route(F, F, None, 4, 200, 8, 2, None, F, F, F, F, F, F, F, F, 1 << 20, stream=0)
     assert ei.value.code == B.MOE_ERR_UNSUPPORTED

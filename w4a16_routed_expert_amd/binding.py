@@ -27,7 +27,7 @@ MOE_ERR_ABSENT_EXPERT = 7
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
     "moe_version", "moe_last_error", "moe_expert_row_bytes",
-    "moe_route_workspace_size", "moe_route",
+    "moe_route_workspace_size", "moe_route", "moe_route_exact",
     "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
     "moe_combine",
 )
@@ -63,6 +63,9 @@ def load(path: str = LIB_PATH):
     L.moe_route_workspace_size.argtypes = [_i, _i, _i]
     L.moe_route.restype = _i
     L.moe_route.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.moe_route_exact.restype = _i
+    L.moe_route_exact.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                  _vp]
     L.moe_w4a16_gateup.restype = _i
     L.moe_w4a16_gateup.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.moe_w4a16_down.restype = _i
@@ -126,6 +129,13 @@ def moe_route(x, w_router, bias, T, H, E, k, logits, topk_ids, topk_w, expert_of
     _check(load().moe_route(_p(x), _p(w_router), _p(bias), T, H, E, k, _p(logits), _p(topk_ids), _p(topk_w),
                             _p(expert_offsets), _p(sorted_pairs), _p(pair_pos), _p(active_list), _p(n_active),
                             _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_route_exact(x, w_router, bias, T, H, E, k, logits, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                    pair_pos, active_list, n_active, ws=None, ws_bytes=0, stream=None):
+    _check(load().moe_route_exact(_p(x), _p(w_router), _p(bias), T, H, E, k, _p(logits), _p(topk_ids), _p(topk_w),
+                                  _p(expert_offsets), _p(sorted_pairs), _p(pair_pos), _p(active_list),
+                                  _p(n_active), _p(ws), ws_bytes, _s(stream)))
 
 
 def moe_w4a16_gateup(x, T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, sorted_pairs, active_list,

@@ -1,5 +1,5 @@
 // Routing for the W4A16 routed-expert layer: router logits, top-k softmax and
-// token-to-expert grouping in one launch.
+// token-to-expert grouping.
 //
 // Routing selects the experts of each token at every routed layer
 // ("horizonrunmap.com/en", section "06 / Follow a token", step "Select
@@ -8,32 +8,31 @@
 // router formula; the logit is the correctly rounded FP32 value of the exact
 // FP16 dot product, so expert selection is independent of summation order.
 //
-// Launch shape: one block per (token, slice of H).  Each block accumulates
-// its slice of every logit of its token exactly, as integers, and stores the
-// partial sums in its own workspace slot (plain stores: no two blocks write
-// the same address, so nothing contends).  A per-token ticket (one atomic per
-// block, released after the stores) finds the block that completes a token;
-// that block acquires, adds the slices exactly, rounds the logits to FP32 and
-// runs top-k and softmax in one wavefront (lane = expert).  The block that
-// completes the last token runs the counting sort for all T*k pairs.  No
-// block ever waits for another, so every block exits.
+// Two launches, no hand-off between blocks of one launch.
+//   Logits: every FP16 x FP16 product is exact in fp64; a block sums them in
+//   fp64 and, alongside, sum |x*w| in FP32.  A standard bound on the fp64
+//   summation error (at most n roundings of relative size 2^-53 along any
+//   summation path) then tells whether the fp64 sum and the exact sum round
+//   to the same FP32 value: true unless the exact value lies within that
+//   bound of an FP32 rounding midpoint.  Logits that fail the test (exact
+//   ties at a midpoint among them) are recomputed exactly with 64-bit integer
+//   limbs by the whole block.
+//   Small batches (decode): route_logits_kernel, one block per (token, group
+//   of 16 experts), spreads the work over many CUs; route_group_kernel (one
+//   block) then runs top-k + softmax per token (one wavefront per token, lane
+//   = expert) and the stable counting sort of the T*k pairs.
+//   Large batches (prefill): route_select_kernel, one block per token, does
+//   logits, top-k and softmax; route_group_kernel only sorts.
 #include "moe_internal.h"
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kThreads = 256;
-constexpr int kSubs = kThreads / 64;     // H sub-slices per block (one wave each)
-constexpr int kSplit = 30;               // products with shift < kSplit go to the low limb
-constexpr int kMaxSlice = 256;           // router rows staged in LDS per block
-constexpr int kMaxSlices = 32;           // H slices per token (sizes the partial-sum workspace)
-
-// Agent-scope loads/stores for data handed between blocks of one launch.
-template <typename T>
-__device__ inline T ld_agent(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-template <typename T>
-__device__ inline void st_agent(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+constexpr int kSelThreads = 512;         // 8 waves per token
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kGrpThreads = 1024;        // 16 waves for the grouping
+constexpr int kGrpWaves = kGrpThreads / 64;
+constexpr int kMaxH = 4096;
+constexpr int kSplit = 30;               // products with shift < kSplit go to the low integer limb
 
 // FP16 bits -> signed integer significand m and exponent field q, value = m * 2^(q-25).
 __device__ inline void dec16(uint32_t b, int &m, int &q)
@@ -43,6 +42,8 @@ __device__ inline void dec16(uint32_t b, int &m, int &q)
     m = (b & 0x8000) ? -mag : mag;
     q = e ? e : 1;
 }
+
+__device__ inline double h2d(uint16_t b) { return (double)(float)__builtin_bit_cast(_Float16, b); }
 
 // Correctly rounded FP32 of (hi * 2^kSplit + lo) * 2^-48, ties to even.
 __device__ float rn32_limbs(long long hi, long long lo)
@@ -81,14 +82,34 @@ __device__ float rn32_limbs(long long hi, long long lo)
     return neg ? -r : r;
 }
 
+// True when every real number within err of v rounds (to nearest, ties to
+// even) to the same FP32 value as v does: no FP32 rounding midpoint lies in
+// [v - err, v + err].
+__device__ inline bool rn32_certain(double v, double err)
+{
+    const float f = (float)v;
+    const unsigned int b = __builtin_bit_cast(unsigned int, f);
+    float up, dn;
+    if (f == 0.0f) {
+        up = __builtin_bit_cast(float, 1u);
+        dn = -up;
+    } else if (f > 0.0f) {
+        up = __builtin_bit_cast(float, b + 1u);
+        dn = __builtin_bit_cast(float, b - 1u);
+    } else {
+        up = __builtin_bit_cast(float, b - 1u);
+        dn = __builtin_bit_cast(float, b + 1u);
+    }
+    const double mid_up = 0.5 * ((double)f + (double)up);      // exact in fp64
+    const double mid_dn = 0.5 * ((double)f + (double)dn);
+    return (v - err > mid_dn) && (v + err < mid_up);
+}
+
 struct RouteArgs {
     const uint16_t *x;      // [T][H]
     const uint16_t *wr;     // [H][E]
     const float *bias;      // [E] or null
-    int T, H, E, k, HS;     // HS = H slices per token
-    long long *part;        // [T][HS][E][2] exact partial limbs (hi, lo) per slice
-    unsigned int *tok_ticket;   // [T]
-    unsigned int *glob_ticket;  // [1]
+    int T, H, E, k;
     float *logits;          // [T][E] or null
     int32_t *ids;           // [T][k]
     float *w;               // [T][k]
@@ -97,59 +118,356 @@ struct RouteArgs {
     int32_t *pair_pos;      // [T*k]
     int32_t *active;        // [E]
     int32_t *n_active;      // [1]
+    int force_exact;        // recompute every logit with the integer path
+    float *lbuf;            // [T][E] logits handed from the logits kernel to the grouping kernel
 };
 
-// Top-k + softmax of token t, executed by one full wavefront; lane = expert,
-// (hi, lo) = the exact logit limbs of that expert.
-__device__ void finalize_token(const RouteArgs &a, int t, int lane, long long hi, long long lo)
+// Exact logit of one expert, computed by the whole block: integer limbs of
+// the products x[h] * wr[h][e], summed in two 64-bit accumulators (each holds
+// fewer than 2^12 terms below 2^51, so neither overflows), then reduced
+// across the block and rounded once.
+__device__ float exact_logit(const RouteArgs &a, int t, int e, long long (*red)[2])
+{
+    const int tid = threadIdx.x;
+    long long hi = 0, lo = 0;
+    for (int h = tid; h < a.H; h += kSelThreads) {
+        int mx, qx, mw, qw;
+        dec16(a.x[(size_t)t * a.H + h], mx, qx);
+        dec16(a.wr[(size_t)h * a.E + e], mw, qw);
+        const long long prod = (long long)(mx * mw);               // |prod| < 2^22
+        const int sh = qx + qw - 2;                                // product = prod * 2^(sh-48), sh in [0, 58]
+        if (sh < kSplit) lo += (long long)((unsigned long long)prod << sh);
+        else hi += (long long)((unsigned long long)prod << (sh - kSplit));
+    }
+    red[tid][0] = hi;
+    red[tid][1] = lo;
+    __syncthreads();
+    for (int s = kSelThreads / 2; s > 0; s >>= 1) {
+        if (tid < s) {
+            red[tid][0] += red[tid + s][0];
+            red[tid][1] += red[tid + s][1];
+        }
+        __syncthreads();
+    }
+    const float r = rn32_limbs(red[0][0], red[0][1]);
+    __syncthreads();                                               // red is reused by the next call
+    return r;
+}
+
+// Top-k (ties to the lower expert index, slots in descending order) and
+// softmax over the k selected logits for token t; one full wavefront, lane =
+// expert, lv = that expert's final logit (bias included).  Each lane ranks
+// its logit against all E logits (read back from the wave's LDS scratch, 64
+// + MOE_MAX_TOPK floats): rank < k is its slot.  The softmax denominator is
+// summed in slot order.  Writes ids and w, and the ids also to s_ids (if not
+// null).
+__device__ void topk_softmax_wave(const RouteArgs &a, int t, int lane, float lv, int *s_ids, float *scratch)
 {
     const int E = a.E, k = a.k;
-    float v = 0.0f;
-    if (lane < E) {
-        v = rn32_limbs(hi, lo);
-        if (a.bias) v = v + a.bias[lane];
-        if (a.logits) a.logits[(size_t)t * E + lane] = v;
-    }
-    bool live = lane < E;
-    float selv[MOE_MAX_TOPK];
-    int seli[MOE_MAX_TOPK];
+    float *s_l = scratch, *s_ex = scratch + 64;
+    s_l[lane] = lane < E ? lv : -INFINITY;          // missing experts never outrank a real one
+    __builtin_amdgcn_wave_barrier();
+    float4 v[16];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-        selv[j] = 0.0f;
-        seli[j] = 0;
-        if (j >= k) continue;
-        float bv = v;
-        int bi = live ? lane : 64;                       // 64 = no candidate
+    for (int i = 0; i < 16; ++i) v[i] = reinterpret_cast<const float4 *>(s_l)[i];
+    int rank = 0;
+    float vmax = lv;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            // order: a candidate beats none; larger value; on equal value, lower index
-            const bool take = oi < 64 && (bi == 64 || ov > bv || (ov == bv && oi < bi));
-            if (take) { bv = ov; bi = oi; }
+    for (int i = 0; i < 16; ++i) {
+        const float vv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = 4 * i + c;
+            rank += (vv[c] > lv) || (vv[c] == lv && j < lane);
+            vmax = fmaxf(vmax, vv[c]);
         }
-        selv[j] = bv;
-        seli[j] = bi;
-        if (lane == bi) live = false;
     }
-    // softmax over the k selected logits (loops fully unrolled: the arrays stay in registers)
-    float ex[MOE_MAX_TOPK];
+    const bool sel = lane < E && rank < k;
+    const float ex = sel ? expf(lv - vmax) : 0.0f;
+    if (sel) s_ex[rank] = ex;
+    __builtin_amdgcn_wave_barrier();
     float den = 0.0f;
+    for (int j = 0; j < k; ++j) den += s_ex[j];
+    if (sel) {
+        a.ids[(size_t)t * k + rank] = lane;
+        a.w[(size_t)t * k + rank] = ex / den;
+        if (s_ids) s_ids[t * k + rank] = lane;
+    }
+    __builtin_amdgcn_wave_barrier();       // scratch is reused by this wave's next token
+}
+
+// Loads VEC consecutive FP16 router weights (experts e0 .. e0+VEC-1 of row h).
+template <int VEC>
+struct WLoad;
+template <>
+struct WLoad<8> {
+    typedef unsigned int T __attribute__((ext_vector_type(4)));
+    static __device__ inline T ld(const uint16_t *p) { return *reinterpret_cast<const T *>(p); }
+    static __device__ inline uint16_t get(const T &v, int j) { return (uint16_t)(v[j >> 1] >> (16 * (j & 1))); }
+};
+template <>
+struct WLoad<4> {
+    typedef unsigned int T __attribute__((ext_vector_type(2)));
+    static __device__ inline T ld(const uint16_t *p) { return *reinterpret_cast<const T *>(p); }
+    static __device__ inline uint16_t get(const T &v, int j) { return (uint16_t)(v[j >> 1] >> (16 * (j & 1))); }
+};
+template <>
+struct WLoad<1> {
+    typedef uint16_t T;
+    static __device__ inline T ld(const uint16_t *p) { return *p; }
+    static __device__ inline uint16_t get(const T &v, int) { return v; }
+};
+
+// One block per token.  fp64 pass: lane = (64/VEC)*hp + eq handles experts
+// VEC*eq .. VEC*eq+VEC-1 (one vector load per row) and rows
+// h = PH*(kSelWaves*i + wave) + hp, PH = 64*VEC/64 row phases per wave.
+template <int VEC>
+__global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
+{
+    constexpr int EQ = 64 / VEC;             // lanes sharing one row
+    constexpr int PH = VEC;                  // rows per wave step (64 / EQ)
+    constexpr int U = 8;                     // rows in flight per thread
+    typedef WLoad<VEC> L;
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.E, H = a.H;
+    __shared__ double s_x[kMaxH];
+    __shared__ double s_acc[kSelWaves][64];
+    __shared__ float s_bnd[kSelWaves][64];
+    __shared__ long long s_red[kSelThreads][2];
+    __shared__ float s_logit[64];
+    __shared__ __attribute__((aligned(16))) float s_topk[64 + MOE_MAX_TOPK];
+    __shared__ unsigned long long s_redo;
+
+    {   // x row -> fp64 in LDS, 4 values per thread per step, all loads first
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 *src = reinterpret_cast<const u32x2 *>(a.x + (size_t)t * H);
+        u32x2 v[kMaxH / 4 / kSelThreads];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-        ex[j] = 0.0f;
-        if (j < k) {
-            ex[j] = expf(selv[j] - selv[0]);
-            den += ex[j];
+        for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) {
+            const int i = tid + r * kSelThreads;
+            v[r] = src[min(i, H / 4 - 1)];
+        }
+#pragma unroll
+        for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) {
+            const int i = tid + r * kSelThreads;
+            if (i < H / 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_x[4 * i + j] = h2d((uint16_t)(v[r][j >> 1] >> (16 * (j & 1))));
+            }
         }
     }
-    if (lane == 0) {
+    __syncthreads();
+
+    const int eq = lane % EQ, hp = lane / EQ;
+    const int e0 = VEC * eq;
+    double acc[VEC];
+    float bnd[VEC];
 #pragma unroll
-        for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-            if (j < k) {
-                st_agent(&a.ids[(size_t)t * k + j], (int32_t)seli[j]);
-                a.w[(size_t)t * k + j] = ex[j] / den;
+    for (int j = 0; j < VEC; ++j) { acc[j] = 0.0; bnd[j] = 0.0f; }
+    if (e0 < E) {
+        const uint16_t *wcol = a.wr + e0;
+        const int step = PH * kSelWaves;
+        // branch-free body: rows past H load a clamped (valid) row and use x = 0
+        for (int h0 = PH * wave + hp; h0 < H; h0 += U * step) {
+            typename L::T wv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const unsigned int h = (unsigned int)min(h0 + u * step, H - 1);
+                wv[u] = L::ld(wcol + h * (unsigned int)E);
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int h = h0 + u * step;
+                const double xv = h < H ? s_x[h] : 0.0;
+                const float xa = fabsf((float)xv);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const float wf = (float)__builtin_bit_cast(_Float16, L::get(wv[u], j));
+                    acc[j] = fma(xv, (double)wf, acc[j]);              // exact product, fp64 sum
+                    bnd[j] = fmaf(xa, fabsf(wf), bnd[j]);              // sum |x*w| (for the error bound)
+                }
+            }
+        }
+    }
+    // sum the PH row phases of each expert within the wave (lanes eq, eq+EQ, ...)
+#pragma unroll
+    for (int off = EQ; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            acc[j] += __shfl_xor(acc[j], off, 64);
+            bnd[j] += __shfl_xor(bnd[j], off, 64);
+        }
+    }
+    if (hp == 0) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            s_acc[wave][e0 + j] = acc[j];
+            s_bnd[wave][e0 + j] = bnd[j];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        double v = 0.0;
+        float B = 0.0f;
+        for (int r = 0; r < kSelWaves; ++r) {
+            v += s_acc[r][lane];
+            B += s_bnd[r][lane];
+        }
+        // Any summation path above has at most n = H/(PH*kSelWaves) + log2(PH)
+        // + kSelWaves <= 1024 + 3 + 8 fp64 additions, so |v - exact| <=
+        // n * 2^-53 * sum|x*w| (plus higher-order terms) <= 2^-42.9 * sum|x*w|;
+        // B (FP32, under 1050 additions) is within a factor 1.0001 of the true
+        // sum|x*w|, so err = 2^-42 * B covers it.
+        const double err = ldexp((double)B, -42);
+        const bool certain = lane >= E || (!a.force_exact && rn32_certain(v, err));
+        s_logit[lane] = (float)v;
+        const unsigned long long m = __ballot(!certain);
+        if (lane == 0) s_redo = m;
+    }
+    __syncthreads();
+    unsigned long long redo = s_redo;
+    while (redo) {                                   // rare: exact recomputation by the whole block
+        const int e = __builtin_ctzll(redo);
+        redo &= redo - 1ull;
+        const float l = exact_logit(a, t, e, s_red);
+        if (tid == 0) s_logit[e] = l;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+
+    // logits (+ bias), then top-k and softmax, lane = expert
+    float lv = 0.0f;
+    if (lane < E) {
+        lv = s_logit[lane];
+        if (a.bias) lv = lv + a.bias[lane];
+        if (a.logits) a.logits[(size_t)t * E + lane] = lv;
+    }
+    topk_softmax_wave(a, t, lane, lv, nullptr, s_topk);
+}
+
+constexpr int kGroupE = 16;                // experts per block in the split logits kernel
+
+// Small batches: one block per (token t, group of kGroupE experts); each
+// block sums the full reduction axis for its experts.  fp64 pass: lane =
+// (EQ)*hp + eq, EQ = kGroupE/VEC lanes per row, loads VEC experts of a row;
+// rows h = RPW*(kSelWaves*i + wave) + hp, RPW = 64/EQ rows per wave step.
+template <int VEC>
+__global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
+{
+    constexpr int EQ = kGroupE / VEC;
+    constexpr int RPW = 64 / EQ;
+    constexpr int U = 8;                     // rows in flight per thread
+    typedef WLoad<VEC> L;
+    const int G = (a.E + kGroupE - 1) / kGroupE;
+    const int t = blockIdx.x / G, g = blockIdx.x % G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.E, H = a.H;
+    __shared__ double s_x[kMaxH];
+    __shared__ double s_acc[kSelWaves][kGroupE];
+    __shared__ float s_bnd[kSelWaves][kGroupE];
+    __shared__ long long s_red[kSelThreads][2];
+    __shared__ float s_logit[kGroupE];
+    __shared__ unsigned long long s_redo;
+
+    {   // x row -> fp64 in LDS
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 *src = reinterpret_cast<const u32x2 *>(a.x + (size_t)t * H);
+        u32x2 v[kMaxH / 4 / kSelThreads];
+#pragma unroll
+        for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) v[r] = src[min(tid + r * kSelThreads, H / 4 - 1)];
+#pragma unroll
+        for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) {
+            const int i = tid + r * kSelThreads;
+            if (i < H / 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_x[4 * i + j] = h2d((uint16_t)(v[r][j >> 1] >> (16 * (j & 1))));
+            }
+        }
+    }
+    __syncthreads();
+
+    const int eq = lane % EQ, hp = lane / EQ;
+    const int e0 = g * kGroupE + VEC * eq;          // first expert of this lane
+    double acc[VEC];
+    float bnd[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) { acc[j] = 0.0; bnd[j] = 0.0f; }
+    if (e0 < E) {
+        const uint16_t *wcol = a.wr + e0;
+        const int step = RPW * kSelWaves;
+        // branch-free body: rows past H load a clamped (valid) row and use x = 0
+        for (int h0 = RPW * wave + hp; h0 < H; h0 += U * step) {
+            typename L::T wv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const unsigned int h = (unsigned int)min(h0 + u * step, H - 1);
+                wv[u] = L::ld(wcol + h * (unsigned int)E);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int h = h0 + u * step;
+                const double xv = h < H ? s_x[h] : 0.0;
+                const float xa = fabsf((float)xv);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const float wf = (float)__builtin_bit_cast(_Float16, L::get(wv[u], j));
+                    acc[j] = fma(xv, (double)wf, acc[j]);              // exact product, fp64 sum
+                    bnd[j] = fmaf(xa, fabsf(wf), bnd[j]);              // sum |x*w| (for the error bound)
+                }
+            }
+        }
+    }
+    // sum the RPW row phases within the wave (lanes eq, eq+EQ, ...)
+#pragma unroll
+    for (int off = EQ; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            acc[j] += __shfl_xor(acc[j], off, 64);
+            bnd[j] += __shfl_xor(bnd[j], off, 64);
+        }
+    }
+    if (hp == 0) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            s_acc[wave][VEC * eq + j] = acc[j];
+            s_bnd[wave][VEC * eq + j] = bnd[j];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int e = g * kGroupE + lane;
+        double v = 0.0;
+        float B = 0.0f;
+        if (lane < kGroupE) {
+            for (int r = 0; r < kSelWaves; ++r) {
+                v += s_acc[r][lane];
+                B += s_bnd[r][lane];
+            }
+        }
+        // same bound as route_select_kernel: at most H/(RPW*kSelWaves) + 6 + 8
+        // fp64 additions on any path, far below 2^9
+        const double err = ldexp((double)B, -42);
+        const bool certain = lane >= kGroupE || e >= E || (!a.force_exact && rn32_certain(v, err));
+        if (lane < kGroupE) s_logit[lane] = (float)v;
+        const unsigned long long m = __ballot(!certain);
+        if (lane == 0) s_redo = m;
+    }
+    __syncthreads();
+    unsigned long long redo = s_redo;
+    while (redo) {                                   // rare: exact recomputation by the whole block
+        const int j = __builtin_ctzll(redo);
+        redo &= redo - 1ull;
+        const float l = exact_logit(a, t, g * kGroupE + j, s_red);
+        if (tid == 0) s_logit[j] = l;
+    }
+    __syncthreads();
+    if (tid < kGroupE) {
+        const int e = g * kGroupE + tid;
+        if (e < E) {
+            float lv = s_logit[tid];
+            if (a.bias) lv = lv + a.bias[e];
+            a.lbuf[(size_t)t * E + e] = lv;
         }
     }
 }
@@ -168,210 +486,149 @@ __device__ inline unsigned long long same_expert_lanes(int e)
     return e >= 0 ? m : 0ull;
 }
 
-// Stable counting sort of all pairs by expert; run by the last block.
-// Counts: LDS atomics over all threads.  Offsets and the active list: one
-// wave, prefix sum by shuffles.  Scatter: wave 0 walks the pairs in order, 64
-// at a time; a pair's place among equal experts of its chunk comes from a
-// ballot, and each expert's running base advances by its chunk count.
-__device__ void group_pairs(const RouteArgs &a)
+// Stable counting sort of the T*k pairs by expert, one block.  Wave w owns
+// the contiguous pair range [w*n/W, (w+1)*n/W): per-wave counts (LDS
+// atomics), a prefix over experts and waves gives each wave its starting
+// position per expert, then each wave walks its range 64 pairs at a time; a
+// pair's rank among equal experts of its chunk comes from a ballot.
+constexpr int kGrpLdsIds = 4096;           // pairs whose ids the grouping keeps in LDS
+
+template <bool TOPK>
+__global__ __launch_bounds__(kGrpThreads) void route_group_kernel(RouteArgs a)
 {
-    __shared__ int cnt[MOE_MAX_EXPERTS];
-    __shared__ int base[MOE_MAX_EXPERTS];
-    const int tid = threadIdx.x, lane = tid & 63;
+    __shared__ int cnt[kGrpWaves][MOE_MAX_EXPERTS];
+    __shared__ int base[kGrpWaves][MOE_MAX_EXPERTS];
+    __shared__ int s_ids[TOPK ? kGrpLdsIds : 1];
+    __shared__ __attribute__((aligned(16))) float s_topk[TOPK ? kGrpWaves : 1][64 + MOE_MAX_TOPK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.T * a.k, E = a.E;
-    if (tid < MOE_MAX_EXPERTS) cnt[tid] = 0;
+    if (TOPK) {
+        // top-k + softmax of every token from the logits kernel's output, one wave per token
+        for (int t = wave; t < a.T; t += kGrpWaves) {
+            const float lv = lane < E ? a.lbuf[(size_t)t * E + lane] : 0.0f;
+            if (a.logits && a.logits != a.lbuf && lane < E) a.logits[(size_t)t * E + lane] = lv;
+            topk_softmax_wave(a, t, lane, lv, s_ids, s_topk[wave]);
+        }
+        __syncthreads();
+    }
+    // ids of pair p: from LDS when this block just produced them, else from memory
+    auto id_of = [&](int p) { return TOPK ? s_ids[p] : a.ids[p]; };
+    const int p0 = (int)((long long)n * wave / kGrpWaves), p1 = (int)((long long)n * (wave + 1) / kGrpWaves);
+    cnt[wave][lane] = 0;
     __syncthreads();
-    for (int p = tid; p < n; p += kThreads) {
-        const int e = ld_agent(&a.ids[p]);
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    for (int p = p0 + lane; p < p1; p += 64) {
+        const int e = id_of(p);
+        if (e >= 0 && e < E) atomicAdd(&cnt[wave][e], 1);
     }
     __syncthreads();
-    if (tid >= 64) return;                  // wave 0 only from here
-    const int c = lane < E ? cnt[lane] : 0;
-    int incl = c;
+    if (wave == 0) {
+        // per expert (lane): total count, exclusive prefix over experts, per-wave starts
+        int c = 0;
+        for (int w = 0; w < kGrpWaves; ++w) c += (lane < E) ? cnt[w][lane] : 0;
+        int incl = c;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const int excl = incl - c;
+        int run = excl;
+        for (int w = 0; w < kGrpWaves; ++w) {
+            base[w][lane] = run;
+            run += (lane < E) ? cnt[w][lane] : 0;
+        }
+        const unsigned long long act = __ballot(lane < E && c > 0);
+        const int na = __popcll(act);
+        const unsigned long long below = (1ull << lane) - 1ull;
+        if (lane < E) {
+            a.offsets[lane] = excl;
+            if (c > 0) a.active[__popcll(act & below)] = lane;
+            if (lane >= na) a.active[lane] = -1;
+            if (lane == E - 1) a.offsets[E] = incl;
+        }
+        if (lane == 0) a.n_active[0] = na;
     }
-    const int excl = incl - c;
-    const unsigned long long act = __ballot(c > 0);
-    const int na = __popcll(act);
+    __syncthreads();
     const unsigned long long below = (1ull << lane) - 1ull;
-    if (lane < E) {
-        a.offsets[lane] = excl;
-        base[lane] = excl;
-        if (c > 0) a.active[__popcll(act & below)] = lane;
-        if (lane >= na) a.active[lane] = -1;
-        if (lane == E - 1) a.offsets[E] = incl;
-    }
-    if (lane == 0) a.n_active[0] = na;
-    for (int c0 = 0; c0 < n; c0 += 64) {
+    for (int c0 = p0; c0 < p1; c0 += 64) {
         const int p = c0 + lane;
-        int e = p < n ? ld_agent(&a.ids[p]) : -1;
+        int e = p < p1 ? id_of(p) : -1;
         if (e >= E) e = -1;
         const unsigned long long peers = same_expert_lanes(e);
         if (e >= 0) {
             const int rank = __popcll(peers & below);
-            const int pos = base[e] + rank;
+            const int pos = base[wave][e] + rank;
             a.sorted_pairs[pos] = p;
             a.pair_pos[p] = pos;
-            if (rank == 0) base[e] = pos + __popcll(peers);     // one leader per expert and chunk
+            if (rank == 0) base[wave][e] = pos + __popcll(peers);   // one leader per expert and chunk
         }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a)
+constexpr int kSmallBatch = 256;           // largest T routed with the split logits kernel
+
+size_t route_ws_bytes(int T, int E) { return ((size_t)T * E * sizeof(float) + 255) / 256 * 256; }
+
+int route_launch(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int E, int k,
+                 float *logits_dev, int32_t *topk_ids_dev, float *topk_w_dev, int32_t *expert_offsets_dev,
+                 int32_t *sorted_pairs_dev, int32_t *pair_pos_dev, int32_t *active_list_dev, int32_t *n_active_dev,
+                 void *ws_dev, size_t ws_bytes, int force_exact, void *stream)
 {
-    const int t = blockIdx.x / a.HS;
-    const int c = blockIdx.x % a.HS;
-    const int tid = threadIdx.x, lane = tid & 63, sub = tid >> 6;
-    const int E = a.E;
-    const int slice = a.H / a.HS;            // multiple of 32, at most kMaxSlice
-    const int per = slice / kSubs;           // multiple of 8
-    const int h0 = c * slice;
+    moe::clear_error();
+    int rc = moe::check_shape(T, H, 0, E, k, false);
+    if (rc) return rc;
+    if (H > kMaxH) return moe::fail(MOE_ERR_UNSUPPORTED, "moe_route: H=%d > %d", H, kMaxH);
+    if (T == 0) return MOE_OK;
+    if (!x_dev || !w_router_dev || !topk_ids_dev || !topk_w_dev || !expert_offsets_dev || !sorted_pairs_dev ||
+        !pair_pos_dev || !active_list_dev || !n_active_dev)
+        return moe::fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer argument");
+    if (!moe::aligned(x_dev, 8) || !moe::aligned(w_router_dev, 2))
+        return moe::fail(MOE_ERR_INVALID_ARG, "moe_route: x must be 8-byte and w_router 2-byte aligned");
+    const bool small = T <= kSmallBatch;
+    float *lbuf = logits_dev;
+    if (small && !lbuf) {
+        if (!ws_dev || ws_bytes < route_ws_bytes(T, E) || !moe::aligned(ws_dev, 16))
+            return moe::fail(MOE_ERR_WORKSPACE, "moe_route: without logits_dev the workspace needs %zu bytes",
+                             route_ws_bytes(T, E));
+        lbuf = (float *)ws_dev;
+    }
 
-    // Stage the router rows h0 .. h0+slice-1 (contiguous, 16-byte aligned) and
-    // the token's decoded activations in LDS.
-    __shared__ u32x4 s_w[kMaxSlice * MOE_MAX_EXPERTS * 2 / 16];
-    __shared__ int2 s_x[kMaxSlice];
-    {
-        // all loads first (one memory latency), then the LDS writes
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.wr + (size_t)h0 * E);
-        const int n16 = slice * E * 2 / 16;
-        constexpr int kPer = kMaxSlice * MOE_MAX_EXPERTS * 2 / 16 / kThreads;
-        u32x4 v[kPer];
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) {                 // unconditional: indices clamped into the slice
-            const int i = min(tid + r * kThreads, n16 - 1);
-            v[r] = src[i];
-        }
-        uint16_t xb = 0;
-        if (tid < slice) xb = a.x[(size_t)t * a.H + h0 + tid];
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int i = tid + r * kThreads;
-            if (i < n16) s_w[i] = v[r];
-        }
-        if (tid < slice) {
-            int m, q;
-            dec16(xb, m, q);
-            s_x[tid] = make_int2(m, q - 2);
-        }
+    RouteArgs a;
+    a.x = (const uint16_t *)x_dev;
+    a.wr = (const uint16_t *)w_router_dev;
+    a.bias = bias_dev;
+    a.T = T; a.H = H; a.E = E; a.k = k;
+    a.logits = logits_dev;
+    a.ids = topk_ids_dev;
+    a.w = topk_w_dev;
+    a.offsets = expert_offsets_dev;
+    a.sorted_pairs = sorted_pairs_dev;
+    a.pair_pos = pair_pos_dev;
+    a.active = active_list_dev;
+    a.n_active = n_active_dev;
+    a.force_exact = force_exact;
+    a.lbuf = lbuf;
+    hipStream_t s = (hipStream_t)stream;
+    // widest router-row load the layout allows: 8 or 4 experts per lane, else 1
+    const bool v8 = E % 8 == 0 && moe::aligned(w_router_dev, 16);
+    const bool v4 = E % 4 == 0 && moe::aligned(w_router_dev, 8);
+    if (small) {
+        const unsigned int blocks = (unsigned int)T * (unsigned int)((E + kGroupE - 1) / kGroupE);
+        if (v8) hipLaunchKernelGGL(route_logits_kernel<8>, dim3(blocks), dim3(kSelThreads), 0, s, a);
+        else if (v4) hipLaunchKernelGGL(route_logits_kernel<4>, dim3(blocks), dim3(kSelThreads), 0, s, a);
+        else hipLaunchKernelGGL(route_logits_kernel<1>, dim3(blocks), dim3(kSelThreads), 0, s, a);
+        rc = moe::check_launch("moe_route (logits)");
+        if (rc) return rc;
+        hipLaunchKernelGGL(route_group_kernel<true>, dim3(1), dim3(kGrpThreads), 0, s, a);
+        return moe::check_launch("moe_route (top-k, group)");
     }
-    __syncthreads();
-    const uint16_t *sw = reinterpret_cast<const uint16_t *>(s_w);
-
-    // exact partial sums of this thread's h range for expert `lane`
-    long long hi = 0, lo = 0;
-    if (lane < E) {
-#pragma unroll 8
-        for (int i = sub * per; i < sub * per + per; ++i) {
-            const int2 xv = s_x[i];
-            int mw, qw;
-            dec16(sw[i * E + lane], mw, qw);
-            const long long prod = (long long)(xv.x * mw);     // |prod| < 2^22
-            const int sh = xv.y + qw;                          // product = prod * 2^(sh-48), sh in [0, 58]
-            if (sh < kSplit) lo += (long long)((unsigned long long)prod << sh);
-            else hi += (long long)((unsigned long long)prod << (sh - kSplit));
-        }
-    }
-    __shared__ long long red[kSubs][64][2];
-    red[sub][lane][0] = hi;
-    red[sub][lane][1] = lo;
-    __syncthreads();
-    if (sub == 0 && lane < E) {
-        long long shi = 0, slo = 0;
-        for (int s = 0; s < kSubs; ++s) { shi += red[s][lane][0]; slo += red[s][lane][1]; }
-        // write-through (agent-scope) stores: nothing is left dirty in this
-        // XCD's L2 for the release below to write back
-        long long *p = a.part + (((size_t)t * a.HS + c) * E + lane) * 2;
-        st_agent(p, shi);
-        st_agent(p + 1, slo);
-    }
-    // Completion: the ticket increment is a release by wave 0, which stored
-    // the partial sums; only the block that takes the last ticket acquires.
-    // (A full fence in every block would write back and invalidate the L2 of
-    // its XCD each time.)
-    __shared__ int last_slice, last_token;
-    if (tid == 0) {
-        const unsigned int prev =
-            __hip_atomic_fetch_add(&a.tok_ticket[t], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        last_slice = (prev == (unsigned int)a.HS - 1u);
-    }
-    __syncthreads();
-    if (!last_slice) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // exact sum of the token's slices: wave `sub` adds slices sub, sub+4, ...
-    hi = 0;
-    lo = 0;
-    if (lane < E) {
-#pragma unroll
-        for (int r = 0; r < kMaxSlices / kSubs; ++r) {
-            const int cc = sub + r * kSubs;
-            if (cc < a.HS) {
-                const long long *p = a.part + (((size_t)t * a.HS + cc) * E + lane) * 2;
-                hi += ld_agent(p);
-                lo += ld_agent(p + 1);
-            }
-        }
-    }
-    __syncthreads();                    // everyone is done with red from the block reduction
-    red[sub][lane][0] = hi;
-    red[sub][lane][1] = lo;
-    __syncthreads();
-    if (sub == 0) {
-        long long shi = 0, slo = 0;
-        for (int s = 0; s < kSubs; ++s) { shi += red[s][lane][0]; slo += red[s][lane][1]; }
-        finalize_token(a, t, lane, shi, slo);
-        if (lane == 0) st_agent(&a.tok_ticket[t], 0u);
-    }
-    if (tid == 0) {
-        const unsigned int prev = __hip_atomic_fetch_add(a.glob_ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        last_token = (prev == (unsigned int)a.T - 1u);
-    }
-    __syncthreads();
-    if (!last_token) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    group_pairs(a);
-    if (tid == 0) st_agent(a.glob_ticket, 0u);
-}
-
-size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
-
-struct WsLayout {
-    size_t part, tok, glob, total;
-};
-
-// Workspace: tickets first (they must start at zero and are left at zero),
-// then the partial sums (fully written before they are read).
-WsLayout ws_layout(int T, int HS, int E)
-{
-    WsLayout L;
-    L.tok = 0;
-    L.glob = align_up((size_t)T * sizeof(unsigned int), 256);
-    L.part = L.glob + 256;
-    L.total = L.part + align_up((size_t)T * HS * E * 2 * sizeof(long long), 256);
-    return L;
-}
-
-// Number of H slices per token: a divisor of H/32 (slices hold a multiple of
-// 32 rows) with slices of 128 .. kMaxSlice rows where H allows, at most
-// kMaxSlices, chosen to give a small batch about 256 blocks.
-int pick_slices(int T, int H)
-{
-    const int units = H / 32;
-    const int min_hs = (H + kMaxSlice - 1) / kMaxSlice;
-    int max_hs = H / 128 > min_hs ? H / 128 : min_hs;
-    if (max_hs > kMaxSlices) max_hs = kMaxSlices;
-    const int target = 256 / (T > 0 ? T : 1);
-    int best = -1;
-    for (int d = 1; d <= units; ++d) {
-        if (units % d || d < min_hs || d > max_hs) continue;
-        if (best < 0) best = d;                 // smallest admissible
-        if (d <= target) best = d;              // largest admissible not above the target
-    }
-    return best;
+    if (v8) hipLaunchKernelGGL(route_select_kernel<8>, dim3((unsigned int)T), dim3(kSelThreads), 0, s, a);
+    else if (v4) hipLaunchKernelGGL(route_select_kernel<4>, dim3((unsigned int)T), dim3(kSelThreads), 0, s, a);
+    else hipLaunchKernelGGL(route_select_kernel<1>, dim3((unsigned int)T), dim3(kSelThreads), 0, s, a);
+    rc = moe::check_launch("moe_route (select)");
+    if (rc) return rc;
+    hipLaunchKernelGGL(route_group_kernel<false>, dim3(1), dim3(kGrpThreads), 0, s, a);
+    return moe::check_launch("moe_route (group)");
 }
 
 }  // namespace
@@ -380,10 +637,9 @@ extern "C" {
 
 size_t moe_route_workspace_size(int T, int H, int E)
 {
-    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || H <= 0 || H % 128 || H > 4096) return 0;
-    const int HS = pick_slices(T, H);
-    if (HS < 1) return 0;
-    return ws_layout(T, HS, E).total;
+    (void)H;
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    return route_ws_bytes(T, E);
 }
 
 int moe_route(const void *x_dev, const void *w_router_dev, const float *bias_dev,
@@ -393,43 +649,20 @@ int moe_route(const void *x_dev, const void *w_router_dev, const float *bias_dev
               int32_t *active_list_dev, int32_t *n_active_dev,
               void *ws_dev, size_t ws_bytes, void *stream)
 {
-    moe::clear_error();
-    int rc = moe::check_shape(T, H, 0, E, k, false);
-    if (rc) return rc;
-    if (H > 4096) return moe::fail(MOE_ERR_UNSUPPORTED, "moe_route: H=%d > 4096", H);
-    if (T == 0) return MOE_OK;
-    if (!x_dev || !w_router_dev || !topk_ids_dev || !topk_w_dev || !expert_offsets_dev || !sorted_pairs_dev ||
-        !pair_pos_dev || !active_list_dev || !n_active_dev)
-        return moe::fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer argument");
-    if (!moe::aligned(x_dev, 2) || !moe::aligned(w_router_dev, 16))
-        return moe::fail(MOE_ERR_INVALID_ARG, "moe_route: x must be 2-byte and w_router 16-byte aligned");
-    const int HS = pick_slices(T, H);
-    if (HS < 1) return moe::fail(MOE_ERR_UNSUPPORTED, "moe_route: no slicing of H=%d", H);
-    const WsLayout L = ws_layout(T, HS, E);
-    if (!ws_dev || ws_bytes < L.total || !moe::aligned(ws_dev, 256))
-        return moe::fail(MOE_ERR_WORKSPACE, "moe_route: workspace needs %zu bytes, 256-byte aligned", L.total);
+    return route_launch(x_dev, w_router_dev, bias_dev, T, H, E, k, logits_dev, topk_ids_dev, topk_w_dev,
+                        expert_offsets_dev, sorted_pairs_dev, pair_pos_dev, active_list_dev, n_active_dev, ws_dev,
+                        ws_bytes, 0, stream);
+}
 
-    RouteArgs a;
-    a.x = (const uint16_t *)x_dev;
-    a.wr = (const uint16_t *)w_router_dev;
-    a.bias = bias_dev;
-    a.T = T; a.H = H; a.E = E; a.k = k;
-    a.HS = HS;
-    char *ws = (char *)ws_dev;
-    a.part = (long long *)(ws + L.part);
-    a.tok_ticket = (unsigned int *)(ws + L.tok);
-    a.glob_ticket = (unsigned int *)(ws + L.glob);
-    a.logits = logits_dev;
-    a.ids = topk_ids_dev;
-    a.w = topk_w_dev;
-    a.offsets = expert_offsets_dev;
-    a.sorted_pairs = sorted_pairs_dev;
-    a.pair_pos = pair_pos_dev;
-    a.active = active_list_dev;
-    a.n_active = n_active_dev;
-    const unsigned int blocks = (unsigned int)T * (unsigned int)a.HS;
-    hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, a);
-    return moe::check_launch("moe_route");
+int moe_route_exact(const void *x_dev, const void *w_router_dev, const float *bias_dev,
+                    int T, int H, int E, int k,
+                    float *logits_dev, int32_t *topk_ids_dev, float *topk_w_dev,
+                    int32_t *expert_offsets_dev, int32_t *sorted_pairs_dev, int32_t *pair_pos_dev,
+                    int32_t *active_list_dev, int32_t *n_active_dev, void *ws_dev, size_t ws_bytes, void *stream)
+{
+    return route_launch(x_dev, w_router_dev, bias_dev, T, H, E, k, logits_dev, topk_ids_dev, topk_w_dev,
+                        expert_offsets_dev, sorted_pairs_dev, pair_pos_dev, active_list_dev, n_active_dev, ws_dev,
+                        ws_bytes, 1, stream);
 }
 
 }  // extern "C"

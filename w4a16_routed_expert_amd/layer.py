@@ -46,18 +46,23 @@ class RoutedExpertLayer:
         self.active_list = torch.empty(E, dtype=torch.int32, device=d)
         self.n_active = torch.empty(1, dtype=torch.int32, device=d)
         self.ws_bytes = B.moe_route_workspace_size(T, H, E)
-        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=d)      # zero before first use
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=d)
         self.h = torch.empty((n, I), dtype=torch.float16, device=d)
         self.pair_out = torch.empty((n, H), dtype=torch.float32, device=d)
         self.status = torch.zeros(1, dtype=torch.int32, device=d)
 
-    def route(self, x: torch.Tensor, stream=None):
+    def route(self, x: torch.Tensor, stream=None, exact: bool = False):
         T = x.shape[0]
         if T > self.max_T:
             self._alloc(T)
-        B.moe_route(x, self.router, self.bias, T, self.H, self.E, self.k, self.logits, self.topk_ids, self.topk_w,
-                    self.expert_offsets, self.sorted_pairs, self.pair_pos, self.active_list, self.n_active, self.ws,
-                    self.ws_bytes, stream)
+        if exact:
+            B.moe_route_exact(x, self.router, self.bias, T, self.H, self.E, self.k, self.logits, self.topk_ids,
+                              self.topk_w, self.expert_offsets, self.sorted_pairs, self.pair_pos, self.active_list,
+                              self.n_active, self.ws, self.ws_bytes, stream)
+        else:
+            B.moe_route(x, self.router, self.bias, T, self.H, self.E, self.k, self.logits, self.topk_ids,
+                        self.topk_w, self.expert_offsets, self.sorted_pairs, self.pair_pos, self.active_list,
+                        self.n_active, self.ws, self.ws_bytes, stream)
 
     def ffn(self, x: torch.Tensor, stream=None, rows=None):
         T = x.shape[0]
