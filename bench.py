@@ -230,7 +230,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gateup_kernel (W4A16 gate/up + SiLU*up)",
+            "kernel": "w4a16_ffn_kernel<gate/up> (W4A16 gate/up + SiLU*up)",
             "achieved": gu_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -8,41 +8,57 @@
 // Precision & quality", paragraphs "Store" and "Compute": FP16 activations,
 // FP32 accumulation stages, explicit rounding).
 //
-// Kernel design (gfx950, wave64).  Decode batches are bandwidth-bound: the
-// kernels exist to keep HBM busy with qpacked bytes.
-//   * Work item = (active expert, RGW groups of 16 weight rows).  Blocks are
-//     persistent: block b walks the contiguous item range
-//     [b*N/G, (b+1)*N/G), so consecutive items usually share the expert and
-//     its activations stay in registers.
-//   * A block is 4 wavefronts; wave w owns 128-column tiles
-//     [w*NT/4, (w+1)*NT/4) of the reduction axis.  Partial sums meet in LDS
-//     (double-buffered, one barrier per item).
-//   * Prefetch without extra registers: as soon as a tile of item i has been
-//     converted to FP16, its registers are reloaded with the same tile of
-//     item i+1, so the next item's loads are in flight while item i finishes.
-//   * A 1024-byte qpacked tile is read by one 16-byte load per lane (fully
-//     coalesced).  Lane 16g + r gets row r, columns 32g .. 32g+31 of the tile:
-//     four 32-bit words, each the 8-value B operand of one
-//     v_mfma_f32_16x16x32_f16 after an exact INT4 -> FP16 conversion in
-//     registers (OR the nibble into the exponent of 1024.0, subtract).
-//   * The A operand is the FP16 activation of up to 16 routed tokens of the
-//     expert (missing tokens are zero), its elements permuted to the order
-//     the conversion produces.  More than 16 tokens take several passes over
-//     the same weight registers.
-//   * The FP16 block scale multiplies the FP32 partial of each tile (scales
-//     are per 256-column block and tiles never straddle a block), so weights
-//     are never rounded after scaling.
+// Kernel design (gfx950, wave64).  Decode batches are bound by HBM: the
+// kernels exist to keep it busy with qpacked bytes while spending as few
+// vector instructions per byte as possible.
+//   * Work unit of a wavefront = one token tile (up to 16 routed tokens of an
+//     expert) x one group of 16 weight rows x the whole reduction axis (or a
+//     1/S slice of it for small batches, S in {2, 4, 8}, reduced in LDS).
+//     The 8 wavefronts of a block take 8/S consecutive row groups of the
+//     same token tile; blocks are persistent and walk a contiguous range of
+//     such items, so the activations of a token tile are staged in LDS once
+//     and shared by every row group of the block.
+//   * Weights: one 16-byte buffer load per lane per 1024-byte tile (fully
+//     coalesced, scalar tile offset + fixed lane offset).  A ring of D tiles
+//     per matrix stays in flight; when a tile has been converted its
+//     registers are reloaded with the tile D steps ahead, which at the end of
+//     a unit is the first tile of the wavefront's next unit.  A unit that
+//     reads no weights (nothing left, rows past the matrix, absent expert)
+//     uses a buffer resource of 0 bytes: its loads return zeros and move no
+//     memory.
+//   * INT4 -> FP16 without arithmetic: a nibble moved to bits 4-7 of an FP16
+//     half and masked out is the subnormal 16 * code * 2^-24 = code * 2^-20.
+//     From a 32-bit word (8 codes, column 2i in the low nibble of byte i)
+//     w & 0x00F000F0 gives columns (1, 5), (w << 4) & .. columns (0, 4),
+//     (w >> 8) & .. columns (3, 7) and (w >> 4) & .. columns (2, 6): 7 vector
+//     instructions per 8 weights, one MFMA B operand.  The activation
+//     fragments in LDS are permuted to the same column order.  The matrix
+//     cores take these subnormals without loss: measured against an exact
+//     sum, code * 2^-20 operands err like FP32 rounding (2^-25 of the sum of
+//     |terms|), while code * 2^-24 (the nibble left at bits 0-3) loses bits
+//     (2^-19.6), so every nibble is moved up.
+//   * The zero point: sum x * (code - 8) = sum x * code - 8 * sum x.  The
+//     second term is per token and scale block, computed once while staging
+//     the activations, and enters as the initial accumulator of the block's
+//     MFMA chain.
+//   * Per scale block: acc += scale * P in FP32 (the FP16 scale multiplies the
+//     FP32 partial, weights are never rounded after scaling); the result is
+//     acc * 2^20.
 #include "moe_internal.h"
 
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxNT = 16;                       // reduction axis <= 2048 columns
+constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit data format (gfx9 family)
+constexpr float kUnit = 1048576.0f;               // 2^20: a code c enters the MFMA as c * 2^-20
+constexpr float kZeroPoint = -8.0f / 1048576.0f;  // -8 * 2^-20
+constexpr uint32_t kNib = 0x00F000F0u;            // bits 4-7 of each half
 
 struct FfnArgs {
     const uint16_t *x;          // [T][H] FP16
@@ -57,43 +73,17 @@ struct FfnArgs {
     uint16_t *h;                // [T*k][I] FP16
     float *out;                 // [T*k][H] FP32
     int32_t *status;
-    size_t off_gq, off_uq, off_dq, off_gs, off_us, off_ds;
+    int row_bytes;
+    int off_q[3], off_s[3];     // gate, up, down sections of a row
 };
+
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ inline u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// 8 INT4 codes of one 32-bit word (columns c..c+7; column c+2i in the low
-// nibble of byte i, c+2i+1 in the high nibble) -> FP16 (code - 8), exact, in
-// the order (c, c+4, c+1, c+5, c+2, c+6, c+3, c+7).
-__device__ inline half8 dequant8(uint32_t w)
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const uint8_t *base, int nbytes)
 {
-    const uint32_t s = w >> 8;
-    const uint32_t p0 = (w & 0x000F000Fu) | 0x64006400u;   // 1024 + code        (c,   c+4)
-    const uint32_t p1 = (w & 0x00F000F0u) | 0x64006400u;   // 1024 + 16 * code   (c+1, c+5)
-    const uint32_t p2 = (s & 0x000F000Fu) | 0x64006400u;   //                    (c+2, c+6)
-    const uint32_t p3 = (s & 0x00F000F0u) | 0x64006400u;   //                    (c+3, c+7)
-    const half2v k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const half2v k1_16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const half2v k72 = {(_Float16)72.0f, (_Float16)72.0f};
-    const half2v h0 = __builtin_bit_cast(half2v, p0) - k1032;
-    const half2v h1 = __builtin_bit_cast(half2v, p1) * k1_16 - k72;
-    const half2v h2 = __builtin_bit_cast(half2v, p2) - k1032;
-    const half2v h3 = __builtin_bit_cast(half2v, p3) * k1_16 - k72;
-    half8 r;
-    r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
-    r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];
-    return r;
-}
-
-// 8 consecutive FP16 activations (x0..x7 in 4 dwords) -> the order of dequant8.
-__device__ inline half8 act8(u32x4 d)
-{
-    u32x4 p;
-    p[0] = (d[0] & 0xFFFFu) | (d[2] << 16);           // x0, x4
-    p[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);       // x1, x5
-    p[2] = (d[1] & 0xFFFFu) | (d[3] << 16);           // x2, x6
-    p[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);       // x3, x7
-    return __builtin_bit_cast(half8, p);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, nbytes, kRsrcWord3);
 }
 
 __device__ inline f32x4 mfma(half8 a, half8 b, f32x4 c)
@@ -102,6 +92,22 @@ __device__ inline f32x4 mfma(half8 a, half8 b, f32x4 c)
 }
 
 __device__ inline uint16_t float_to_half_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+__device__ inline float half_bits_to_float(uint32_t b)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xFFFFu));
+}
+
+// FP16 scale -> float, converted at this point of the program so the
+// register that held it can be reloaded at once (left to itself the compiler
+// folds the conversion into a later mixed-precision FMA, which keeps the old
+// value alive past the reload and costs a copy and an early wait).
+__device__ inline float scale_f32(_Float16 h)
+{
+    float f;
+    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(h));
+    return f;
+}
 
 // Barrier that orders LDS only: prefetched global loads stay in flight across it
 // (__syncthreads() would also wait for every outstanding global load).
@@ -112,17 +118,9 @@ __device__ inline void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// FP16 scale bits (low half of a register) -> float, as an explicit conversion
-// at this point of the program (the compiler would otherwise fold it into a
-// later mixed-precision FMA and keep the half register alive past its refill).
-__device__ inline float scale_f32(uint32_t bits)
-{
-    float f;
-    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(bits));
-    return f;
-}
+// Two FP16 values from the low (lo) or high (hi) halves of two dwords.
+__device__ inline uint32_t lo2(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ inline uint32_t hi2(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
 // Per-block table of the active slots, built once in LDS: expert, first
 // grouped pair, pair count, device slot and the first work item of the slot.
@@ -159,8 +157,7 @@ __device__ void build_table(SlotTable &tb, const FfnArgs &a, const int32_t *__re
             e = -1;
         }
     }
-    int cnt = (e >= 0) ? ((n + 15) / 16) * items_per_tile : 0;
-    // inclusive scan of the item counts across the wave
+    const int cnt = (e >= 0) ? ((n + 15) / 16) * items_per_tile : 0;
     int incl = cnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -177,222 +174,325 @@ __device__ void build_table(SlotTable &tb, const FfnArgs &a, const int32_t *__re
     if (lane == 0) tb.first[0] = 0;
 }
 
-// One work item: 16 tokens (tile mt) of one active slot x RGW row groups.
-struct Item {
-    int slot, mt, rg0;
-    int e, p0, n, sl;
-    const uint8_t *row;     // expert row; for an absent expert, slot 0's row (read but never used)
+// Tiles kept in flight per matrix: the whole unit when it is short, else the
+// largest divisor of the unit's tile count with at most 8 tiles of weights
+// (an even one when there is one, so scale blocks never straddle rounds).
+constexpr int ring_depth(int ntw, int nmat)
+{
+    if (ntw * nmat <= 12) return ntw;
+    int best = 1, best_even = 0;
+    for (int d = 1; d * nmat <= 8; ++d)
+        if (ntw % d == 0) {
+            best = d;
+            if (d % 2 == 0) best_even = d;
+        }
+    return best_even ? best_even : best;
+}
+
+template <int NT, int S, int NMAT>
+struct Shared {
+    static constexpr int RS = S > 1 ? 1 : 0;
+    u32x4 xl[NT * 4 * 64];            // activation fragments [tile][kind][lane]
+    float sx[(NT + 1) / 2][16];       // -8 * 2^-20 * (sum of a token's activations over a scale block)
+    float sxp[NT][4][16];             // staging partial sums [tile][32-column group][token]
+    float red[RS ? S - 1 : 1][RS ? kWaves / S : 1][RS ? NMAT : 1][RS ? 4 : 1][RS ? 64 : 1];
+    SlotTable tb;
 };
 
-// Per-item register buffer: weights and scales of NMAT matrices x RGW row groups x MAXT tiles.
-template <int NMAT, int RGW, int MAXT>
-struct WBuf {
-    u32x4 w[NMAT][RGW][MAXT];
-    uint32_t s[NMAT][RGW][MAXT];      // FP16 scale bits, one register each (no packing on refill)
+// What one wavefront computes in one item.
+struct Unit {
+    const uint8_t *row;   // expert row (the rows base when nothing is read)
+    int nrec;             // bytes the loads may read; 0: loads return zeros
+    int slot;             // index into the slot table, -1 = no item
+    int mt;               // token tile of the slot
+    int rg;               // row group (valid when < RG)
+    int p0;               // first grouped pair of the token tile
+    int nval;             // tokens in the tile (1..16)
+    bool write;           // the unit has rows to write
+    bool absent;          // the expert has no device row
 };
 
-template <int NMAT, int RGW, int MAXT, bool GATEUP>
-struct Stream {
+template <bool GATEUP, int NT, int S>
+struct Ffn {
+    static constexpr int NMAT = GATEUP ? 2 : 1;
+    static constexpr int NTW = NT / S;          // tiles of one wavefront
+    static constexpr int RGB = kWaves / S;      // row groups per item
+    static constexpr int NB = (NT + 1) / 2;     // scale blocks of the reduction axis
+    static constexpr int D = ring_depth(NTW, NMAT);
+    static_assert(NT >= 1 && NT <= kMaxNT, "reduction axis of 128 .. 2048 columns");
+    static_assert(NT % S == 0 && (S == 1 || NTW % 2 == 0), "split slices cover whole scale blocks");
+    static_assert(NTW % D == 0, "ring depth divides the unit");
+
+    using Lds = Shared<NT, S, NMAT>;
+
     const FfnArgs &a;
-    int K, R, NT, NB, RGI;          // reduction length, rows per matrix, tiles, blocks, items per token tile
-    int kb, ke;                     // this wave's tile range
-    int lane, wave, r16, g4;
-    size_t offq[NMAT], offs[NMAT];
+    Lds &L;
+    int lane, wave, g4, n16, ks, rgl, t0;
+    int RG, CH;               // row groups of the output, items per token tile
+    int nact;
 
-    __device__ Stream(const FfnArgs &args) : a(args)
+    __device__ Ffn(const FfnArgs &args, Lds &lds, int nact_) : a(args), L(lds), nact(nact_)
     {
-        K = GATEUP ? a.H : a.I;
-        R = GATEUP ? a.I : a.H;
-        NT = K / 128;
-        NB = (K + 255) / 256;
-        RGI = R / 16 / RGW;
         const int tid = threadIdx.x;
         lane = tid & 63;
-        wave = uni(tid >> 6);           // wave-uniform: tile ranges and addresses stay scalar
-        r16 = lane & 15;
+        wave = uni(tid >> 6);
         g4 = lane >> 4;
-        kb = wave * NT / kWaves;
-        ke = (wave + 1) * NT / kWaves;
-        if (GATEUP) {
-            offq[0] = a.off_gq; offs[0] = a.off_gs;
-            offq[NMAT - 1] = a.off_uq; offs[NMAT - 1] = a.off_us;
-        } else {
-            offq[0] = a.off_dq; offs[0] = a.off_ds;
-        }
+        n16 = lane & 15;
+        ks = wave % S;
+        rgl = wave / S;
+        t0 = ks * NTW;
+        RG = (GATEUP ? a.I : a.H) / 16;
+        CH = (RG + RGB - 1) / RGB;
     }
 
-    // Work item `it` of the block-wide enumeration (slot-major, then token tile, then row groups).
-    __device__ Item item(const SlotTable &tb, int nact, int it, int slot_hint) const
+    // Unit of this wavefront in item `it` (slot search starts at `hint`).
+    __device__ Unit unit(int it, int hint) const
     {
-        int s = slot_hint;
-        while (s + 1 < nact && tb.first[s + 1] <= it) ++s;
+        int s = hint;
+        while (s + 1 < nact && L.tb.first[s + 1] <= it) ++s;
         s = uni(s);
-        Item m;
-        m.slot = s;
-        const int local = uni(it - tb.first[s]);
-        m.mt = local / RGI;
-        m.rg0 = (local % RGI) * RGW;
-        m.e = uni(tb.e[s]);
-        m.p0 = uni(tb.p0[s]);
-        m.n = uni(tb.n[s]);
-        m.sl = uni(tb.sl[s]);
-        m.row = a.rows + (size_t)(m.sl >= 0 ? m.sl : 0) * a.stride;
-        return m;
+        Unit u;
+        u.slot = s;
+        const int local = uni(it - L.tb.first[s]);
+        u.mt = local / CH;
+        const int c = local - u.mt * CH;
+        const int n = uni(L.tb.n[s]);
+        const int sl = uni(L.tb.sl[s]);
+        u.p0 = uni(L.tb.p0[s]) + 16 * u.mt;
+        u.nval = min(16, n - 16 * u.mt);
+        u.rg = c * RGB + rgl;
+        u.absent = sl < 0;
+        u.write = u.rg < RG;
+        const bool reads = u.write && !u.absent;
+        u.row = a.rows + (reads ? (size_t)sl * a.stride : 0);
+        u.nrec = reads ? a.row_bytes : 0;
+        if (!u.write) u.rg = 0;
+        return u;
     }
 
-    // Loads tile j of row group rg0 + r, matrix mat: scalar row base + scalar
-    // tile offset + per-lane offset.
-    __device__ void load_tile(WBuf<NMAT, RGW, MAXT> &b, const Item &m, int mat, int r, int j) const
+    __device__ Unit none() const
     {
-        const uint8_t *qbase = m.row + offq[mat] + ((size_t)(m.rg0 + r) * NT + kb + j) * 1024;
-        const uint16_t *sbase = reinterpret_cast<const uint16_t *>(m.row + offs[mat]) +
-                                ((size_t)(m.rg0 + r) * NB + ((kb + j) >> 1)) * 16;
-        b.w[mat][r][j] = ld16(qbase + lane * 16);
-        b.s[mat][r][j] = sbase[r16];
+        Unit u;
+        u.row = a.rows;
+        u.nrec = 0;
+        u.slot = -1;
+        u.mt = 0;
+        u.rg = 0;
+        u.p0 = 0;
+        u.nval = 0;
+        u.write = false;
+        u.absent = false;
+        return u;
     }
 
-    __device__ void issue(WBuf<NMAT, RGW, MAXT> &b, const Item &m) const
+    // Tile j of a unit (row base, readable bytes, row group) of matrix mat.
+    __device__ u32x4 load_q(const uint8_t *row, int nrec, int rg, int mat, int j) const
     {
-#pragma unroll
-        for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-            for (int r = 0; r < RGW; ++r)
-#pragma unroll
-                for (int j = 0; j < MAXT; ++j)
-                    if (kb + j < ke) load_tile(b, m, mat, r, j);
+        const int qm = GATEUP ? a.off_q[mat] : a.off_q[2];
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc(row, nrec), lane * 16, qm + ((rg * NT) + t0 + j) * 1024, 0);
     }
 
-    // A-operand fragments of the item's 16 tokens, in the element order of dequant8.
-    __device__ void load_x(half8 (&X)[MAXT][4], const Item &m) const
+    // FP16 scale of the block of tile j, row n16 of the row group.
+    __device__ _Float16 load_s(const uint8_t *row, int nrec, int rg, int mat, int j) const
     {
-        const uint16_t *src = nullptr;
-        const int pi = m.mt * 16 + r16;
-        if (pi < m.n) {
-            if (GATEUP) {
-                const int tok = a.sorted_pairs[m.p0 + pi] / a.k;
-                if (tok >= 0 && tok < a.T) src = a.x + (size_t)tok * a.H + 32 * g4;
-            } else {
-                src = a.h + (size_t)(m.p0 + pi) * a.I + 32 * g4;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < MAXT; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                X[j][q] = act8((src && kb + j < ke) ? ld16(src + 128 * (kb + j) + 8 * q) : u32x4{0u, 0u, 0u, 0u});
+        const int sm = GATEUP ? a.off_s[mat] : a.off_s[2];
+        const uint16_t b = __builtin_amdgcn_raw_buffer_load_b16(rsrc(row, nrec), n16 * 2,
+                                                                 sm + (rg * NB + (t0 + j) / 2) * 32, 0);
+        return __builtin_bit_cast(_Float16, b);
     }
 
-    // Computes item m from the weights in b.  If nxt is given, each tile's
-    // registers are reloaded with the same tile of item nxt right after the
-    // tile has been converted.  Ends with the LDS reduction and the epilogue.
-    __device__ void compute(const Item &m, WBuf<NMAT, RGW, MAXT> &b, const half8 (&X)[MAXT][4], const Item *nxt,
-                            float (*red)[kWaves][NMAT * RGW][4][64], int &rbuf) const
+    // Activations of a token tile -> LDS fragments (permuted to the column
+    // order of the weight conversion) and per-block sums for the zero point.
+    __device__ void stage(const Unit &u) const
     {
-        f32x4 acc[NMAT][RGW];
-#pragma unroll
-        for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-            for (int r = 0; r < RGW; ++r) acc[mat][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < MAXT; ++j) {
-            if (kb + j < ke) {
-#pragma unroll
-                for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-                    for (int r = 0; r < RGW; ++r) {
-                        half8 d[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) d[q] = dequant8(b.w[mat][r][j][q]);
-                        const float sc = scale_f32(b.s[mat][r][j]);
-                        if (nxt) {
-                            // every read of this tile's registers happens before they are
-                            // reloaded, so the refill reuses them (no copies, no early wait)
-                            __builtin_amdgcn_sched_barrier(0);
-                            load_tile(b, *nxt, mat, r, j);
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                        f32x4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) p = mfma(X[j][q], d[q], p);
-                        acc[mat][r] += sc * p;
-                    }
-            }
-        }
-        float (*rd)[NMAT * RGW][4][64] = red[rbuf];
-#pragma unroll
-        for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-            for (int r = 0; r < RGW; ++r)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) rd[wave][mat * RGW + r][v][lane] = acc[mat][r][v];
-        lds_barrier();
-        // waves 0..3: wave v finishes token mt*16 + 4*g4 + v, row r16 of each row group.
-        // An absent expert (no device row) gets zeros and flags the status word.
-        const bool gone = m.sl < 0;
-        if (gone && threadIdx.x == 0 && a.status) *a.status = MOE_ERR_ABSENT_EXPERT;
-        if (wave < 4) {
-            const int v = wave;
-            const int i = m.mt * 16 + 4 * g4 + v;
-            if (i < m.n) {
-                const size_t p = (size_t)(m.p0 + i);
+        lds_barrier();                     // every wave is done with the previous tile
+        const int nval = u.nval;
+        for (int task = threadIdx.x; task < 16 * NT * 4; task += kThreads) {
+            const int m = task & 15, tg = task >> 4;
+            const int t = tg >> 2, g = tg & 3;
+            u32x4 d0 = {0u, 0u, 0u, 0u}, d1 = d0, d2 = d0, d3 = d0;
+            if (m < nval) {
+                const uint16_t *src = nullptr;
                 if (GATEUP) {
-                    float g = 0.f, u = 0.f;
-#pragma unroll
-                    for (int w = 0; w < kWaves; ++w) { g += rd[w][0][v][lane]; u += rd[w][1][v][lane]; }
-                    a.h[p * a.I + m.rg0 * 16 + r16] = gone ? (uint16_t)0 : float_to_half_bits(g / (1.0f + expf(-g)) * u);
+                    const int tok = a.sorted_pairs[u.p0 + m] / a.k;
+                    if (tok >= 0 && tok < a.T) src = a.x + (size_t)tok * a.H;
                 } else {
+                    src = a.h + (size_t)(u.p0 + m) * a.I;
+                }
+                if (src) {
+                    src += 128 * t + 32 * g;
+                    d0 = ld16(src);
+                    d1 = ld16(src + 8);
+                    d2 = ld16(src + 16);
+                    d3 = ld16(src + 24);
+                }
+            }
+            u32x4 *dst = &L.xl[(t * 4) * 64 + g * 16 + m];
+            // kind q holds columns 8q + (1, 5, 0, 4, 3, 7, 2, 6) of the group,
+            // the order in which the weight conversion yields them
+            dst[0] = u32x4{hi2(d0[0], d0[2]), lo2(d0[0], d0[2]), hi2(d0[1], d0[3]), lo2(d0[1], d0[3])};
+            dst[64] = u32x4{hi2(d1[0], d1[2]), lo2(d1[0], d1[2]), hi2(d1[1], d1[3]), lo2(d1[1], d1[3])};
+            dst[128] = u32x4{hi2(d2[0], d2[2]), lo2(d2[0], d2[2]), hi2(d2[1], d2[3]), lo2(d2[1], d2[3])};
+            dst[192] = u32x4{hi2(d3[0], d3[2]), lo2(d3[0], d3[2]), hi2(d3[1], d3[3]), lo2(d3[1], d3[3])};
+            float s = 0.f;
 #pragma unroll
-                    for (int r = 0; r < RGW; ++r) {
-                        float o = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                s += half_bits_to_float(d0[i]) + half_bits_to_float(d0[i] >> 16);
+                s += half_bits_to_float(d1[i]) + half_bits_to_float(d1[i] >> 16);
+                s += half_bits_to_float(d2[i]) + half_bits_to_float(d2[i] >> 16);
+                s += half_bits_to_float(d3[i]) + half_bits_to_float(d3[i] >> 16);
+            }
+            L.sxp[t][g][m] = s;
+        }
+        lds_barrier();
+        for (int i = threadIdx.x; i < NB * 16; i += kThreads) {
+            const int b = i >> 4, m = i & 15;
+            float s = 0.f;
+            for (int t = 2 * b; t < 2 * b + 2 && t < NT; ++t)
 #pragma unroll
-                        for (int w = 0; w < kWaves; ++w) o += rd[w][r][v][lane];
-                        a.out[p * a.H + (m.rg0 + r) * 16 + r16] = gone ? 0.0f : o;
-                    }
+                for (int g = 0; g < 4; ++g) s += L.sxp[t][g][m];
+            L.sx[b][m] = s * kZeroPoint;
+        }
+        lds_barrier();
+    }
+
+    // One unit: stream the weight tiles through the ring, refilling each slot
+    // with the tile D steps ahead (from unit `nxt` past the end), then write
+    // the unit's outputs.  Rounds of D tiles run as a loop, so the ring slot
+    // of every tile is fixed and the loop carries the ring in place.
+    __device__ void run(const Unit &cur, const Unit &nxt, u32x4 (&wq)[D][NMAT], _Float16 (&ws)[D][NMAT]) const
+    {
+        constexpr int NR = NTW / D;
+        const u32x4 *xl = &L.xl[t0 * 4 * 64 + lane];
+        const f32x4 *sx = reinterpret_cast<const f32x4 *>(&L.sx[t0 / 2][4 * g4]);
+        f32x4 acc[NMAT], p[NMAT];
+#pragma unroll
+        for (int mat = 0; mat < NMAT; ++mat) acc[mat] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int jo = 0; jo < NR; ++jo) {
+            // the refills of this round: the next round of this unit, or the
+            // first round of the next unit
+            const bool last = jo == NR - 1;
+            const uint8_t *rrow = last ? nxt.row : cur.row;
+            const int rnrec = last ? nxt.nrec : cur.nrec;
+            const int rrg = last ? nxt.rg : cur.rg;
+            const int rj0 = last ? 0 : (jo + 1) * D;
+#pragma unroll
+            for (int jd = 0; jd < D; ++jd) {
+                const int j = jo * D + jd;
+                if (j % 2 == 0) {
+                    const f32x4 z = sx[(j / 2) * 4];      // zero-point term of this scale block
+#pragma unroll
+                    for (int mat = 0; mat < NMAT; ++mat) p[mat] = z;
+                }
+                half8 xa[4];
+#pragma unroll
+                for (int kd = 0; kd < 4; ++kd) xa[kd] = __builtin_bit_cast(half8, xl[(j * 4 + kd) * 64]);
+                const bool merge = (j % 2 == 1) || (j == NTW - 1);
+                float sc[NMAT];
+#pragma unroll
+                for (int mat = 0; mat < NMAT; ++mat) {
+                    const u32x4 w = wq[jd][mat];
+                    half8 b[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        b[q] = __builtin_bit_cast(half8, u32x4{w[q] & kNib, (w[q] << 4) & kNib, (w[q] >> 8) & kNib,
+                                                               (w[q] >> 4) & kNib});
+                    sc[mat] = scale_f32(ws[jd][mat]);
+                    // every read of this slot happens above: reload it in place
+                    __builtin_amdgcn_sched_barrier(0);
+                    wq[jd][mat] = load_q(rrow, rnrec, rrg, mat, rj0 + jd);
+                    ws[jd][mat] = load_s(rrow, rnrec, rrg, mat, rj0 + jd);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) p[mat] = mfma(xa[q], b[q], p[mat]);
+                }
+                if (merge) {
+#pragma unroll
+                    for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[mat][r] += sc[mat] * p[mat][r];
                 }
             }
         }
-        rbuf ^= 1;              // the next item writes the other buffer: one barrier per item
+        if (S > 1) {
+            // K slices 1..S-1 hand their partials to slice 0 of the same row group
+            if (ks > 0) {
+#pragma unroll
+                for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) L.red[ks - 1][rgl][mat][r][lane] = acc[mat][r];
+            }
+            lds_barrier();
+            if (ks == 0) {
+#pragma unroll
+                for (int q = 1; q < S; ++q)
+#pragma unroll
+                    for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[mat][r] += L.red[q - 1][rgl][mat][r][lane];
+            }
+            lds_barrier();
+            if (ks != 0) return;
+        }
+        if (!cur.write) return;
+        if (cur.absent && lane == 0 && a.status) *a.status = MOE_ERR_ABSENT_EXPERT;
+        // lane (g4, n16) holds tokens 4*g4 + r of row n16 of the row group
+        const int col = cur.rg * 16 + n16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * g4 + r;
+            if (m < cur.nval) {
+                const size_t pr = (size_t)(cur.p0 + m);
+                if constexpr (GATEUP) {
+                    const float g = acc[0][r] * kUnit, u = acc[NMAT - 1][r] * kUnit;
+                    a.h[pr * a.I + col] = cur.absent ? (uint16_t)0 : float_to_half_bits(g / (1.0f + expf(-g)) * u);
+                } else {
+                    a.out[pr * a.H + col] = cur.absent ? 0.0f : acc[0][r] * kUnit;
+                }
+            }
+        }
     }
 };
 
-template <int NMAT, int RGW, int MAXT, bool GATEUP>
-__global__ __launch_bounds__(kThreads) void w4a16_stream_kernel(FfnArgs a, const int32_t *__restrict__ active,
-                                                                const int32_t *__restrict__ offsets,
-                                                                const int32_t *__restrict__ slot_map,
-                                                                const int32_t *__restrict__ n_active)
+template <bool GATEUP, int NT, int S>
+__global__ __launch_bounds__(kThreads) void w4a16_ffn_kernel(FfnArgs a, const int32_t *__restrict__ active,
+                                                             const int32_t *__restrict__ offsets,
+                                                             const int32_t *__restrict__ slot_map,
+                                                             const int32_t *__restrict__ n_active)
 {
-    static_assert(!GATEUP || (NMAT == 2 && RGW == 1), "gate/up items are one row group of both matrices");
-    __shared__ float red[2][kWaves][NMAT * RGW][4][64];
-    __shared__ SlotTable tb;
-    const Stream<NMAT, RGW, MAXT, GATEUP> S(a);
+    using F = Ffn<GATEUP, NT, S>;
+    __shared__ typename F::Lds L;
     int nact = *n_active;
     if (nact > a.E) nact = a.E;
     if (nact <= 0) return;
-    if (threadIdx.x < 64) build_table(tb, a, active, offsets, slot_map, nact, S.RGI);
+    const F f(a, L, nact);
+    if (threadIdx.x < 64) build_table(L.tb, a, active, offsets, slot_map, nact, f.CH);
     __syncthreads();
-    const long long N = tb.first[nact];
+    const long long N = L.tb.first[nact];
     const int it0 = (int)(N * blockIdx.x / gridDim.x), it1 = (int)(N * (blockIdx.x + 1) / gridDim.x);
     if (it0 >= it1) return;
 
-    WBuf<NMAT, RGW, MAXT> w;
-    half8 X[MAXT][4];
-    int rbuf = 0;
-    Item cur = S.item(tb, nact, it0, 0);
-    S.issue(w, cur);
-    S.load_x(X, cur);
-    // Every item but the last refills the weight registers with the next
-    // item's tiles while it is computed; the body is the same for every item
-    // so the refilled registers need no copies on the loop's back edge.
-    for (int it = it0; it + 1 < it1; ++it) {
-        const Item nxt = S.item(tb, nact, it + 1, cur.slot);
-        S.compute(cur, w, X, &nxt, red, rbuf);
-        if (nxt.slot != cur.slot || nxt.mt != cur.mt) S.load_x(X, nxt);
+    u32x4 wq[F::D][F::NMAT];
+    _Float16 ws[F::D][F::NMAT];
+    Unit cur = f.unit(it0, 0);
+#pragma unroll
+    for (int j = 0; j < F::D; ++j)
+#pragma unroll
+        for (int mat = 0; mat < F::NMAT; ++mat) {
+            wq[j][mat] = f.load_q(cur.row, cur.nrec, cur.rg, mat, j);
+            ws[j][mat] = f.load_s(cur.row, cur.nrec, cur.rg, mat, j);
+        }
+    f.stage(cur);
+    // The body is the same for every item, so the ring registers need no
+    // copies on the loop's back edge.
+    for (int it = it0; it < it1; ++it) {
+        const Unit nxt = (it + 1 < it1) ? f.unit(it + 1, cur.slot) : f.none();
+        f.run(cur, nxt, wq, ws);
+        if (nxt.slot >= 0 && (nxt.slot != cur.slot || nxt.mt != cur.mt)) f.stage(nxt);
         cur = nxt;
     }
-    S.compute(cur, w, X, nullptr, red, rbuf);
 }
-
-constexpr int kDownRGW = 2;
 
 int cu_count()
 {
@@ -410,33 +510,83 @@ int cu_count()
     return 256;
 }
 
-// Launch: the number of 128-column tiles per wave selects the template
-// instance; the grid is one wave of resident blocks (CUs x occupancy), capped
-// by an upper bound of the number of work items.
-template <int NMAT, int RGW, bool GATEUP>
-int launch_stream(const FfnArgs &a, hipStream_t s, const char *who)
+template <bool GATEUP, int NT, int S>
+int launch_one(const FfnArgs &a, hipStream_t s, long long max_items, const char *who)
+{
+    auto kern = w4a16_ffn_kernel<GATEUP, NT, S>;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess || occ <= 0) occ = 1;
+    long long g = (long long)cu_count() * occ;
+    if (g > max_items) g = max_items;
+    if (g < 1) g = 1;
+    hipLaunchKernelGGL(kern, dim3((unsigned int)g), dim3(kThreads), 0, s, a, a.active, a.offsets, a.slot_map,
+                       a.n_active);
+    return moe::check_launch(who);
+}
+
+// Split of the reduction axis: the smallest S that gives about 16 resident
+// wavefronts per CU of work, from the expected number of routed experts of a
+// uniform router (a launch-shape choice only: any S gives the same sums in
+// the same order per slice).
+int choose_split(int NT, int RG, int T, int k, int E)
+{
+    const double P = (double)T * k;
+    double miss = 1.0;
+    for (int i = 0; i < T && miss > 1e-9; ++i) miss *= 1.0 - (double)k / E;
+    const double slots = E * (1.0 - miss) + P / 16.0;
+    const double waves = 16.0 * cu_count();
+    int S = 1;
+    while (S < 8 && slots * RG * S < waves) {
+        const int n = S * 2;
+        if (NT % n || (NT / n) % 2) break;
+        S = n;
+    }
+    return S;
+}
+
+template <bool GATEUP, int NT>
+int launch_nt(const FfnArgs &a, hipStream_t s, int S, long long max_items, const char *who)
+{
+    if constexpr (NT % 4 == 0) {
+        if (S == 2) return launch_one<GATEUP, NT, 2>(a, s, max_items * 2, who);
+    }
+    if constexpr (NT % 8 == 0) {
+        if (S == 4) return launch_one<GATEUP, NT, 4>(a, s, max_items * 4, who);
+    }
+    if constexpr (NT % 16 == 0) {
+        if (S == 8) return launch_one<GATEUP, NT, 8>(a, s, max_items * 8, who);
+    }
+    return launch_one<GATEUP, NT, 1>(a, s, max_items, who);
+}
+
+template <bool GATEUP>
+int launch_ffn(const FfnArgs &a, hipStream_t s, const char *who)
 {
     const int K = GATEUP ? a.H : a.I;
     const int R = GATEUP ? a.I : a.H;
-    const int maxt = (K / 128 + kWaves - 1) / kWaves;
+    const int NT = K / 128, RG = R / 16;
     const long long pairs = (long long)a.T * a.k;
     const long long max_slots = pairs < a.E ? pairs : a.E;
-    const long long max_items = (max_slots + pairs / 16) * (R / 16 / RGW);
-    const int cus = cu_count();
-    auto go = [&](auto kern) {
-        int occ = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess || occ <= 0) occ = 1;
-        long long g = (long long)cus * occ;
-        if (g > max_items) g = max_items;
-        if (g < 1) g = 1;
-        hipLaunchKernelGGL(kern, dim3((unsigned int)g), dim3(kThreads), 0, s, a, a.active, a.offsets, a.slot_map,
-                           a.n_active);
-        return moe::check_launch(who);
-    };
-    switch (maxt) {
-    case 1: return go(w4a16_stream_kernel<NMAT, RGW, 1, GATEUP>);
-    case 2: return go(w4a16_stream_kernel<NMAT, RGW, 2, GATEUP>);
-    default: return moe::fail(MOE_ERR_UNSUPPORTED, "%s: reduction length %d > 2048", who, K);
+    const long long max_items = (max_slots + pairs / 16) * ((RG + kWaves - 1) / kWaves);
+    const int S = choose_split(NT, RG, a.T, a.k, a.E);
+    switch (NT) {
+    case 1: return launch_nt<GATEUP, 1>(a, s, S, max_items, who);
+    case 2: return launch_nt<GATEUP, 2>(a, s, S, max_items, who);
+    case 3: return launch_nt<GATEUP, 3>(a, s, S, max_items, who);
+    case 4: return launch_nt<GATEUP, 4>(a, s, S, max_items, who);
+    case 5: return launch_nt<GATEUP, 5>(a, s, S, max_items, who);
+    case 6: return launch_nt<GATEUP, 6>(a, s, S, max_items, who);
+    case 7: return launch_nt<GATEUP, 7>(a, s, S, max_items, who);
+    case 8: return launch_nt<GATEUP, 8>(a, s, S, max_items, who);
+    case 9: return launch_nt<GATEUP, 9>(a, s, S, max_items, who);
+    case 10: return launch_nt<GATEUP, 10>(a, s, S, max_items, who);
+    case 11: return launch_nt<GATEUP, 11>(a, s, S, max_items, who);
+    case 12: return launch_nt<GATEUP, 12>(a, s, S, max_items, who);
+    case 13: return launch_nt<GATEUP, 13>(a, s, S, max_items, who);
+    case 14: return launch_nt<GATEUP, 14>(a, s, S, max_items, who);
+    case 15: return launch_nt<GATEUP, 15>(a, s, S, max_items, who);
+    case 16: return launch_nt<GATEUP, 16>(a, s, S, max_items, who);
+    default: return moe::fail(MOE_ERR_UNSUPPORTED, "%s: reduction length %d > %d", who, K, kMaxNT * 128);
     }
 }
 
@@ -448,7 +598,8 @@ int make_args(FfnArgs &a, const void *x_dev, int T, int H, int I, int E, int k, 
     int rc = moe::check_shape(T, H, I, E, k, true);
     if (rc) return rc;
     if (T == 0) return -1;          // nothing to do; callers return MOE_OK
-    if (H > 2048 || I > 2048) return moe::fail(MOE_ERR_UNSUPPORTED, "%s: H and I must be <= 2048", who);
+    if (H > kMaxNT * 128 || I > kMaxNT * 128)
+        return moe::fail(MOE_ERR_UNSUPPORTED, "%s: H and I must be <= %d", who, kMaxNT * 128);
     size_t off[6];
     const size_t rb = moe::row_bytes(H, I, off);
     if (!rows_dev || !expert_offsets_dev || !active_list_dev || !n_active_dev || !h_dev)
@@ -471,20 +622,17 @@ int make_args(FfnArgs &a, const void *x_dev, int T, int H, int I, int E, int k, 
     a.h = (uint16_t *)h_dev;
     a.out = pair_out_dev;
     a.status = status_dev;
-    a.off_gq = off[0]; a.off_uq = off[1]; a.off_dq = off[2];
-    a.off_gs = off[3]; a.off_us = off[4]; a.off_ds = off[5];
+    a.row_bytes = (int)rb;          // < 2^31 for H, I <= 2048
+    for (int i = 0; i < 3; ++i) {
+        a.off_q[i] = (int)off[i];
+        a.off_s[i] = (int)off[3 + i];
+    }
     return MOE_OK;
 }
 
-int launch_gateup(const FfnArgs &a, hipStream_t s)
-{
-    return launch_stream<2, 1, true>(a, s, "moe_w4a16_gateup");
-}
+int launch_gateup(const FfnArgs &a, hipStream_t s) { return launch_ffn<true>(a, s, "moe_w4a16_gateup"); }
 
-int launch_down(const FfnArgs &a, hipStream_t s)
-{
-    return launch_stream<1, kDownRGW, false>(a, s, "moe_w4a16_down");
-}
+int launch_down(const FfnArgs &a, hipStream_t s) { return launch_ffn<false>(a, s, "moe_w4a16_down"); }
 
 }  // namespace
 
