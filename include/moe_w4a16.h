@@ -94,7 +94,9 @@ size_t moe_expert_row_bytes(int H, int I, size_t *off6);
 
 /* ------------------------------------------------------------ routing
  * moe_route: router logits, top-k softmax and token-to-expert grouping (two
- * kernel launches: logits, then one block for top-k and the grouping).
+ * kernel launches: for T <= 256 logits spread over many blocks, then one
+ * block for top-k and the grouping; for larger T per-token logits and top-k,
+ * then the grouping).
  *   logit[t][e] = RN32( exact sum_h x[t][h] * w_router[h][e] ) (+ bias[e])
  *     The correctly rounded FP32 value of the exact dot product of FP16
  *     values, so the selected experts do not depend on summation order.  The
@@ -111,10 +113,10 @@ size_t moe_expert_row_bytes(int H, int I, size_t *off6);
  *   logits_dev: FP32 [T][E] copy of the logits (bias included), or NULL.
  * Inputs:  x_dev FP16 [T][H] row-major; w_router_dev FP16 [H][E] row-major;
  *          bias_dev FP32 [E] or NULL.
- * ws_dev / ws_bytes: workspace of moe_route_workspace_size(T, H, E) bytes
- *   (16-byte aligned) that holds the logits between the two kernels; it may
- *   be NULL when logits_dev is given.  It needs no initialization.  One
- *   workspace must not be used by two calls that can overlap.
+ * ws_dev / ws_bytes: workspace of moe_route_workspace_size(T, H, E) bytes,
+ *   256-byte aligned, required; it holds the logits between the two kernels
+ *   and needs no initialization.  One workspace must not be used by two calls
+ *   that can overlap; a workspace sized for T serves any T' <= T.
  * Limits: T <= 65536, H <= 4096 (bounds the exact integer accumulators);
  *   x_dev 8-byte aligned. */
 size_t moe_route_workspace_size(int T, int H, int E);

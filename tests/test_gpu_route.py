@@ -29,19 +29,18 @@ def run_route(x, wr, k, bias=None, exact=False):
                n_active=torch.empty(1, dtype=torch.int32, device=dev))
     args = (out["logits"], out["ids"], out["w"], out["offsets"], out["sorted_pairs"], out["pair_pos"],
             out["active"], out["n_active"])
-    if exact:
-        B.moe_route_exact(xd, wd, bd, T, H, E, k, *args)
-    else:
-        B.moe_route(xd, wd, bd, T, H, E, k, *args, None, 0)
-    # and once more without the logits output (the workspace carries them)
     nb = B.moe_route_workspace_size(T, H, E)
-    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    if exact:
+        B.moe_route_exact(xd, wd, bd, T, H, E, k, *args, ws, nb)
+    else:
+        B.moe_route(xd, wd, bd, T, H, E, k, *args, ws, nb)
+    # and once more without the logits output
     ids2 = torch.empty_like(out["ids"])
     args2 = (None, ids2) + args[2:]
     B.moe_route(xd, wd, bd, T, H, E, k, *args2, ws, nb)
     torch.cuda.synchronize()
     assert torch.equal(ids2, out["ids"])
-    torch.cuda.synchronize()
     return {n: t.cpu().numpy() for n, t in out.items()}
 
 

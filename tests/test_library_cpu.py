@@ -45,6 +45,7 @@ def test_row_layout_matches_the_generator(lib):
 
 def test_route_workspace_holds_the_logits(lib):
     assert B.moe_route_workspace_size(32, 2048, 64) >= 32 * 64 * 4
+    assert B.moe_route_workspace_size(32, 2048, 64) % 256 == 0
     assert B.moe_route_workspace_size(4, 2048, 65) == 0          # unsupported shapes report 0
 
 
@@ -65,6 +66,12 @@ def test_host_validation_rejects_bad_arguments(lib):
     with pytest.raises(B.MoeError) as ei:
         B.moe_route(F, F, None, 4, 200, 8, 2, None, F, F, F, F, F, F, F, F, 1 << 20, stream=0)
     assert ei.value.code == B.MOE_ERR_UNSUPPORTED
+    with pytest.raises(B.MoeError) as ei:     # the workspace is required
+        B.moe_route(F, F, None, 4, 256, 8, 2, F, F, F, F, F, F, F, F, None, 0, stream=0)
+    assert ei.value.code == B.MOE_ERR_WORKSPACE
+    with pytest.raises(B.MoeError) as ei:     # and must be 256-byte aligned
+        B.moe_route(F, F, None, 4, 256, 8, 2, F, F, F, F, F, F, F, F, F + 16, 1 << 20, stream=0)
+    assert ei.value.code == B.MOE_ERR_WORKSPACE
     with pytest.raises(B.MoeError) as ei:     # row stride not a multiple of 256
         B.moe_w4a16_expert_ffn(F, 4, 256, 512, 8, 2, F, 199_680 + 16, None, F, F, F, F, F, F, stream=0)
     assert ei.value.code == B.MOE_ERR_INVALID_ARG

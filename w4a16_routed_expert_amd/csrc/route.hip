@@ -8,21 +8,20 @@
 // router formula; the logit is the correctly rounded FP32 value of the exact
 // FP16 dot product, so expert selection is independent of summation order.
 //
-// Two launches, no hand-off between blocks of one launch.
-//   Logits: every FP16 x FP16 product is exact in fp64; a block sums them in
-//   fp64 and, alongside, sum |x*w| in FP32.  A standard bound on the fp64
-//   summation error (at most n roundings of relative size 2^-53 along any
-//   summation path) then tells whether the fp64 sum and the exact sum round
-//   to the same FP32 value: true unless the exact value lies within that
-//   bound of an FP32 rounding midpoint.  Logits that fail the test (exact
-//   ties at a midpoint among them) are recomputed exactly with 64-bit integer
-//   limbs by the whole block.
+// Logits: every FP16 x FP16 product is exact in fp64; a block sums them in
+// fp64 and, alongside, sum |x*w| in FP32.  A standard bound on the fp64
+// summation error (at most n roundings of relative size 2^-53 along any
+// summation path) then tells whether the fp64 sum and the exact sum round to
+// the same FP32 value: true unless the exact value lies within that bound of
+// an FP32 rounding midpoint.  Logits that fail the test (exact ties at a
+// midpoint among them) are recomputed exactly with 64-bit integer limbs by
+// the whole block.
 //   Small batches (decode): route_logits_kernel, one block per (token, group
-//   of 16 experts), spreads the work over many CUs; route_group_kernel (one
+//   of 16 experts), spreads the logits over many CUs; route_group_kernel (one
 //   block) then runs top-k + softmax per token (one wavefront per token, lane
 //   = expert) and the stable counting sort of the T*k pairs.
 //   Large batches (prefill): route_select_kernel, one block per token, does
-//   logits, top-k and softmax; route_group_kernel only sorts.
+//   logits, top-k and softmax; route_group_kernel sorts.
 #include "moe_internal.h"
 
 namespace {
@@ -154,46 +153,60 @@ __device__ float exact_logit(const RouteArgs &a, int t, int e, long long (*red)[
     return r;
 }
 
+// Maximum of a float over the 64 lanes of a wavefront, in every lane: DPP
+// shifts build per-row prefix maxima (lane 15 of each row of 16 holds the
+// row's maximum), two row broadcasts fold the rows into lane 63, and a
+// readlane hands it to every lane.
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_max_step(float v)
+{
+    const int o = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY), __builtin_bit_cast(int, v), CTRL,
+                                              ROW_MASK, 0xf, false);
+    return fmaxf(v, __builtin_bit_cast(float, o));
+}
+
+__device__ inline float wave_max(float v)
+{
+    v = dpp_max_step<0x111, 0xf>(v);         // row_shr:1
+    v = dpp_max_step<0x112, 0xf>(v);         // row_shr:2
+    v = dpp_max_step<0x114, 0xf>(v);         // row_shr:4
+    v = dpp_max_step<0x118, 0xf>(v);         // row_shr:8
+    v = dpp_max_step<0x142, 0xa>(v);         // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step<0x143, 0xc>(v);         // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // Top-k (ties to the lower expert index, slots in descending order) and
 // softmax over the k selected logits for token t; one full wavefront, lane =
-// expert, lv = that expert's final logit (bias included).  Each lane ranks
-// its logit against all E logits (read back from the wave's LDS scratch, 64
-// + MOE_MAX_TOPK floats): rank < k is its slot.  The softmax denominator is
-// summed in slot order.  Writes ids and w, and the ids also to s_ids (if not
-// null).
-__device__ void topk_softmax_wave(const RouteArgs &a, int t, int lane, float lv, int *s_ids, float *scratch)
+// expert, lv = that expert's final logit (bias included).  k rounds of a
+// wavefront maximum; the lowest lane holding it wins the slot and drops out.
+// Lane j < k keeps slot j; the softmax denominator is summed in slot order.
+// Writes ids and w, and the ids also to s_ids (if not null).
+__device__ void topk_softmax_wave(const RouteArgs &a, int t, int lane, float lv, int *s_ids)
 {
     const int E = a.E, k = a.k;
-    float *s_l = scratch, *s_ex = scratch + 64;
-    s_l[lane] = lane < E ? lv : -INFINITY;          // missing experts never outrank a real one
-    __builtin_amdgcn_wave_barrier();
-    float4 v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = reinterpret_cast<const float4 *>(s_l)[i];
-    int rank = 0;
-    float vmax = lv;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float vv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int j = 4 * i + c;
-            rank += (vv[c] > lv) || (vv[c] == lv && j < lane);
-            vmax = fmaxf(vmax, vv[c]);
+    float v = lane < E ? lv : -INFINITY;     // missing experts never outrank a real one
+    int my_id = 0;
+    float my_l = 0.0f, m0 = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const float m = wave_max(v);
+        const int win = (int)__builtin_ctzll(__ballot(v == m));
+        if (lane == win) v = -INFINITY;
+        if (lane == j) {
+            my_id = win;
+            my_l = m;
         }
+        if (j == 0) m0 = m;
     }
-    const bool sel = lane < E && rank < k;
-    const float ex = sel ? expf(lv - vmax) : 0.0f;
-    if (sel) s_ex[rank] = ex;
-    __builtin_amdgcn_wave_barrier();
+    const float ex = lane < k ? expf(my_l - m0) : 0.0f;
     float den = 0.0f;
-    for (int j = 0; j < k; ++j) den += s_ex[j];
-    if (sel) {
-        a.ids[(size_t)t * k + rank] = lane;
-        a.w[(size_t)t * k + rank] = ex / den;
-        if (s_ids) s_ids[t * k + rank] = lane;
+    for (int j = 0; j < k; ++j)
+        den += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+    if (lane < k) {
+        a.ids[(size_t)t * k + lane] = my_id;
+        a.w[(size_t)t * k + lane] = ex / den;
+        if (s_ids) s_ids[t * k + lane] = my_id;
     }
-    __builtin_amdgcn_wave_barrier();       // scratch is reused by this wave's next token
 }
 
 // Loads VEC consecutive FP16 router weights (experts e0 .. e0+VEC-1 of row h).
@@ -236,7 +249,6 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
     __shared__ float s_bnd[kSelWaves][64];
     __shared__ long long s_red[kSelThreads][2];
     __shared__ float s_logit[64];
-    __shared__ __attribute__((aligned(16))) float s_topk[64 + MOE_MAX_TOPK];
     __shared__ unsigned long long s_redo;
 
     {   // x row -> fp64 in LDS, 4 values per thread per step, all loads first
@@ -343,15 +355,127 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
         if (a.bias) lv = lv + a.bias[lane];
         if (a.logits) a.logits[(size_t)t * E + lane] = lv;
     }
-    topk_softmax_wave(a, t, lane, lv, nullptr, s_topk);
+    topk_softmax_wave(a, t, lane, lv, nullptr);
 }
 
-constexpr int kGroupE = 16;                // experts per block in the split logits kernel
+constexpr int kGroupE = 16;                // experts per block in the decode kernel
 
-// Small batches: one block per (token t, group of kGroupE experts); each
-// block sums the full reduction axis for its experts.  fp64 pass: lane =
-// (EQ)*hp + eq, EQ = kGroupE/VEC lanes per row, loads VEC experts of a row;
-// rows h = RPW*(kSelWaves*i + wave) + hp, RPW = 64/EQ rows per wave step.
+// Lanes of the wave holding the same value e (0 <= e < 64) as this lane;
+// lanes with e < 0 match nothing.
+__device__ inline unsigned long long same_expert_lanes(int e)
+{
+    unsigned long long m = __ballot(e >= 0);
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long v = __ballot(bit);
+        m &= bit ? v : ~v;
+    }
+    return e >= 0 ? m : 0ull;
+}
+
+constexpr int kGrpLdsIds = 4096;           // pairs whose ids the grouping keeps in LDS
+constexpr int kTopkBatch = 8;              // tokens whose logits a wave loads at once
+
+template <int NW, bool TOPK>
+struct GroupLds {
+    int cnt[NW][MOE_MAX_EXPERTS];
+    int base[NW][MOE_MAX_EXPERTS];
+    int ids[TOPK ? kGrpLdsIds : 1];
+};
+
+// Run by one block of NW wavefronts.  With TOPK, first the top-k + softmax of
+// every token from the logits in a.lbuf (one wave per token, lane = expert);
+// then the stable counting sort of the T*k pairs by expert.  Wave w owns the
+// contiguous pair range [w*n/NW, (w+1)*n/NW): per-wave counts (LDS atomics),
+// a prefix over experts and waves gives each wave its starting position per
+// expert, then each wave walks its range 64 pairs at a time; a pair's rank
+// among equal experts of its chunk comes from a ballot.
+template <int NW, bool TOPK>
+__device__ void group_phase(const RouteArgs &a, GroupLds<NW, TOPK> &S)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = a.T * a.k, E = a.E;
+    if (TOPK) {
+        // logits of up to kTopkBatch tokens per wave are loaded before any is used
+        for (int t0 = wave; t0 < a.T; t0 += NW * kTopkBatch) {
+            float lv[kTopkBatch];
+#pragma unroll
+            for (int i = 0; i < kTopkBatch; ++i) {
+                const int t = t0 + i * NW;
+                lv[i] = (lane < E && t < a.T) ? a.lbuf[(size_t)t * E + lane] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < kTopkBatch; ++i) {
+                const int t = t0 + i * NW;
+                if (t < a.T) {
+                    if (a.logits && a.logits != a.lbuf && lane < E) a.logits[(size_t)t * E + lane] = lv[i];
+                    topk_softmax_wave(a, t, lane, lv[i], S.ids);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // ids of pair p: from LDS when this block just produced them, else from memory
+    auto id_of = [&](int p) { return TOPK ? S.ids[p] : a.ids[p]; };
+    const int p0 = (int)((long long)n * wave / NW), p1 = (int)((long long)n * (wave + 1) / NW);
+    S.cnt[wave][lane] = 0;
+    __syncthreads();
+    for (int p = p0 + lane; p < p1; p += 64) {
+        const int e = id_of(p);
+        if (e >= 0 && e < E) atomicAdd(&S.cnt[wave][e], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // per expert (lane): total count, exclusive prefix over experts, per-wave starts
+        int c = 0;
+        for (int w = 0; w < NW; ++w) c += (lane < E) ? S.cnt[w][lane] : 0;
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const int excl = incl - c;
+        int run = excl;
+        for (int w = 0; w < NW; ++w) {
+            S.base[w][lane] = run;
+            run += (lane < E) ? S.cnt[w][lane] : 0;
+        }
+        const unsigned long long act = __ballot(lane < E && c > 0);
+        const int na = __popcll(act);
+        const unsigned long long below = (1ull << lane) - 1ull;
+        if (lane < E) {
+            a.offsets[lane] = excl;
+            if (c > 0) a.active[__popcll(act & below)] = lane;
+            if (lane >= na) a.active[lane] = -1;
+            if (lane == E - 1) a.offsets[E] = incl;
+        }
+        if (lane == 0) a.n_active[0] = na;
+    }
+    __syncthreads();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int c0 = p0; c0 < p1; c0 += 64) {
+        const int p = c0 + lane;
+        int e = p < p1 ? id_of(p) : -1;
+        if (e >= E) e = -1;
+        const unsigned long long peers = same_expert_lanes(e);
+        if (e >= 0) {
+            const int rank = __popcll(peers & below);
+            const int pos = S.base[wave][e] + rank;
+            a.sorted_pairs[pos] = p;
+            a.pair_pos[p] = pos;
+            if (rank == 0) S.base[wave][e] = pos + __popcll(peers);   // one leader per expert and chunk
+        }
+    }
+}
+
+// Small batches: block = (token t, group g of kGroupE experts) computes those
+// logits (+ bias) into a.lbuf; route_group_kernel<true> then routes and
+// groups.  fp64 pass: lane = EQ*hp + eq, EQ = kGroupE/VEC lanes per
+// row, loads VEC experts of a row; rows h = RPW*(kSelWaves*i + wave) + hp,
+// RPW = 64/EQ rows per wave step.  The first batch of router rows is loaded
+// before the activation row is staged, so the two memory latencies overlap.
 template <int VEC>
 __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
 {
@@ -370,6 +494,22 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
     __shared__ float s_logit[kGroupE];
     __shared__ unsigned long long s_redo;
 
+    const int eq = lane % EQ, hp = lane / EQ;
+    const int e0 = g * kGroupE + VEC * eq;          // first expert of this lane
+    const uint16_t *wcol = a.wr + (e0 < E ? e0 : 0);
+    const int step = RPW * kSelWaves;
+    int h0 = RPW * wave + hp;
+    typename L::T wv[U];
+    // rows past H load a clamped (valid) row and use x = 0
+    auto load_rows = [&](int hb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const unsigned int h = (unsigned int)min(hb + u * step, H - 1);
+            wv[u] = L::ld(wcol + h * (unsigned int)E);
+        }
+    };
+    load_rows(h0);
+
     {   // x row -> fp64 in LDS
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         const u32x2 *src = reinterpret_cast<const u32x2 *>(a.x + (size_t)t * H);
@@ -387,36 +527,24 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
     }
     __syncthreads();
 
-    const int eq = lane % EQ, hp = lane / EQ;
-    const int e0 = g * kGroupE + VEC * eq;          // first expert of this lane
     double acc[VEC];
     float bnd[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) { acc[j] = 0.0; bnd[j] = 0.0f; }
-    if (e0 < E) {
-        const uint16_t *wcol = a.wr + e0;
-        const int step = RPW * kSelWaves;
-        // branch-free body: rows past H load a clamped (valid) row and use x = 0
-        for (int h0 = RPW * wave + hp; h0 < H; h0 += U * step) {
-            typename L::T wv[U];
+    for (; h0 < H; h0 += U * step) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const unsigned int h = (unsigned int)min(h0 + u * step, H - 1);
-                wv[u] = L::ld(wcol + h * (unsigned int)E);
-            }
+        for (int u = 0; u < U; ++u) {
+            const int h = h0 + u * step;
+            const double xv = (h < H && e0 < E) ? s_x[h] : 0.0;
+            const float xa = fabsf((float)xv);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int h = h0 + u * step;
-                const double xv = h < H ? s_x[h] : 0.0;
-                const float xa = fabsf((float)xv);
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) {
-                    const float wf = (float)__builtin_bit_cast(_Float16, L::get(wv[u], j));
-                    acc[j] = fma(xv, (double)wf, acc[j]);              // exact product, fp64 sum
-                    bnd[j] = fmaf(xa, fabsf(wf), bnd[j]);              // sum |x*w| (for the error bound)
-                }
+            for (int j = 0; j < VEC; ++j) {
+                const float wf = (float)__builtin_bit_cast(_Float16, L::get(wv[u], j));
+                acc[j] = fma(xv, (double)wf, acc[j]);              // exact product, fp64 sum
+                bnd[j] = fmaf(xa, fabsf(wf), bnd[j]);              // sum |x*w| (for the error bound)
             }
         }
+        if (h0 + U * step < H) load_rows(h0 + U * step);
     }
     // sum the RPW row phases within the wave (lanes eq, eq+EQ, ...)
 #pragma unroll
@@ -472,101 +600,18 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
     }
 }
 
-// Lanes of the wave holding the same value e (0 <= e < 64) as this lane;
-// lanes with e < 0 match nothing.
-__device__ inline unsigned long long same_expert_lanes(int e)
-{
-    unsigned long long m = __ballot(e >= 0);
-#pragma unroll
-    for (int b = 0; b < 6; ++b) {
-        const bool bit = (e >> b) & 1;
-        const unsigned long long v = __ballot(bit);
-        m &= bit ? v : ~v;
-    }
-    return e >= 0 ? m : 0ull;
-}
-
-// Stable counting sort of the T*k pairs by expert, one block.  Wave w owns
-// the contiguous pair range [w*n/W, (w+1)*n/W): per-wave counts (LDS
-// atomics), a prefix over experts and waves gives each wave its starting
-// position per expert, then each wave walks its range 64 pairs at a time; a
-// pair's rank among equal experts of its chunk comes from a ballot.
-constexpr int kGrpLdsIds = 4096;           // pairs whose ids the grouping keeps in LDS
-
+// One block: top-k + softmax of every token from a.lbuf (TOPK), then the
+// grouping.
 template <bool TOPK>
 __global__ __launch_bounds__(kGrpThreads) void route_group_kernel(RouteArgs a)
 {
-    __shared__ int cnt[kGrpWaves][MOE_MAX_EXPERTS];
-    __shared__ int base[kGrpWaves][MOE_MAX_EXPERTS];
-    __shared__ int s_ids[TOPK ? kGrpLdsIds : 1];
-    __shared__ __attribute__((aligned(16))) float s_topk[TOPK ? kGrpWaves : 1][64 + MOE_MAX_TOPK];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = a.T * a.k, E = a.E;
-    if (TOPK) {
-        // top-k + softmax of every token from the logits kernel's output, one wave per token
-        for (int t = wave; t < a.T; t += kGrpWaves) {
-            const float lv = lane < E ? a.lbuf[(size_t)t * E + lane] : 0.0f;
-            if (a.logits && a.logits != a.lbuf && lane < E) a.logits[(size_t)t * E + lane] = lv;
-            topk_softmax_wave(a, t, lane, lv, s_ids, s_topk[wave]);
-        }
-        __syncthreads();
-    }
-    // ids of pair p: from LDS when this block just produced them, else from memory
-    auto id_of = [&](int p) { return TOPK ? s_ids[p] : a.ids[p]; };
-    const int p0 = (int)((long long)n * wave / kGrpWaves), p1 = (int)((long long)n * (wave + 1) / kGrpWaves);
-    cnt[wave][lane] = 0;
-    __syncthreads();
-    for (int p = p0 + lane; p < p1; p += 64) {
-        const int e = id_of(p);
-        if (e >= 0 && e < E) atomicAdd(&cnt[wave][e], 1);
-    }
-    __syncthreads();
-    if (wave == 0) {
-        // per expert (lane): total count, exclusive prefix over experts, per-wave starts
-        int c = 0;
-        for (int w = 0; w < kGrpWaves; ++w) c += (lane < E) ? cnt[w][lane] : 0;
-        int incl = c;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
-        const int excl = incl - c;
-        int run = excl;
-        for (int w = 0; w < kGrpWaves; ++w) {
-            base[w][lane] = run;
-            run += (lane < E) ? cnt[w][lane] : 0;
-        }
-        const unsigned long long act = __ballot(lane < E && c > 0);
-        const int na = __popcll(act);
-        const unsigned long long below = (1ull << lane) - 1ull;
-        if (lane < E) {
-            a.offsets[lane] = excl;
-            if (c > 0) a.active[__popcll(act & below)] = lane;
-            if (lane >= na) a.active[lane] = -1;
-            if (lane == E - 1) a.offsets[E] = incl;
-        }
-        if (lane == 0) a.n_active[0] = na;
-    }
-    __syncthreads();
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int c0 = p0; c0 < p1; c0 += 64) {
-        const int p = c0 + lane;
-        int e = p < p1 ? id_of(p) : -1;
-        if (e >= E) e = -1;
-        const unsigned long long peers = same_expert_lanes(e);
-        if (e >= 0) {
-            const int rank = __popcll(peers & below);
-            const int pos = base[wave][e] + rank;
-            a.sorted_pairs[pos] = p;
-            a.pair_pos[p] = pos;
-            if (rank == 0) base[wave][e] = pos + __popcll(peers);   // one leader per expert and chunk
-        }
-    }
+    __shared__ GroupLds<kGrpWaves, TOPK> s_grp;
+    group_phase<kGrpWaves, TOPK>(a, s_grp);
 }
 
 constexpr int kSmallBatch = 256;           // largest T routed with the split logits kernel
 
+// Workspace: the logits [T][E] handed from the logit blocks to the grouping block.
 size_t route_ws_bytes(int T, int E) { return ((size_t)T * E * sizeof(float) + 255) / 256 * 256; }
 
 int route_launch(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int E, int k,
@@ -585,13 +630,10 @@ int route_launch(const void *x_dev, const void *w_router_dev, const float *bias_
     if (!moe::aligned(x_dev, 8) || !moe::aligned(w_router_dev, 2))
         return moe::fail(MOE_ERR_INVALID_ARG, "moe_route: x must be 8-byte and w_router 2-byte aligned");
     const bool small = T <= kSmallBatch;
-    float *lbuf = logits_dev;
-    if (small && !lbuf) {
-        if (!ws_dev || ws_bytes < route_ws_bytes(T, E) || !moe::aligned(ws_dev, 16))
-            return moe::fail(MOE_ERR_WORKSPACE, "moe_route: without logits_dev the workspace needs %zu bytes",
-                             route_ws_bytes(T, E));
-        lbuf = (float *)ws_dev;
-    }
+    if (!ws_dev || ws_bytes < route_ws_bytes(T, E) || !moe::aligned(ws_dev, 256))
+        return moe::fail(MOE_ERR_WORKSPACE, "moe_route: the workspace needs %zu bytes, 256-byte aligned",
+                         route_ws_bytes(T, E));
+    float *lbuf = (float *)ws_dev;
 
     RouteArgs a;
     a.x = (const uint16_t *)x_dev;

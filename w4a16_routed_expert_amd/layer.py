@@ -46,7 +46,7 @@ class RoutedExpertLayer:
         self.active_list = torch.empty(E, dtype=torch.int32, device=d)
         self.n_active = torch.empty(1, dtype=torch.int32, device=d)
         self.ws_bytes = B.moe_route_workspace_size(T, H, E)
-        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=d)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=d)
         self.h = torch.empty((n, I), dtype=torch.float16, device=d)
         self.pair_out = torch.empty((n, H), dtype=torch.float32, device=d)
         self.status = torch.zeros(1, dtype=torch.int32, device=d)
