@@ -175,6 +175,29 @@ int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
                          const int32_t *active_list_dev, const int32_t *n_active_dev,
                          void *h_dev, float *pair_out_dev, int32_t *status_dev, void *stream);
 
+/* ------------------------------------------------------------ shared expert
+ * moe_shared_ffn: the FP16 shared expert of a layer that has one (non-routed
+ * weights stay FP16: "horizonrunmap.com/en", section "08 / Precision &
+ * quality", paragraph "Other components"), with the rounding points of a
+ * routed expert:
+ *   g = Wsg x_t, u = Wsu x_t (FP32 sums of FP16 products),
+ *   hs = RN16(silu(g) * u),  shared_out[t] = Wsd hs (FP32),
+ *   shared_gate[t] = 1 / (1 + exp(-(w_sgate . x_t)))  (FP32).
+ * The layer output then adds shared_gate[t] * shared_out[t] (moe_combine).
+ * Inputs:  x_dev FP16 [T][H]; w_gate_dev, w_up_dev FP16 [Is][H]; w_down_dev
+ *          FP16 [H][Is]; w_sgate_dev FP16 [H]; all row-major, 16-byte aligned
+ *          (w_sgate 2-byte).  H and Is positive multiples of 128, each
+ *          matrix under 2 GiB.
+ * Outputs: shared_out_dev FP32 [T][H] (16-byte aligned), shared_gate_dev FP32 [T].
+ * ws_dev / ws_bytes: workspace of moe_shared_ffn_workspace_size(T, H, Is)
+ *   bytes (256-byte aligned) holding hs between the two kernels; no
+ *   initialization; not shared by overlapping calls.
+ * Two kernel launches on `stream`; T = 0 enqueues nothing. */
+size_t moe_shared_ffn_workspace_size(int T, int H, int Is);
+int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_dev, const void *w_down_dev,
+                   const void *w_sgate_dev, int T, int H, int Is, float *shared_out_dev, float *shared_gate_dev,
+                   void *ws_dev, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------ combine
  * y[t][c] = RN16( sum_{j=0..k-1} topk_w[t][j] * pair_out[pair_pos[t*k+j]][c]
  *                 (+ shared_gate[t] * shared_out[t][c]) ), FP32, j ascending.

@@ -1,0 +1,83 @@
+"""GPU parity of the FP16 shared expert (moe_shared_ffn) and of the layer with it.
+
+The shared expert's outputs are compared with the oracle per token row
+(normwise, like the routed experts' per-pair outputs: its FP16 activation hs is
+rounded, so single outputs move with one-ulp flips of hs); the sigmoid gate to
+1e-6 absolute; the layer output y with the elementwise rule of parity_util.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parity_util import assert_close_rows
+from w4a16_routed_expert_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def small_shared(H, Is, seed):
+    g = np.random.default_rng(seed)
+    mk = lambda *shape: (g.standard_normal(shape, dtype=np.float32) * np.float32(0.02)).astype(np.float16)
+    return mk(Is, H), mk(Is, H), mk(H, Is), mk(H)
+
+
+def run_shared(x, shared):
+    from w4a16_routed_expert_amd import binding as B
+    dev = torch.device("cuda:0")
+    Wsg, Wsu, Wsd, wg = (torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in shared)
+    T, H = x.shape
+    Is = Wsg.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    out = torch.full((max(T, 1), H), float("nan"), dtype=torch.float32, device=dev)
+    sig = torch.full((max(T, 1),), float("nan"), dtype=torch.float32, device=dev)
+    nb = B.moe_shared_ffn_workspace_size(T, H, Is)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    B.moe_shared_ffn(xd, Wsg, Wsu, Wsd, wg, T, H, Is, out, sig, ws, nb)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()[:T], sig.cpu().numpy()[:T]
+
+
+def check_shared(x, shared, what):
+    os_ref, sig_ref = oracle.shared_ffn(x, *shared)
+    os_gpu, sig_gpu = run_shared(x, shared)
+    assert np.all(np.isfinite(os_gpu)) and np.all(np.isfinite(sig_gpu)), f"{what}: unwritten outputs"
+    assert_close_rows(os_gpu.astype(np.float64), os_ref, f"{what}: shared_out", floor=1.0)
+    assert np.allclose(sig_gpu, sig_ref, rtol=0, atol=1e-6), f"{what}: shared gate"
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 20, 33])
+def test_small_shared_expert(T):
+    # H = 256 gives each of the 8 reduction slices of a row group 0 or 1 tile
+    x = (np.random.default_rng(T).standard_normal((T, 256))).astype(np.float16)
+    check_shared(x, small_shared(256, 512, 7), f"small shared T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_qwen_shared_expert(T):
+    cfg = synth.CONFIGS["qwen"]
+    check_shared(synth.make_x(cfg, T, step=2), synth.make_shared(cfg), f"qwen shared T={T}")
+
+
+def test_qwen_layer_with_shared_expert():
+    from w4a16_routed_expert_amd import binding as B
+    from w4a16_routed_expert_amd.layer import RoutedExpertLayer
+    cfg = synth.CONFIGS["qwen"]
+    T = 16
+    dev = torch.device("cuda:0")
+    rows, wr, x = synth.make_expert_rows(cfg), synth.make_router(cfg), synth.make_x(cfg, T, step=4)
+    shared = synth.make_shared(cfg)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, shared=shared)
+    lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev), torch.from_numpy(wr).to(dev),
+                            max_T=T, device=dev)
+    xd = torch.from_numpy(x).to(dev)
+    Wsg, Wsu, Wsd, wg = (torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in shared)
+    os_ = torch.empty((T, cfg.H), dtype=torch.float32, device=dev)
+    sig = torch.empty(T, dtype=torch.float32, device=dev)
+    nb = B.moe_shared_ffn_workspace_size(T, cfg.H, cfg.shared_I)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    B.moe_shared_ffn(xd, Wsg, Wsu, Wsd, wg, T, cfg.H, cfg.shared_I, os_, sig, ws, nb)
+    y = lay.forward(xd, shared_out=os_, shared_gate=sig)
+    torch.cuda.synchronize()
+    assert np.array_equal(lay.topk_ids.cpu().numpy()[:T], ref["ids"])
+    assert_close_rows(y.cpu().numpy().view(np.uint16), ref["y"], "qwen layer with shared expert: y")

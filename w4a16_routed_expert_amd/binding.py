@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_version", "moe_last_error", "moe_expert_row_bytes",
     "moe_route_workspace_size", "moe_route", "moe_route_exact",
     "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
-    "moe_combine",
+    "moe_combine", "moe_shared_ffn_workspace_size", "moe_shared_ffn",
 )
 
 
@@ -75,6 +75,10 @@ def load(path: str = LIB_PATH):
                                        _vp]
     L.moe_combine.restype = _i
     L.moe_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]
+    L.moe_shared_ffn_workspace_size.restype = _sz
+    L.moe_shared_ffn_workspace_size.argtypes = [_i, _i, _i]
+    L.moe_shared_ffn.restype = _i
+    L.moe_shared_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]
     _lib = L
     return L
 
@@ -160,3 +164,12 @@ def moe_w4a16_expert_ffn(x, T, H, I, E, k, rows, row_stride, slot_map, expert_of
 def moe_combine(pair_out, pair_pos, topk_w, shared_out, shared_gate, T, H, k, y, stream=None):
     _check(load().moe_combine(_p(pair_out), _p(pair_pos), _p(topk_w), _p(shared_out), _p(shared_gate), T, H, k,
                               _p(y), _s(stream)))
+
+
+def moe_shared_ffn_workspace_size(T, H, Is) -> int:
+    return int(load().moe_shared_ffn_workspace_size(T, H, Is))
+
+
+def moe_shared_ffn(x, w_gate, w_up, w_down, w_sgate, T, H, Is, shared_out, shared_gate, ws, ws_bytes, stream=None):
+    _check(load().moe_shared_ffn(_p(x), _p(w_gate), _p(w_up), _p(w_down), _p(w_sgate), T, H, Is, _p(shared_out),
+                                 _p(shared_gate), _p(ws), ws_bytes, _s(stream)))
