@@ -1,20 +1,25 @@
 """Benchmark of the W4A16 routed-expert layer on one MI355X.
 
 A step is one pass of the layer -- route (logits, top-k, grouping), W4A16
-gate/up + SiLU*up, W4A16 down, weighted combine -- over one batch of T
-synthetic FP16 tokens whose expert rows already sit in HBM.  Steps rotate over
-R byte-identical replicas of the layer's expert rows at distinct addresses
-(R * layer bytes >= 1 GiB, four times the 256 MB Infinity Cache), so the
-weights stream from HBM rather than from the cache, and over a set of fresh
-activation batches.  Each step is captured once into a HIP graph (one graph
-per replica) and the timed loop replays the graphs.
+gate/up + SiLU*up, W4A16 down, the FP16 shared expert where the layer has one,
+weighted combine -- over one batch of T synthetic FP16 tokens whose expert rows
+already sit in HBM.  Steps rotate over R byte-identical replicas of the layer's
+weights at distinct addresses (R * layer bytes >= 1 GiB, four times the 256 MB
+Infinity Cache), so the weights stream from HBM rather than from the cache,
+and over a set of fresh activation batches.  Each (replica, batch) step is
+captured once into a HIP graph and the timed loop replays the graphs.
 
-Per-kernel durations come from HIP events around each kernel of the same steps
-run eagerly on the stream the kernels are launched on.  The roofline object
-reports the dominant kernel (W4A16 gate/up): algorithmic bytes per launch =
-qpacked gate+up bytes of the experts that launch actually reads (active
-experts x 2 x (I*H/2 + I*ceil(H/256)*2)), divided by its average duration,
-against the 8 TB/s HBM peak.
+Per-kernel durations (`kernel_us`) come from HIP events around each call of the
+same steps run eagerly on the stream the kernels are launched on.  The roofline
+object reports the dominant kernel (W4A16 gate/up): its duration is measured
+with HIP events around a graph of back-to-back gate/up launches over the
+replicas on the launch stream, and its algorithmic bytes per launch are the
+qpacked gate+up bytes of the experts that launch reads (active experts x 2 x
+(I*H/2 + I*ceil(H/256)*2)), against the 8 TB/s HBM peak.  `traffic` is the
+HBM byte count per launch measured with rocprofv3 counters (FETCH_SIZE x 2 +
+WRITE_SIZE, the factors calibrated on a plain copy), read from
+profiles/gateup_traffic.json when that file was measured on the current
+kernel source, else null.
 
 The CPU baseline times the oracle (single-threaded C, fp64) on a bounded
 sample of the same workload.
@@ -22,6 +27,7 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +40,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FFN_SOURCE = os.path.join(ROOT, "w4a16_routed_expert_amd", "csrc", "expert_ffn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic.json")
 
 
 def parse():
@@ -48,13 +56,72 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--kernel-only", default=None, choices=[None, "gateup"],
-                    help="profile helper: after setup, launch only this kernel --steps times")
+    ap.add_argument("--kernel-only", default=None, choices=[None, "gateup", "copy"],
+                    help="profile helper: after setup, launch only this kernel --steps times "
+                         "(copy: a 256 MiB device-to-device copy, the counter calibration)")
+    ap.add_argument("--traffic-report", nargs=5, metavar=("GU_FETCH", "GU_WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
+                    default=None,
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output directories of a --kernel-only "
+                         "gateup run and a --kernel-only copy run into the traffic file OUT, then exit")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+
+
+def pmc_per_dispatch(directory: str, kernel_substr: str, counter: str) -> float:
+    """Mean counter value (KiB for FETCH_SIZE/WRITE_SIZE) per dispatch of the matching kernel."""
+    import csv
+    import glob
+    vals = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} records for {kernel_substr} under {directory}")
+    return sum(vals) / len(vals)
+
+
+def traffic_report(gu_fetch, gu_write, copy_fetch, copy_write, out_path, config_name, T):
+    """HBM bytes per gate/up launch: each counter scaled by its reading on a copy of known size."""
+    cf = COPY_BYTES / (pmc_per_dispatch(copy_fetch, "copyBuffer", "FETCH_SIZE") * 1024)
+    cw = COPY_BYTES / (pmc_per_dispatch(copy_write, "copyBuffer", "WRITE_SIZE") * 1024)
+    fetch = pmc_per_dispatch(gu_fetch, "w4a16_ffn_kernel<true", "FETCH_SIZE") * 1024 * cf
+    write = pmc_per_dispatch(gu_write, "w4a16_ffn_kernel<true", "WRITE_SIZE") * 1024 * cw
+    d = {"workload": f"{config_name}_T{T}", "source_sha256": source_digest(FFN_SOURCE),
+         "bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+         "fetch_factor": cf, "write_factor": cw}
+    with open(out_path, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(d))
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(config_name: str, T: int):
+    """HBM bytes per gate/up launch from the counter file, if it matches this source and workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != source_digest(FFN_SOURCE) or d.get("workload") != f"{config_name}_T{T}":
+        return None
+    return d.get("bytes_per_launch")
 
 
 def main():
     args = parse()
+    if args.traffic_report:
+        from w4a16_routed_expert_amd import synth
+        cfg = synth.CONFIGS[args.config]
+        traffic_report(*args.traffic_report, cfg.name, args.tokens or max(cfg.batches))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
               "(the layer is single-GPU; multi-GPU sharding is described in the design notes, not built).",
@@ -70,11 +137,22 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.kernel_only == "copy":
+        # before any other device copy, so the copy kernels profiled are exactly these
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_only": "copy", "launches": args.steps, "bytes": COPY_BYTES}))
+        return
     cfg = synth.CONFIGS[args.config]
     T = args.tokens or max(cfg.batches)
     H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+    Is = cfg.shared_I
     row_bytes, _ = B.moe_expert_row_bytes(H, I)
-    layer_bytes = row_bytes * E
+    shared_bytes = 3 * Is * H * 2 + H * 2 if Is else 0
+    layer_bytes = row_bytes * E + shared_bytes
     R = args.replicas or max(1, -(-(1 << 30) // layer_bytes))
     S = args.inputs
 
@@ -83,13 +161,23 @@ def main():
     rows_np = synth.make_expert_rows(cfg)
     wr_np = synth.make_router(cfg)
     xs_np = [synth.make_x(cfg, T, step=s) for s in range(S)]
+    shared_np = synth.make_shared(cfg) if Is else None
     gen_s = time.time() - t0
     rows0 = torch.from_numpy(rows_np).to(dev)
     replicas = [rows0] + [rows0.clone() for _ in range(R - 1)]
+    shared_reps = None
+    if Is:
+        sh0 = [torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in shared_np]
+        shared_reps = [sh0] + [[m.clone() for m in sh0] for _ in range(R - 1)]
     router = torch.from_numpy(wr_np).to(dev)
     xs = [torch.from_numpy(x).to(dev) for x in xs_np]
     lay = RoutedExpertLayer(H, I, E, k, rows0, router, max_T=T, device=dev)
     y = torch.empty((T, H), dtype=torch.float16, device=dev)
+    if Is:
+        sh_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        sh_gate = torch.empty(T, dtype=torch.float32, device=dev)
+        sh_ws_bytes = B.moe_shared_ffn_workspace_size(T, H, Is)
+        sh_ws = torch.empty(sh_ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     # active experts per input batch (sets the algorithmic bytes of each launch)
@@ -103,26 +191,35 @@ def main():
 
     # step s uses replica s % R and input batch (s // R) % S
     def step_args(s):
-        return replicas[s % R], xs[(s // R) % S], n_act[(s // R) % S]
+        return s % R, xs[(s // R) % S], n_act[(s // R) % S]
 
     def run_step(s, ev=None):
-        rows, x, _ = step_args(s)
-        if ev is not None:
-            ev[0].record(stream)
+        r, x, _ = step_args(s)
+        rows = replicas[r]
+        marks = iter(ev) if ev is not None else None
+
+        def mark():
+            if marks is not None:
+                next(marks).record(stream)
+        mark()
         lay.route(x)
-        if ev is not None:
-            ev[1].record(stream)
+        mark()
         B.moe_w4a16_gateup(x, T, H, I, E, k, rows, lay.row_stride, None, lay.expert_offsets, lay.sorted_pairs,
                            lay.active_list, lay.n_active, lay.h, lay.status)
-        if ev is not None:
-            ev[2].record(stream)
+        mark()
         B.moe_w4a16_down(T, H, I, E, k, rows, lay.row_stride, None, lay.expert_offsets, lay.active_list,
                          lay.n_active, lay.h, lay.pair_out, lay.status)
-        if ev is not None:
-            ev[3].record(stream)
-        lay.combine(T, y)
-        if ev is not None:
-            ev[4].record(stream)
+        mark()
+        if Is:
+            Wsg, Wsu, Wsd, wg = shared_reps[r]
+            B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes)
+            mark()
+            lay.combine(T, y, sh_out, sh_gate)
+        else:
+            lay.combine(T, y)
+        mark()
+
+    names = ["route", "gateup", "down"] + (["shared"] if Is else []) + ["combine"]
 
     if args.kernel_only == "gateup":
         lay.route(xs[0])
@@ -170,20 +267,57 @@ def main():
 
     # ---------------------------------------------------------------- per-kernel events (eager, same steps)
     n_ev = min(K, 400)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_ev)]
     for s in range(n_ev):
         run_step(s, evs[s])
     torch.cuda.synchronize()
-    dur = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(4)] for s in range(n_ev)]) * 1e3  # us
-    names = ["route", "gateup", "down", "combine"]
+    dur = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(len(names))] for s in range(n_ev)]) * 1e3
     mean_us = {n: float(dur[:, i].mean()) for i, n in enumerate(names)}
-    gu_bytes = np.array([gateup_unit * step_args(s)[2] for s in range(n_ev)], dtype=np.float64)
-    dn_bytes = np.array([down_unit * step_args(s)[2] for s in range(n_ev)], dtype=np.float64)
-    gu_gbs = float(gu_bytes.mean() / (mean_us["gateup"] * 1e-6) / 1e9)
-    ffn_gbs = float((gu_bytes.mean() + dn_bytes.mean()) / ((mean_us["gateup"] + mean_us["down"]) * 1e-6) / 1e9)
+    gu_bytes_step = np.array([gateup_unit * step_args(s)[2] for s in range(n_ev)], dtype=np.float64)
+    dn_bytes_step = np.array([down_unit * step_args(s)[2] for s in range(n_ev)], dtype=np.float64)
+    ffn_gbs = float((gu_bytes_step.mean() + dn_bytes_step.mean()) /
+                    ((mean_us["gateup"] + mean_us["down"]) * 1e-6) / 1e9)
+
+    # ---------------------------------------------------------------- gate/up roofline: back-to-back launches
+    lay.route(xs[0])
+    torch.cuda.synchronize()
+    n_b2b = 2 * R
+
+    def gateup_burst():
+        for i in range(n_b2b):
+            rows = replicas[i % R]
+            B.moe_w4a16_gateup(xs[0], T, H, I, E, k, rows, lay.row_stride, None, lay.expert_offsets,
+                               lay.sorted_pairs, lay.active_list, lay.n_active, lay.h, lay.status)
+    gateup_burst()
+    torch.cuda.synchronize()
+    if args.no_graph:
+        burst = gateup_burst
+    else:
+        gb = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(gb, stream=cap):
+            gateup_burst()
+        burst = gb.replay
+    burst()
+    torch.cuda.synchronize()
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        burst()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gu_us = e0.elapsed_time(e1) * 1e3 / (reps * n_b2b)
+    gu_bytes = float(gateup_unit * n_act[0])
+    gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
 
     # ---------------------------------------------------------------- parity spot check of the timed path
-    lay.forward(xs[0], y)
+    if Is:
+        Wsg, Wsu, Wsd, wg = shared_reps[0]
+        B.moe_shared_ffn(xs[0], Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes)
+        lay.forward(xs[0], y, shared_out=sh_out, shared_gate=sh_gate)
+    else:
+        lay.forward(xs[0], y)
     torch.cuda.synchronize()
     y_gpu = y.cpu().numpy()
 
@@ -192,22 +326,23 @@ def main():
     if not args.skip_cpu:
         import oracle
         n_calls, cpu_s, tok = 0, 0.0, 0
-        sample_T = T
+        parity_norm = None
         while cpu_s < args.cpu_seconds and n_calls < S:
             tc = time.perf_counter()
-            ref = oracle.layer(xs_np[n_calls], wr_np, rows_np, H, I, E, k)
+            ref = oracle.layer(xs_np[n_calls], wr_np, rows_np, H, I, E, k, shared=shared_np)
             cpu_s += time.perf_counter() - tc
-            tok += sample_T
+            tok += T
             if n_calls == 0:
-                d = np.abs(ref["y"].view(np.float16).astype(np.float64) - y_gpu.astype(np.float64))
-                m = np.abs(ref["y"].view(np.float16).astype(np.float64)).max(axis=1, keepdims=True)
-                parity_norm = float((d / m).max())
+                yr = ref["y"].view(np.float16).astype(np.float64)
+                d = np.abs(yr - y_gpu.astype(np.float64))
+                parity_norm = float((d / np.abs(yr).max(axis=1, keepdims=True)).max())
             n_calls += 1
         cpu = {"value": tok / cpu_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_calls} oracle layer call(s) of {sample_T} tokens on the same inputs "
+               "sample": f"{n_calls} oracle layer call(s) of {T} tokens on the same inputs "
                          f"({cpu_s:.1f} s, single-threaded C, fp64)",
                "gpu_vs_oracle_normwise_err": parity_norm}
 
+    workload = f"{cfg.name}_decode_layer_T{T}" if args.config != "prefill" else f"prefill_T{T}"
     out = {
         "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode)",
         "value": tokens_per_s,
@@ -222,8 +357,9 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}_decode_layer_T{T}" if args.config != "prefill" else f"prefill_T{T}",
+            "workload": workload,
             "experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
+            "shared_expert_intermediate": Is,
             "weights": "int4 qpacked, 256-value blocks, fp16 scales; fp16 activations, fp32 accumulation",
             "replicas": R, "input_batches": S, "graph_replay": not args.no_graph,
             "mean_active_experts": float(np.mean(n_act)),
@@ -235,16 +371,21 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gu_gbs / HBM_PEAK_GBS,
-            "traffic": None,
-            "algorithmic_bytes_per_launch": float(gu_bytes.mean()),
-            "avg_launch_us": mean_us["gateup"],
+            "traffic": measured_traffic(cfg.name, T),
+            "algorithmic_bytes_per_launch": gu_bytes,
+            "avg_launch_us": gu_us,
+            "timing": f"HIP events around {reps} replays of a graph of {n_b2b} back-to-back launches",
         },
         "ffn_hbm": {"achieved_gbs": ffn_gbs, "frac": ffn_gbs / HBM_PEAK_GBS,
-                    "qpacked_bytes_per_step": float(gu_bytes.mean() + dn_bytes.mean())},
+                    "qpacked_bytes_per_step": float(gu_bytes_step.mean() + dn_bytes_step.mean()),
+                    "timing": "per-kernel HIP events, eager steps"},
         "kernel_us": mean_us,
         "cpu_baseline": cpu,
         "setup_s": {"generate_inputs": gen_s},
     }
+    if Is:
+        out["shared_hbm"] = {"bytes_per_step": shared_bytes,
+                             "achieved_gbs": shared_bytes / (mean_us["shared"] * 1e-6) / 1e9}
     print(json.dumps(out))
 
 

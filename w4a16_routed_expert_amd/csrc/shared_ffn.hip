@@ -10,9 +10,10 @@
 // Kernel design (gfx950, wave64).  Decode batches make this a skinny GEMM,
 // bound by HBM (69 MB of FP16 weights for the Qwen shape):
 //   * The weights are plain row-major [R][K] FP16.  A work unit is 16 output
-//     rows x a 1/S slice of the reduction axis x one token tile of 16 tokens;
-//     the S waves of a row group reduce their FP32 partials in LDS in a fixed
-//     order.  A block holds 8/S row groups of one token tile.
+//     rows x a 1/S slice of the reduction axis x MT token tiles of 16 tokens
+//     (up to 64 tokens share each weight load); the S waves of a row group
+//     reduce their FP32 partials in LDS in a fixed order.  A block holds 8/S
+//     row groups of one pass over MT token tiles.
 //   * Per 128-column tile a lane loads four 16-byte pieces of its row (columns
 //     32s + 8g .. +7, s = 0..3): each is one MFMA B operand as stored, and the
 //     A operand is the same columns of a token's activation row, read straight
@@ -76,12 +77,13 @@ __device__ inline uint16_t float_to_half_bits(float v) { return __builtin_bit_ca
 // reduction axis).  GATEUP: the gate and up projections of x and the SwiGLU
 // epilogue into hs; else the down projection of hs into out.  Blocks past the
 // last item compute sigma (GATEUP only).
-template <bool GATEUP, int S, int D>
+template <bool GATEUP, int S, int D, int MT>
 __global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items)
 {
     constexpr int NMAT = GATEUP ? 2 : 1;
     constexpr int RGB = kWaves / S;
-    __shared__ float red[S > 1 ? S - 1 : 1][S > 1 ? RGB : 1][S > 1 ? NMAT : 1][S > 1 ? 4 : 1][S > 1 ? 64 : 1];
+    constexpr int NACC = NMAT * MT;
+    __shared__ float red[S > 1 ? S - 1 : 1][S > 1 ? RGB : 1][S > 1 ? NACC : 1][S > 1 ? 4 : 1][S > 1 ? 64 : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int g4 = lane >> 4, n16 = lane & 15;
     const int K = GATEUP ? a.H : a.Is, R = GATEUP ? a.Is : a.H;
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items
         return;
     }
 
-    const int mt = blockIdx.x / CH, c = blockIdx.x % CH;
+    const int pass = blockIdx.x / CH, c = blockIdx.x % CH;
     const int rgl = wave / S, ks = wave % S;
     const int rg = c * RGB + rgl;
     const bool row_ok = rg < RG;
@@ -119,13 +121,17 @@ __global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items
     }
     const int wbytes = R * K * 2;                            // < 2^31 (checked on the host)
     const int wvoff = row_ok ? ((rg * 16 + n16) * K + 8 * g4) * 2 : kOob;
-    // activations: lane (g4, n16) reads token 16 mt + n16, same columns
+    // activations: lane (g4, n16) of token tile m reads token 16 (MT pass + m) + n16, same columns
     const uint16_t *am = GATEUP ? a.x : a.hs;
-    const int tok = mt * 16 + n16;
     const int abytes = a.T * K * 2;
-    const int avoff = tok < a.T ? (tok * K + 8 * g4) * 2 : kOob;
+    int avoff[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int tok = (pass * MT + m) * 16 + n16;
+        avoff[m] = tok < a.T ? (tok * K + 8 * g4) * 2 : kOob;
+    }
 
-    u32x4 wb[D][NMAT][4], ab[D][4];
+    u32x4 wb[D][NMAT][4], ab[D][MT][4];
     auto issue = [&](int d, int t) {
         const bool ok = t < t1;
         const int soff = (ok ? t : 0) * 256;
@@ -137,7 +143,9 @@ __global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items
         }
         const __amdgpu_buffer_rsrc_t arr = rsrc(am, ok ? abytes : 0);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) ab[d][s] = bload(arr, avoff, soff + 64 * s);
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ab[d][m][s] = bload(arr, avoff[m], soff + 64 * s);
     };
     // the same load order as the refills in the loop, so the wait before each
     // slot's first use counts only the loads issued after it
@@ -148,16 +156,20 @@ __global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    f32x4 acc[NMAT];
+    f32x4 acc[NMAT][MT];
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat) acc[mat] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[mat][m] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < NR; ++r) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int mat = 0; mat < NMAT; ++mat) acc[mat] = mfma(ab[d][s], wb[d][mat][s], acc[mat]);
+                for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) acc[mat][m] = mfma(ab[d][m][s], wb[d][mat][s], acc[mat][m]);
             // every read of this slot happens above: reload it in place
             __builtin_amdgcn_sched_barrier(0);
             issue(d, t0 + (r + 1) * D + d);
@@ -170,7 +182,9 @@ __global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items
 #pragma unroll
             for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) red[ks - 1][rgl][mat][q][lane] = acc[mat][q];
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) red[ks - 1][rgl][mat * MT + m][q][lane] = acc[mat][m][q];
         }
         lds_barrier();
         if (ks != 0) return;
@@ -179,39 +193,55 @@ __global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items
 #pragma unroll
             for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[mat][q] += red[k2 - 1][rgl][mat][q][lane];
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[mat][m][q] += red[k2 - 1][rgl][mat * MT + m][q][lane];
     }
     if (!row_ok) return;
-    // lane (g4, n16) holds tokens 16 mt + 4 g4 + q of row 16 rg + n16
+    // lane (g4, n16) holds tokens 16 (MT pass + m) + 4 g4 + q of row 16 rg + n16
     const int col = rg * 16 + n16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int t = mt * 16 + 4 * g4 + q;
-        if (t < a.T) {
-            if constexpr (GATEUP) {
-                const float g = acc[0][q], u = acc[NMAT - 1][q];
-                a.hs[(size_t)t * a.Is + col] = float_to_half_bits(g / (1.0f + expf(-g)) * u);
-            } else {
-                a.out[(size_t)t * a.H + col] = acc[0][q];
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = (pass * MT + m) * 16 + 4 * g4 + q;
+            if (t < a.T) {
+                if constexpr (GATEUP) {
+                    const float g = acc[0][m][q], u = acc[NMAT - 1][m][q];
+                    a.hs[(size_t)t * a.Is + col] = float_to_half_bits(g / (1.0f + expf(-g)) * u);
+                } else {
+                    a.out[(size_t)t * a.H + col] = acc[0][m][q];
+                }
             }
         }
-    }
 }
 
 constexpr int kSplit = 8;
 
-template <bool GATEUP, int D>
-int launch(const SArgs &a, hipStream_t s, const char *who)
+// MT token tiles share every weight load; a pass covers 16*MT tokens.
+template <bool GATEUP, int D, int MT>
+int launch_mt(const SArgs &a, hipStream_t s, const char *who)
 {
     const int R = GATEUP ? a.Is : a.H;
     const int RG = R / 16, RGB = kWaves / kSplit;
     const int CH = (RG + RGB - 1) / RGB;
-    const int MT = (a.T + 15) / 16;
-    const int n_items = CH * MT;
+    const int passes = (a.T + 16 * MT - 1) / (16 * MT);
+    const int n_items = CH * passes;
     const int sig_blocks = GATEUP ? (a.T + kWaves - 1) / kWaves : 0;
-    hipLaunchKernelGGL((fp16_ffn_kernel<GATEUP, kSplit, D>), dim3((unsigned int)(n_items + sig_blocks)),
+    hipLaunchKernelGGL((fp16_ffn_kernel<GATEUP, kSplit, D, MT>), dim3((unsigned int)(n_items + sig_blocks)),
                        dim3(kThreads), 0, s, a, n_items);
     return moe::check_launch(who);
+}
+
+template <bool GATEUP>
+int launch(const SArgs &a, hipStream_t s, const char *who)
+{
+    // (gate/up holds two weight matrices per tile, so its register budget
+    // allows two token tiles per pass)
+    const int tiles = (a.T + 15) / 16;
+    if (tiles <= 1) return launch_mt<GATEUP, GATEUP ? 2 : 3, 1>(a, s, who);
+    if (GATEUP || tiles == 2) return launch_mt<GATEUP, GATEUP ? 1 : 2, 2>(a, s, who);
+    return launch_mt<false, 1, 4>(a, s, who);
 }
 
 size_t ws_bytes(int T, int Is) { return ((size_t)T * Is * 2 + 255) / 256 * 256; }
@@ -257,9 +287,9 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
     a.out = shared_out_dev;
     a.sigma = shared_gate_dev;
     hipStream_t s = (hipStream_t)stream;
-    int rc = launch<true, 2>(a, s, "moe_shared_ffn (gate/up)");
+    int rc = launch<true>(a, s, "moe_shared_ffn (gate/up)");
     if (rc) return rc;
-    return launch<false, 3>(a, s, "moe_shared_ffn (down)");
+    return launch<false>(a, s, "moe_shared_ffn (down)");
 }
 
 }  // extern "C"
