@@ -198,6 +198,84 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
                    const void *w_sgate_dev, int T, int H, int Is, float *shared_out_dev, float *shared_gate_dev,
                    void *ws_dev, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------ resident expert table
+ * Which experts have a published device row, and the miss path that brings a
+ * missing row to the GPU ("Horizon RunMap - architecture", section
+ * "Immutable authority and miss lifecycle"; "Horizon technical notes —
+ * publication edition v1", section "Immutable cache — the scope of ADR
+ * 0009"):
+ *   - the host source holds every expert's qpacked row; it belongs to the
+ *     caller, must stay unchanged and outlive the table, and is only read;
+ *   - the table owns nslots = capacity + spare_rows device rows (one
+ *     allocation, row_stride = row bytes rounded up to 256), a device map
+ *     int32 [E] (slot of each expert, -1 = no published row; pass it as
+ *     slot_map_dev to the FFN calls) and staging_rows pinned staging buffers;
+ *     nothing else is allocated after moe_table_create;
+ *   - a miss is copied host source -> pinned staging (host memcpy, after the
+ *     staging buffer's previous copy has finished) -> a spare device row
+ *     (hipMemcpyAsync on the caller's stream); the new map is published on
+ *     the same stream after the copies, so kernels enqueued later see the new
+ *     rows and never a partly written one;
+ *   - misses go to spare rows (lowest slot first); when there are too few,
+ *     least recently used published experts outside the current step give
+ *     up their rows first; after the upload, while more than `capacity`
+ *     experts are published, the least recently used experts outside the
+ *     current step lose their device copy (ties go to the lower expert id);
+ *     a row is refilled only after the consumer event last recorded with
+ *     moe_table_record_consumers (kernels that may still read it);
+ *   - no expert bytes ever move device -> host and the host source is never
+ *     written (counters expert_d2h_bytes and host_writes stay 0).
+ * Use per step: bring the active expert list to the host, moe_table_misses,
+ * moe_upload_expert_rows(misses), the FFN calls with moe_table_device's rows
+ * and map, then moe_table_record_consumers on the stream of those calls.
+ * A table is used by one host thread at a time.
+ * Errors: MOE_ERR_CAPACITY when create cannot allocate or an upload has
+ * more misses than spare rows plus rows of experts outside the step;
+ * MOE_ERR_FAULTED when a HIP call failed after
+ * copies were enqueued (the table then refuses further uploads). */
+typedef struct moe_table moe_table;
+
+typedef struct {
+    int E, H, I;                       /* experts, hidden size, expert intermediate size */
+    int capacity;                      /* experts published between steps (1..E) */
+    int spare_rows;                    /* extra device rows that receive misses */
+    int staging_rows;                  /* pinned staging buffers of one row each (1..16) */
+    const void *host_source;           /* host: expert e's row at host_source + e*host_row_stride */
+    size_t host_row_stride;            /* >= moe_expert_row_bytes(H, I) */
+    const int32_t *initial_resident;   /* host: `capacity` distinct expert ids, or NULL for 0..capacity-1 */
+} moe_table_desc;
+
+typedef struct {
+    uint64_t steps;                    /* moe_table_misses calls */
+    uint64_t hits, misses;             /* active experts found published / not */
+    uint64_t evictions;                /* device copies dropped */
+    uint64_t h2d_bytes;                /* expert bytes copied host -> device after creation */
+    uint64_t staging_waits;            /* uploads that waited for a staging buffer */
+    uint64_t expert_d2h_bytes;         /* always 0 */
+    uint64_t host_writes;              /* always 0 */
+} moe_table_counters;
+
+/* Creates the table and uploads the initial residents (synchronizes
+ * `stream` before returning).  *out receives the table. */
+int moe_table_create(moe_table **out, const moe_table_desc *desc, void *stream);
+/* Waits for the device to finish with the table, then frees it (NULL is a no-op). */
+void moe_table_destroy(moe_table *table);
+/* Device rows, their stride and the published device map. */
+int moe_table_device(const moe_table *table, const void **rows_dev, size_t *row_stride,
+                     const int32_t **slot_map_dev);
+/* Starts a step: records the active experts (host array of n ids; duplicates
+ * count once) as used now and writes those without a published row to
+ * miss_out (capacity n), their number to *n_miss. */
+int moe_table_misses(moe_table *table, const int32_t *active_host, int n, int32_t *miss_out, int *n_miss);
+/* Uploads the n missing experts into spare rows and publishes the new map,
+ * both on `stream`.  The ids must not be published already. */
+int moe_upload_expert_rows(moe_table *table, const int32_t *expert_ids, int n, void *stream);
+/* Records, on `stream`, the point after which the rows read so far may be refilled. */
+int moe_table_record_consumers(moe_table *table, void *stream);
+int moe_table_stats(const moe_table *table, moe_table_counters *out);
+/* Host copy of the published map (E entries, slot or -1). */
+int moe_table_published(const moe_table *table, int32_t *slot_map_host);
+
 /* ------------------------------------------------------------ combine
  * y[t][c] = RN16( sum_{j=0..k-1} topk_w[t][j] * pair_out[pair_pos[t*k+j]][c]
  *                 (+ shared_gate[t] * shared_out[t][c]) ), FP32, j ascending.

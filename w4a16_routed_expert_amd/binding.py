@@ -30,7 +30,20 @@ EXPORTS = (
     "moe_route_workspace_size", "moe_route", "moe_route_exact",
     "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
     "moe_combine", "moe_shared_ffn_workspace_size", "moe_shared_ffn",
+    "moe_table_create", "moe_table_destroy", "moe_table_device", "moe_table_misses", "moe_upload_expert_rows",
+    "moe_table_record_consumers", "moe_table_stats", "moe_table_published",
 )
+
+
+class TableDesc(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int), ("H", ctypes.c_int), ("I", ctypes.c_int), ("capacity", ctypes.c_int),
+                ("spare_rows", ctypes.c_int), ("staging_rows", ctypes.c_int), ("host_source", ctypes.c_void_p),
+                ("host_row_stride", ctypes.c_size_t), ("initial_resident", ctypes.c_void_p)]
+
+
+class TableCounters(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("steps", "hits", "misses", "evictions", "h2d_bytes", "staging_waits",
+                                               "expert_d2h_bytes", "host_writes")]
 
 
 class MoeError(RuntimeError):
@@ -79,6 +92,22 @@ def load(path: str = LIB_PATH):
     L.moe_shared_ffn_workspace_size.argtypes = [_i, _i, _i]
     L.moe_shared_ffn.restype = _i
     L.moe_shared_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]
+    L.moe_table_create.restype = _i
+    L.moe_table_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(TableDesc), _vp]
+    L.moe_table_destroy.restype = None
+    L.moe_table_destroy.argtypes = [_vp]
+    L.moe_table_device.restype = _i
+    L.moe_table_device.argtypes = [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_sz), ctypes.POINTER(_vp)]
+    L.moe_table_misses.restype = _i
+    L.moe_table_misses.argtypes = [_vp, _vp, _i, _vp, ctypes.POINTER(_i)]
+    L.moe_upload_expert_rows.restype = _i
+    L.moe_upload_expert_rows.argtypes = [_vp, _vp, _i, _vp]
+    L.moe_table_record_consumers.restype = _i
+    L.moe_table_record_consumers.argtypes = [_vp, _vp]
+    L.moe_table_stats.restype = _i
+    L.moe_table_stats.argtypes = [_vp, ctypes.POINTER(TableCounters)]
+    L.moe_table_published.restype = _i
+    L.moe_table_published.argtypes = [_vp, _vp]
     _lib = L
     return L
 
@@ -173,3 +202,62 @@ def moe_shared_ffn_workspace_size(T, H, Is) -> int:
 def moe_shared_ffn(x, w_gate, w_up, w_down, w_sgate, T, H, Is, shared_out, shared_gate, ws, ws_bytes, stream=None):
     _check(load().moe_shared_ffn(_p(x), _p(w_gate), _p(w_up), _p(w_down), _p(w_sgate), T, H, Is, _p(shared_out),
                                  _p(shared_gate), _p(ws), ws_bytes, _s(stream)))
+
+
+# ------------------------------------------------------------------ resident expert table
+def moe_table_create(E, H, I, capacity, spare_rows, staging_rows, host_source, host_row_stride,
+                     initial_resident=None, stream=None):
+    """host_source: a C-contiguous uint8 numpy array [E, host_row_stride] that must outlive the table.
+    Returns the table handle (an int)."""
+    import numpy as np
+    init = None if initial_resident is None else np.ascontiguousarray(initial_resident, dtype=np.int32)
+    d = TableDesc(E, H, I, capacity, spare_rows, staging_rows, host_source.ctypes.data, host_row_stride,
+                  None if init is None else init.ctypes.data)
+    out = _vp()
+    _check(load().moe_table_create(ctypes.byref(out), ctypes.byref(d), _s(stream)))
+    return out.value
+
+
+def moe_table_destroy(table):
+    load().moe_table_destroy(table)
+
+
+def moe_table_device(table):
+    """(rows device address, row stride, slot map device address)."""
+    rows, stride, smap = _vp(), _sz(), _vp()
+    _check(load().moe_table_device(table, ctypes.byref(rows), ctypes.byref(stride), ctypes.byref(smap)))
+    return rows.value, stride.value, smap.value
+
+
+def moe_table_misses(table, active):
+    """active: host int32 array of expert ids.  Returns the int32 array of misses."""
+    import numpy as np
+    act = np.ascontiguousarray(active, dtype=np.int32)
+    miss = np.empty(max(len(act), 1), dtype=np.int32)
+    n = _i()
+    _check(load().moe_table_misses(table, act.ctypes.data if len(act) else None, len(act), miss.ctypes.data,
+                                   ctypes.byref(n)))
+    return miss[:n.value].copy()
+
+
+def moe_upload_expert_rows(table, expert_ids, stream=None):
+    import numpy as np
+    ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    _check(load().moe_upload_expert_rows(table, ids.ctypes.data if len(ids) else None, len(ids), _s(stream)))
+
+
+def moe_table_record_consumers(table, stream=None):
+    _check(load().moe_table_record_consumers(table, _s(stream)))
+
+
+def moe_table_stats(table) -> dict:
+    c = TableCounters()
+    _check(load().moe_table_stats(table, ctypes.byref(c)))
+    return {n: int(getattr(c, n)) for n, _ in TableCounters._fields_}
+
+
+def moe_table_published(table, E):
+    import numpy as np
+    m = np.empty(E, dtype=np.int32)
+    _check(load().moe_table_published(table, m.ctypes.data))
+    return m

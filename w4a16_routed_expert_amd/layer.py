@@ -64,23 +64,86 @@ class RoutedExpertLayer:
                         self.topk_w, self.expert_offsets, self.sorted_pairs, self.pair_pos, self.active_list,
                         self.n_active, self.ws, self.ws_bytes, stream)
 
-    def ffn(self, x: torch.Tensor, stream=None, rows=None):
+    def ffn(self, x: torch.Tensor, stream=None, rows=None, table=None):
+        """Expert FFN over the rows tensor (or `rows`), or over a ResidentExpertTable's device rows."""
         T = x.shape[0]
-        B.moe_w4a16_expert_ffn(x, T, self.H, self.I, self.E, self.k, self.rows if rows is None else rows,
-                               self.row_stride, self.slot_map, self.expert_offsets, self.sorted_pairs,
-                               self.active_list, self.n_active, self.h, self.pair_out, self.status, stream)
+        if table is not None:
+            rows_dev, stride, smap = table.device()
+        else:
+            rows_dev, stride, smap = (self.rows if rows is None else rows), self.row_stride, self.slot_map
+        B.moe_w4a16_expert_ffn(x, T, self.H, self.I, self.E, self.k, rows_dev, stride, smap, self.expert_offsets,
+                               self.sorted_pairs, self.active_list, self.n_active, self.h, self.pair_out,
+                               self.status, stream)
 
     def combine(self, T: int, y: torch.Tensor, shared_out=None, shared_gate=None, stream=None):
         B.moe_combine(self.pair_out, self.pair_pos, self.topk_w, shared_out, shared_gate, T, self.H, self.k, y,
                       stream)
 
     def forward(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None, rows=None,
-                shared_out=None, shared_gate=None) -> torch.Tensor:
-        """y = layer(x); x float16 [T, H] on the device."""
+                shared_out=None, shared_gate=None, table=None) -> torch.Tensor:
+        """y = layer(x); x float16 [T, H] on the device.  With a ResidentExpertTable the
+        routed experts' misses are uploaded (host round trip of the active list) before
+        the expert FFN reads the table's rows."""
         T = x.shape[0]
         if y is None:
             y = torch.empty((T, self.H), dtype=torch.float16, device=self.device)
         self.route(x, stream)
-        self.ffn(x, stream, rows)
+        if table is not None:
+            table.prepare(self.active_experts(), stream)
+        self.ffn(x, stream, rows, table)
+        if table is not None:
+            table.record_consumers(stream)
         self.combine(T, y, shared_out, shared_gate, stream)
         return y
+
+    def active_experts(self):
+        """Active expert ids of the last route, on the host (synchronizes with the device)."""
+        n = int(self.n_active.cpu()[0])
+        return self.active_list[:n].cpu().numpy()
+
+
+class ResidentExpertTable:
+    """A resident expert table (moe_table_*) over an immutable host source of qpacked rows.
+
+    host_rows: uint8 numpy array [E, stride] holding every expert's row; kept referenced (and
+    never written) for the table's lifetime.  capacity experts stay published between steps;
+    spare_rows device rows receive misses.
+    """
+
+    def __init__(self, host_rows, H: int, I: int, capacity: int, spare_rows: int, staging_rows: int = 2,
+                 initial_resident=None, stream=None):
+        import numpy as np
+        self.host_rows = np.ascontiguousarray(host_rows)
+        self.E = self.host_rows.shape[0]
+        self.handle = B.moe_table_create(self.E, H, I, capacity, spare_rows, staging_rows, self.host_rows,
+                                         self.host_rows.strides[0], initial_resident, stream)
+
+    def device(self):
+        return B.moe_table_device(self.handle)
+
+    def prepare(self, active, stream=None):
+        """Start a step with these active experts: upload and publish the misses. Returns the misses."""
+        misses = B.moe_table_misses(self.handle, active)
+        if len(misses):
+            B.moe_upload_expert_rows(self.handle, misses, stream)
+        return misses
+
+    def record_consumers(self, stream=None):
+        B.moe_table_record_consumers(self.handle, stream)
+
+    def stats(self) -> dict:
+        return B.moe_table_stats(self.handle)
+
+    def published(self):
+        return B.moe_table_published(self.handle, self.E)
+
+    def close(self):
+        if self.handle:
+            B.moe_table_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
