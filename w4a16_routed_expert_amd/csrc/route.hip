@@ -24,6 +24,8 @@
 //   logits, top-k and softmax; route_group_kernel sorts.
 #include "moe_internal.h"
 
+#include <climits>
+
 namespace {
 
 constexpr int kSelThreads = 512;         // 8 waves per token
@@ -153,19 +155,17 @@ __device__ float exact_logit(const RouteArgs &a, int t, int e, long long (*red)[
     return r;
 }
 
-// Maximum of a float over the 64 lanes of a wavefront, in every lane: DPP
+// Maximum of an int over the 64 lanes of a wavefront, in every lane: DPP
 // shifts build per-row prefix maxima (lane 15 of each row of 16 holds the
 // row's maximum), two row broadcasts fold the rows into lane 63, and a
 // readlane hands it to every lane.
 template <int CTRL, int ROW_MASK>
-__device__ inline float dpp_max_step(float v)
+__device__ inline int dpp_max_step(int v)
 {
-    const int o = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY), __builtin_bit_cast(int, v), CTRL,
-                                              ROW_MASK, 0xf, false);
-    return fmaxf(v, __builtin_bit_cast(float, o));
+    return max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, CTRL, ROW_MASK, 0xf, false));
 }
 
-__device__ inline float wave_max(float v)
+__device__ inline int wave_max(int v)
 {
     v = dpp_max_step<0x111, 0xf>(v);         // row_shr:1
     v = dpp_max_step<0x112, 0xf>(v);         // row_shr:2
@@ -173,39 +173,130 @@ __device__ inline float wave_max(float v)
     v = dpp_max_step<0x118, 0xf>(v);         // row_shr:8
     v = dpp_max_step<0x142, 0xa>(v);         // row_bcast:15 into rows 1 and 3
     v = dpp_max_step<0x143, 0xc>(v);         // row_bcast:31 into rows 2 and 3
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// An int with the order of the finite float f (-0 and +0 map to one key).
+__device__ inline int order_key(float f)
+{
+    const int b = __builtin_bit_cast(int, f + 0.0f);
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+
+// Cross-lane sums without the LDS crossbar.  add_row_ror<N>: each lane adds
+// the value N lanes away inside its row of 16 (DPP rotation); add_partner:
+// adds the value of lane l ^ 16 (SIXTEEN) or l ^ 32 (gfx950 permlane swaps).
+template <int N>
+__device__ inline uint32_t ror_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
+}
+
+template <int N>
+__device__ inline double add_row_ror(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint64_t r = (uint64_t)ror_u32<N>((uint32_t)b) | ((uint64_t)ror_u32<N>((uint32_t)(b >> 32)) << 32);
+    return v + __builtin_bit_cast(double, r);
+}
+
+template <int N>
+__device__ inline float add_row_ror(float v)
+{
+    return v + __builtin_bit_cast(float, ror_u32<N>(__builtin_bit_cast(uint32_t, v)));
+}
+
+// One of the two swap results is the lane's own value, so XOR-ing both with
+// it leaves the partner's.
+template <bool SIXTEEN>
+__device__ inline uint32_t partner_u32(uint32_t v)
+{
+    const auto r = SIXTEEN ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] ^ r[1] ^ v;
+}
+
+template <bool SIXTEEN>
+__device__ inline double add_partner(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint64_t r = (uint64_t)partner_u32<SIXTEEN>((uint32_t)b) |
+                       ((uint64_t)partner_u32<SIXTEEN>((uint32_t)(b >> 32)) << 32);
+    return v + __builtin_bit_cast(double, r);
+}
+
+template <bool SIXTEEN>
+__device__ inline float add_partner(float v)
+{
+    return v + __builtin_bit_cast(float, partner_u32<SIXTEEN>(__builtin_bit_cast(uint32_t, v)));
+}
+
+// Sum over the lanes of the wavefront that share lane % EQ (EQ a power of two <= 16).
+template <int EQ, typename V>
+__device__ inline V sum_phases(V v)
+{
+    if constexpr (EQ <= 1) v = add_row_ror<1>(v);
+    if constexpr (EQ <= 2) v = add_row_ror<2>(v);
+    if constexpr (EQ <= 4) v = add_row_ror<4>(v);
+    if constexpr (EQ <= 8) v = add_row_ror<8>(v);
+    v = add_partner<true>(v);
+    return add_partner<false>(v);
 }
 
 // Top-k (ties to the lower expert index, slots in descending order) and
-// softmax over the k selected logits for token t; one full wavefront, lane =
-// expert, lv = that expert's final logit (bias included).  k rounds of a
-// wavefront maximum; the lowest lane holding it wins the slot and drops out.
-// Lane j < k keeps slot j; the softmax denominator is summed in slot order.
+// softmax over the k selected logits, for NTOK tokens at once (independent
+// chains, so their latencies overlap); one full wavefront, lane = expert,
+// lv[i] = that expert's final logit (bias included) for token tok[i] (tokens
+// >= a.T are skipped).  k rounds of a wavefront maximum; the lowest lane
+// holding it wins the slot and drops out.  Lane j < k keeps slot j.  The
+// softmax denominator is summed in a fixed order (DPP prefix over lanes 0..7).
 // Writes ids and w, and the ids also to s_ids (if not null).
-__device__ void topk_softmax_wave(const RouteArgs &a, int t, int lane, float lv, int *s_ids)
+template <int NTOK>
+__device__ void topk_softmax_wave(const RouteArgs &a, const int (&tok)[NTOK], int lane, const float (&lv)[NTOK],
+                                  int *s_ids)
 {
     const int E = a.E, k = a.k;
-    float v = lane < E ? lv : -INFINITY;     // missing experts never outrank a real one
-    int my_id = 0;
-    float my_l = 0.0f, m0 = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const float m = wave_max(v);
-        const int win = (int)__builtin_ctzll(__ballot(v == m));
-        if (lane == win) v = -INFINITY;
-        if (lane == j) {
-            my_id = win;
-            my_l = m;
-        }
-        if (j == 0) m0 = m;
+    int key[NTOK];
+    float my_l[NTOK], m0[NTOK];
+    int my_id[NTOK];
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        key[i] = lane < E ? order_key(lv[i]) : INT_MIN;  // missing experts never outrank a real one
+        my_id[i] = 0;
+        my_l[i] = 0.0f;
+        m0[i] = 0.0f;
     }
-    const float ex = lane < k ? expf(my_l - m0) : 0.0f;
-    float den = 0.0f;
-    for (int j = 0; j < k; ++j)
-        den += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
-    if (lane < k) {
-        a.ids[(size_t)t * k + lane] = my_id;
-        a.w[(size_t)t * k + lane] = ex / den;
-        if (s_ids) s_ids[t * k + lane] = my_id;
+    for (int j = 0; j < k; ++j) {
+        int m[NTOK];
+#pragma unroll
+        for (int i = 0; i < NTOK; ++i) m[i] = wave_max(key[i]);
+#pragma unroll
+        for (int i = 0; i < NTOK; ++i) {
+            const int win = (int)__builtin_ctzll(__ballot(key[i] == m[i]));
+            const float l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv[i]), win));
+            if (lane == win) key[i] = INT_MIN;
+            if (lane == j) {
+                my_id[i] = win;
+                my_l[i] = l;
+            }
+            if (j == 0) m0[i] = l;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        if (tok[i] >= a.T) continue;
+        const float ex = lane < k ? expf(my_l[i] - m0[i]) : 0.0f;
+        float den = ex;                       // lanes 0..7 of row 0 hold the k values
+        den += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, den), 0x111, 0xf, 0xf, false));
+        den += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, den), 0x112, 0xf, 0xf, false));
+        den += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, den), 0x114, 0xf, 0xf, false));
+        den = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, den), 7));
+        if (lane < k) {
+            const size_t p = (size_t)tok[i] * k + lane;
+            a.ids[p] = my_id[i];
+            a.w[p] = ex / den;
+            if (s_ids) s_ids[p] = my_id[i];
+        }
     }
 }
 
@@ -223,6 +314,12 @@ struct WLoad<4> {
     typedef unsigned int T __attribute__((ext_vector_type(2)));
     static __device__ inline T ld(const uint16_t *p) { return *reinterpret_cast<const T *>(p); }
     static __device__ inline uint16_t get(const T &v, int j) { return (uint16_t)(v[j >> 1] >> (16 * (j & 1))); }
+};
+template <>
+struct WLoad<2> {
+    typedef unsigned int T;
+    static __device__ inline T ld(const uint16_t *p) { return *reinterpret_cast<const T *>(p); }
+    static __device__ inline uint16_t get(const T &v, int j) { return (uint16_t)(v >> (16 * j)); }
 };
 template <>
 struct WLoad<1> {
@@ -355,7 +452,9 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
         if (a.bias) lv = lv + a.bias[lane];
         if (a.logits) a.logits[(size_t)t * E + lane] = lv;
     }
-    topk_softmax_wave(a, t, lane, lv, nullptr);
+    const int tok[1] = {t};
+    const float l1[1] = {lv};
+    topk_softmax_wave<1>(a, tok, lane, l1, nullptr);
 }
 
 constexpr int kGroupE = 16;                // experts per block in the decode kernel
@@ -375,7 +474,7 @@ __device__ inline unsigned long long same_expert_lanes(int e)
 }
 
 constexpr int kGrpLdsIds = 4096;           // pairs whose ids the grouping keeps in LDS
-constexpr int kTopkBatch = 8;              // tokens whose logits a wave loads at once
+constexpr int kTopkBatch = 2;              // tokens a wave routes together
 
 template <int NW, bool TOPK>
 struct GroupLds {
@@ -397,22 +496,22 @@ __device__ void group_phase(const RouteArgs &a, GroupLds<NW, TOPK> &S)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.T * a.k, E = a.E;
     if (TOPK) {
-        // logits of up to kTopkBatch tokens per wave are loaded before any is used
+        // kTopkBatch tokens per wave at a time: logits loaded, then routed together
         for (int t0 = wave; t0 < a.T; t0 += NW * kTopkBatch) {
+            int tok[kTopkBatch];
             float lv[kTopkBatch];
 #pragma unroll
             for (int i = 0; i < kTopkBatch; ++i) {
-                const int t = t0 + i * NW;
-                lv[i] = (lane < E && t < a.T) ? a.lbuf[(size_t)t * E + lane] : 0.0f;
+                tok[i] = t0 + i * NW;
+                // clamped (always valid) addresses: the loads issue back to back
+                lv[i] = a.lbuf[(size_t)min(tok[i], a.T - 1) * E + min(lane, E - 1)];
             }
+            if (a.logits && a.logits != a.lbuf && lane < E) {
 #pragma unroll
-            for (int i = 0; i < kTopkBatch; ++i) {
-                const int t = t0 + i * NW;
-                if (t < a.T) {
-                    if (a.logits && a.logits != a.lbuf && lane < E) a.logits[(size_t)t * E + lane] = lv[i];
-                    topk_softmax_wave(a, t, lane, lv[i], S.ids);
-                }
+                for (int i = 0; i < kTopkBatch; ++i)
+                    if (tok[i] < a.T) a.logits[(size_t)tok[i] * E + lane] = lv[i];
             }
+            topk_softmax_wave<kTopkBatch>(a, tok, lane, lv, S.ids);
         }
         __syncthreads();
     }
@@ -481,7 +580,7 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
 {
     constexpr int EQ = kGroupE / VEC;
     constexpr int RPW = 64 / EQ;
-    constexpr int U = 8;                     // rows in flight per thread
+    constexpr int U = VEC >= 8 ? 8 : 32;     // rows in flight per thread (all of H = 2048 in one batch)
     typedef WLoad<VEC> L;
     const int G = (a.E + kGroupE - 1) / kGroupE;
     const int t = blockIdx.x / G, g = blockIdx.x % G;
@@ -548,12 +647,9 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
     }
     // sum the RPW row phases within the wave (lanes eq, eq+EQ, ...)
 #pragma unroll
-    for (int off = EQ; off < 64; off <<= 1) {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            acc[j] += __shfl_xor(acc[j], off, 64);
-            bnd[j] += __shfl_xor(bnd[j], off, 64);
-        }
+    for (int j = 0; j < VEC; ++j) {
+        acc[j] = sum_phases<EQ>(acc[j]);
+        bnd[j] = sum_phases<EQ>(bnd[j]);
     }
     if (hp == 0) {
 #pragma unroll
@@ -573,8 +669,8 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
                 B += s_bnd[r][lane];
             }
         }
-        // same bound as route_select_kernel: at most H/(RPW*kSelWaves) + 6 + 8
-        // fp64 additions on any path, far below 2^9
+        // any summation path above has at most H/(RPW*kSelWaves) + 6 + 8 fp64
+        // additions, far below 2^9
         const double err = ldexp((double)B, -42);
         const bool certain = lane >= kGroupE || e >= E || (!a.force_exact && rn32_certain(v, err));
         if (lane < kGroupE) s_logit[lane] = (float)v;
@@ -656,8 +752,9 @@ int route_launch(const void *x_dev, const void *w_router_dev, const float *bias_
     const bool v4 = E % 4 == 0 && moe::aligned(w_router_dev, 8);
     if (small) {
         const unsigned int blocks = (unsigned int)T * (unsigned int)((E + kGroupE - 1) / kGroupE);
-        if (v8) hipLaunchKernelGGL(route_logits_kernel<8>, dim3(blocks), dim3(kSelThreads), 0, s, a);
-        else if (v4) hipLaunchKernelGGL(route_logits_kernel<4>, dim3(blocks), dim3(kSelThreads), 0, s, a);
+        // two experts per lane: short cross-lane sums, 4-byte router loads
+        if (E % 2 == 0 && moe::aligned(w_router_dev, 4))
+            hipLaunchKernelGGL(route_logits_kernel<2>, dim3(blocks), dim3(kSelThreads), 0, s, a);
         else hipLaunchKernelGGL(route_logits_kernel<1>, dim3(blocks), dim3(kSelThreads), 0, s, a);
         rc = moe::check_launch("moe_route (logits)");
         if (rc) return rc;
