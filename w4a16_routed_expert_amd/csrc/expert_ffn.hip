@@ -158,12 +158,7 @@ __device__ void build_table(SlotTable &tb, const FfnArgs &a, const int32_t *__re
         }
     }
     const int cnt = (e >= 0) ? ((n + 15) / 16) * items_per_tile : 0;
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
+    const int incl = moe::wave_inclusive_sum(cnt);
     if (lane < MOE_MAX_EXPERTS) {
         tb.e[lane] = e;
         tb.p0[lane] = p0;

@@ -231,7 +231,7 @@ __device__ inline float add_partner(float v)
     return v + __builtin_bit_cast(float, partner_u32<SIXTEEN>(__builtin_bit_cast(uint32_t, v)));
 }
 
-// Sum over the lanes of the wavefront that share lane % EQ (EQ a power of two <= 16).
+// Sum over the lanes of the wavefront that share lane % EQ (EQ a power of two <= 64).
 template <int EQ, typename V>
 __device__ inline V sum_phases(V v)
 {
@@ -239,8 +239,9 @@ __device__ inline V sum_phases(V v)
     if constexpr (EQ <= 2) v = add_row_ror<2>(v);
     if constexpr (EQ <= 4) v = add_row_ror<4>(v);
     if constexpr (EQ <= 8) v = add_row_ror<8>(v);
-    v = add_partner<true>(v);
-    return add_partner<false>(v);
+    if constexpr (EQ <= 16) v = add_partner<true>(v);
+    if constexpr (EQ <= 32) v = add_partner<false>(v);
+    return v;
 }
 
 // Top-k (ties to the lower expert index, slots in descending order) and
@@ -401,12 +402,9 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
     }
     // sum the PH row phases of each expert within the wave (lanes eq, eq+EQ, ...)
 #pragma unroll
-    for (int off = EQ; off < 64; off <<= 1) {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            acc[j] += __shfl_xor(acc[j], off, 64);
-            bnd[j] += __shfl_xor(bnd[j], off, 64);
-        }
+    for (int j = 0; j < VEC; ++j) {
+        acc[j] = sum_phases<EQ>(acc[j]);
+        bnd[j] = sum_phases<EQ>(bnd[j]);
     }
     if (hp == 0) {
 #pragma unroll
@@ -529,12 +527,7 @@ __device__ void group_phase(const RouteArgs &a, GroupLds<NW, TOPK> &S)
         // per expert (lane): total count, exclusive prefix over experts, per-wave starts
         int c = 0;
         for (int w = 0; w < NW; ++w) c += (lane < E) ? S.cnt[w][lane] : 0;
-        int incl = c;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
+        const int incl = moe::wave_inclusive_sum(c);
         const int excl = incl - c;
         int run = excl;
         for (int w = 0; w < NW; ++w) {
