@@ -159,6 +159,21 @@ int moe_route_exact(const void *x_dev, const void *w_router_dev, const float *bi
  * Weights are read as INT4 codes and converted to FP16 in registers; the
  * per-block FP16 scale is applied to the FP32 partial sum of each block, so
  * no expanded weight matrix is ever stored. */
+
+/* Kernel family of the three calls above (process-wide; MOE_FFN_PATH_AUTO by
+ * default).  Both families compute the same sums per scale block in FP32 and
+ * round at the same points, so their outputs agree to FP32 summation order.
+ *   MOE_FFN_PATH_STREAM: one wavefront per 16 pairs x 16 rows of an expert,
+ *     streaming each weight tile once per 16 pairs (built for decode batches,
+ *     bound by HBM);
+ *   MOE_FFN_PATH_GEMM: a grouped GEMM over 128-pair tiles of each expert
+ *     (built for prefill batches, bound by the matrix cores);
+ *   MOE_FFN_PATH_AUTO: the GEMM when T*k >= 64*E, else the streaming kernels.
+ * Returns MOE_OK, or MOE_ERR_INVALID_ARG for an unknown value.  Not
+ * synchronized with calls running on other threads. */
+enum moe_ffn_path { MOE_FFN_PATH_AUTO = 0, MOE_FFN_PATH_STREAM = 1, MOE_FFN_PATH_GEMM = 2 };
+int moe_set_ffn_path(int path);
+
 int moe_w4a16_gateup(const void *x_dev, int T, int H, int I, int E, int k,
                      const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                      const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,

@@ -1,18 +1,25 @@
 """Shared helpers of the parity tests (no arithmetic of the layer itself)."""
 import numpy as np
 
-# Layer-output tolerance: |got - want| <= REL * max(|want|, floor), floor = 2^-4 * max_c |want[t, c]|.
+# Layer-output tolerance: |got - want| <= REL * max(|want|, floor), floor = 2^-3 * max_c |want[t, c]|.
 # The relative bound 2e-3 applies after FP16 rounding of the output.  The floor
 # exists because the SwiGLU output h is rounded to FP16 before the down
 # projection: FP32 and fp64 evaluations of the same h round differently when
 # the value sits next to an FP16 rounding midpoint (about 1 element in 300),
 # and each such 1-ulp flip moves every output of that pair by |w_d| * ulp(h)
 # in absolute terms.  Outputs that are small through cancellation then see a
-# large relative change.  An FP32 model of the kernel arithmetic needs a floor
-# of up to 2^-5.8 * max|y_t| on the Qwen-shaped layer (2^-7 on OLMoE), so
-# 2^-4 leaves a margin of about 3.5x.  Normwise errors are reported as well.
+# large relative change.  A plain FP32 model of the layer (numpy matmuls on the
+# same weights) needs a floor of up to 2^-5.8 * max|y_t| on the Qwen-shaped
+# layer, 2^-7 on OLMoE, 2^-4.8 on the tiny layer at 300 tokens and 2^-3.6 on
+# the tiny layer at 300 tokens all routed to two experts; 2^-3 covers all of
+# them.  Normwise errors are reported as well.
 REL = 2e-3
-FLOOR = 2.0 ** -4
+FLOOR = 2.0 ** -3
+
+# Floor of the stage-wise comparison (the oracle's down projection and combine
+# applied to the GPU's own h): without the h rounding flips only FP32
+# summation-order noise remains, and the proposed 2^-8 floor holds.
+STAGE_FLOOR = 2.0 ** -8
 
 
 def f16_to_f64(a):

@@ -11,67 +11,12 @@ import numpy as np
 import pytest
 
 import oracle
-from parity_util import assert_close_rows, error_report
+from layer_util import check_full, gpu_layer, rows_of
+from parity_util import assert_close_rows
 from w4a16_routed_expert_amd import synth
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
-
-_ROWS = {}
-
-
-def rows_of(name):
-    if name not in _ROWS:
-        _ROWS[name] = synth.make_expert_rows(synth.CONFIGS[name])
-    return _ROWS[name]
-
-
-def gpu_layer(cfg, rows_np, wr, x, bias=None, slot_map=None, rows_dev=None):
-    from w4a16_routed_expert_amd.layer import RoutedExpertLayer
-    dev = torch.device("cuda:0")
-    T = x.shape[0]
-    if rows_dev is None:
-        rows_dev = torch.from_numpy(rows_np).to(dev)
-    lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, rows_dev, torch.from_numpy(wr).to(dev),
-                            None if bias is None else torch.from_numpy(bias).to(dev),
-                            None if slot_map is None else torch.from_numpy(slot_map).to(dev),
-                            max_T=max(T, 1), device=dev)
-    y = lay.forward(torch.from_numpy(x).to(dev))
-    torch.cuda.synchronize()
-    n = T * cfg.k
-    na = int(lay.n_active.cpu()[0]) if T else 0
-    return dict(y=y.cpu().numpy(), logits=lay.logits.cpu().numpy()[:T], ids=lay.topk_ids.cpu().numpy()[:T],
-                w=lay.topk_w.cpu().numpy()[:T], offsets=lay.expert_offsets.cpu().numpy(),
-                sorted_pairs=lay.sorted_pairs.cpu().numpy()[:n], pair_pos=lay.pair_pos.cpu().numpy()[:n],
-                active=lay.active_list.cpu().numpy(), n_active=na, h=lay.h.cpu().numpy()[:n],
-                pair_out=lay.pair_out.cpu().numpy()[:n], status=int(lay.status.cpu()[0]), layer=lay)
-
-
-def check_full(cfg, got, ref, what):
-    T, k = got["ids"].shape
-    assert np.array_equal(got["logits"].view(np.uint32), ref["logits"].view(np.uint32)), f"{what}: logits not bit-exact"
-    assert np.array_equal(got["ids"], ref["ids"]), f"{what}: expert ids differ"
-    assert np.allclose(got["w"], ref["w"], rtol=1e-5, atol=1e-7), f"{what}: routing weights differ"
-    assert np.allclose(got["w"].sum(axis=1), 1.0, atol=k * 2.0 ** -23)
-    assert np.array_equal(got["offsets"], ref["offsets"]), f"{what}: expert offsets differ"
-    assert np.array_equal(got["sorted_pairs"], ref["sorted_pairs"]), f"{what}: sorted pairs differ"
-    assert np.array_equal(got["pair_pos"], ref["pair_pos"]), f"{what}: pair positions differ"
-    assert got["n_active"] == ref["n_active"]
-    assert np.array_equal(got["active"][:ref["n_active"]], ref["active"])
-    assert np.all(got["active"][ref["n_active"]:] == -1)
-    if ref.get("h") is not None:
-        # grouped position pos holds pair sorted_pairs[pos]
-        assert_close_rows(got["h"].view(np.uint16), ref["h"][ref["sorted_pairs"]], f"{what}: h")
-    # Per-pair expert outputs are compared normwise (2e-3 of each pair's largest
-    # output): a 1-ulp flip of a large FP16 h (ulp 2^-8 for h in [4, 8)) times a
-    # large down weight moves single outputs by ~1e-4, which an elementwise test
-    # of these unrounded intermediates would flag.  The layer output y below is
-    # held to the elementwise criterion.
-    o_ref = ref["o"][ref["sorted_pairs"]]
-    assert_close_rows(got["pair_out"].astype(np.float64), o_ref, f"{what}: expert outputs", floor=1.0)
-    assert_close_rows(got["y"].view(np.uint16), ref["y"], f"{what}: y")
-    rel, norm = error_report(got["y"].view(np.uint16), ref["y"])
-    print(f"{what}: max rel err (no floor) {rel:.3g}, max normwise {norm:.3g}")
 
 
 # ---------------------------------------------------------------- tiny layer
@@ -80,7 +25,7 @@ def test_tiny_layer(T):
     cfg = synth.CONFIGS["tiny"]
     rows, wr, x = rows_of("tiny"), synth.make_router(cfg), synth.make_x(cfg, T)
     ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
-    check_full(cfg, gpu_layer(cfg, rows, wr, x), ref, f"tiny T={T}")
+    check_full(cfg, gpu_layer(cfg, rows, wr, x), ref, f"tiny T={T}", rows=rows)
 
 
 def test_skewed_routing_many_tokens_per_expert():
@@ -93,7 +38,7 @@ def test_skewed_routing_many_tokens_per_expert():
     bias[5], bias[2] = 50.0, 40.0
     ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, bias=bias, want_h=True)
     assert ref["n_active"] == 2
-    check_full(cfg, gpu_layer(cfg, rows, wr, x, bias=bias), ref, "tiny skewed")
+    check_full(cfg, gpu_layer(cfg, rows, wr, x, bias=bias), ref, "tiny skewed", rows=rows)
 
 
 def test_zero_router_ties_go_to_lower_index():
@@ -105,7 +50,7 @@ def test_zero_router_ties_go_to_lower_index():
     got = gpu_layer(cfg, rows, wr, x)
     assert np.array_equal(got["ids"], np.tile(np.arange(cfg.k), (T, 1)))
     assert np.all(got["w"] == np.float32(1.0 / cfg.k))
-    check_full(cfg, got, ref, "tiny zero router")
+    check_full(cfg, got, ref, "tiny zero router", rows=rows)
 
 
 def test_empty_batch():
@@ -158,7 +103,7 @@ def test_olmoe_decode_layer(T):
     cfg = synth.CONFIGS["olmoe"]
     rows, wr, x = rows_of("olmoe"), synth.make_router(cfg), synth.make_x(cfg, T)
     ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
-    check_full(cfg, gpu_layer(cfg, rows, wr, x), ref, f"olmoe T={T}")
+    check_full(cfg, gpu_layer(cfg, rows, wr, x), ref, f"olmoe T={T}", rows=rows)
 
 
 @pytest.mark.parametrize("T", [1, 16, 64])
@@ -166,7 +111,7 @@ def test_qwen_routed_decode_layer(T):
     cfg = synth.CONFIGS["qwen"]
     rows, wr, x = rows_of("qwen"), synth.make_router(cfg), synth.make_x(cfg, T)
     ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
-    check_full(cfg, gpu_layer(cfg, rows, wr, x), ref, f"qwen T={T}")
+    check_full(cfg, gpu_layer(cfg, rows, wr, x), ref, f"qwen T={T}", rows=rows)
 
 
 def test_olmoe_zipf_biased_layer():
@@ -175,7 +120,7 @@ def test_olmoe_zipf_biased_layer():
     rows, wr, x = rows_of("olmoe"), synth.make_router(cfg, layer=3), synth.make_x(cfg, T, layer=3)
     bias = synth.make_zipf_bias(cfg, layer=3)
     ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, bias=bias, want_h=True)
-    check_full(cfg, gpu_layer(cfg, rows, wr, x, bias=bias), ref, "olmoe zipf T=32")
+    check_full(cfg, gpu_layer(cfg, rows, wr, x, bias=bias), ref, "olmoe zipf T=32", rows=rows)
 
 
 def test_prefill_batch_sampled_tokens():

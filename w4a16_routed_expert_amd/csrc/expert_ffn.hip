@@ -44,130 +44,17 @@
 //   * Per scale block: acc += scale * P in FP32 (the FP16 scale multiplies the
 //     FP32 partial, weights are never rounded after scaling); the result is
 //     acc * 2^20.
-#include "moe_internal.h"
+#include "ffn_common.h"
+
+#include <atomic>
 
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using namespace ffn;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxNT = 16;                       // reduction axis <= 2048 columns
-constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit data format (gfx9 family)
-constexpr float kUnit = 1048576.0f;               // 2^20: a code c enters the MFMA as c * 2^-20
-constexpr float kZeroPoint = -8.0f / 1048576.0f;  // -8 * 2^-20
-constexpr uint32_t kNib = 0x00F000F0u;            // bits 4-7 of each half
-
-struct FfnArgs {
-    const uint16_t *x;          // [T][H] FP16
-    int T, H, I, E, k;
-    const uint8_t *rows;
-    size_t stride;
-    const int32_t *slot_map;    // [E] or null
-    const int32_t *offsets;     // [E+1]
-    const int32_t *sorted_pairs;
-    const int32_t *active;      // [E], -1 past the active count
-    const int32_t *n_active;    // [1]
-    uint16_t *h;                // [T*k][I] FP16
-    float *out;                 // [T*k][H] FP32
-    int32_t *status;
-    int row_bytes;
-    int off_q[3], off_s[3];     // gate, up, down sections of a row
-};
-
-__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ inline u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const uint8_t *base, int nbytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, nbytes, kRsrcWord3);
-}
-
-__device__ inline f32x4 mfma(half8 a, half8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ inline uint16_t float_to_half_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
-
-__device__ inline float half_bits_to_float(uint32_t b)
-{
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xFFFFu));
-}
-
-// FP16 scale -> float, converted at this point of the program so the
-// register that held it can be reloaded at once (left to itself the compiler
-// folds the conversion into a later mixed-precision FMA, which keeps the old
-// value alive past the reload and costs a copy and an early wait).
-__device__ inline float scale_f32(_Float16 h)
-{
-    float f;
-    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(h));
-    return f;
-}
-
-// Barrier that orders LDS only: prefetched global loads stay in flight across it
-// (__syncthreads() would also wait for every outstanding global load).
-__device__ inline void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Two FP16 values from the low (lo) or high (hi) halves of two dwords.
-__device__ inline uint32_t lo2(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ inline uint32_t hi2(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-// Per-block table of the active slots, built once in LDS: expert, first
-// grouped pair, pair count, device slot and the first work item of the slot.
-struct SlotTable {
-    int e[MOE_MAX_EXPERTS];
-    int p0[MOE_MAX_EXPERTS];
-    int n[MOE_MAX_EXPERTS];
-    int sl[MOE_MAX_EXPERTS];
-    int first[MOE_MAX_EXPERTS + 1];
-};
-
-// Built by wave 0, one lane per slot.  Routing metadata outside its valid
-// range (a workspace that was not zero-filled, say) marks the status word and
-// the slot gets no work.
-__device__ void build_table(SlotTable &tb, const FfnArgs &a, const int32_t *__restrict__ active,
-                            const int32_t *__restrict__ offsets, const int32_t *__restrict__ slot_map,
-                            int nact, int items_per_tile)
-{
-    const int lane = threadIdx.x;          // wave 0 only
-    int e = -1, p0 = 0, n = 0, sl = -1;
-    if (lane < nact) {
-        e = active[lane];
-        if (e >= 0 && e < a.E) {
-            const int q0 = offsets[e], q1 = offsets[e + 1];
-            if (q0 >= 0 && q1 >= q0 && (long long)q1 <= (long long)a.T * a.k) {
-                p0 = q0;
-                n = q1 - q0;
-                sl = slot_map ? slot_map[e] : e;
-            } else {
-                if (a.status) *a.status = MOE_ERR_INVALID_ARG;
-                e = -1;
-            }
-        } else {
-            e = -1;
-        }
-    }
-    const int cnt = (e >= 0) ? ((n + 15) / 16) * items_per_tile : 0;
-    const int incl = moe::wave_inclusive_sum(cnt);
-    if (lane < MOE_MAX_EXPERTS) {
-        tb.e[lane] = e;
-        tb.p0[lane] = p0;
-        tb.n[lane] = n;
-        tb.sl[lane] = sl;
-        tb.first[lane + 1] = incl;
-    }
-    if (lane == 0) tb.first[0] = 0;
-}
 
 // Tiles kept in flight per matrix: the whole unit when it is short, else the
 // largest divisor of the unit's tile count with at most 8 tiles of weights
@@ -325,10 +212,10 @@ struct Ffn {
             u32x4 *dst = &L.xl[(t * 4) * 64 + g * 16 + m];
             // kind q holds columns 8q + (1, 5, 0, 4, 3, 7, 2, 6) of the group,
             // the order in which the weight conversion yields them
-            dst[0] = u32x4{hi2(d0[0], d0[2]), lo2(d0[0], d0[2]), hi2(d0[1], d0[3]), lo2(d0[1], d0[3])};
-            dst[64] = u32x4{hi2(d1[0], d1[2]), lo2(d1[0], d1[2]), hi2(d1[1], d1[3]), lo2(d1[1], d1[3])};
-            dst[128] = u32x4{hi2(d2[0], d2[2]), lo2(d2[0], d2[2]), hi2(d2[1], d2[3]), lo2(d2[1], d2[3])};
-            dst[192] = u32x4{hi2(d3[0], d3[2]), lo2(d3[0], d3[2]), hi2(d3[1], d3[3]), lo2(d3[1], d3[3])};
+            dst[0] = permute_activations(d0);
+            dst[64] = permute_activations(d1);
+            dst[128] = permute_activations(d2);
+            dst[192] = permute_activations(d3);
             float s = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -390,9 +277,7 @@ struct Ffn {
                     const u32x4 w = wq[jd][mat];
                     half8 b[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        b[q] = __builtin_bit_cast(half8, u32x4{w[q] & kNib, (w[q] << 4) & kNib, (w[q] >> 8) & kNib,
-                                                               (w[q] >> 4) & kNib});
+                    for (int q = 0; q < 4; ++q) b[q] = codes_to_operand(w[q]);
                     sc[mat] = scale_f32(ws[jd][mat]);
                     // every read of this slot happens above: reload it in place
                     __builtin_amdgcn_sched_barrier(0);
@@ -462,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_ffn_kernel(FfnArgs a, const in
     if (nact > a.E) nact = a.E;
     if (nact <= 0) return;
     const F f(a, L, nact);
-    if (threadIdx.x < 64) build_table(L.tb, a, active, offsets, slot_map, nact, f.CH);
+    if (threadIdx.x < 64) build_table(L.tb, a, active, offsets, slot_map, nact, 16, f.CH);
     __syncthreads();
     const long long N = L.tb.first[nact];
     const int it0 = (int)(N * blockIdx.x / gridDim.x), it1 = (int)(N * (blockIdx.x + 1) / gridDim.x);
@@ -489,7 +374,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_ffn_kernel(FfnArgs a, const in
     }
 }
 
-int cu_count()
+}  // namespace
+
+int ffn::cu_count()
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -504,6 +391,8 @@ int cu_count()
     }
     return 256;
 }
+
+namespace {
 
 template <bool GATEUP, int NT, int S>
 int launch_one(const FfnArgs &a, hipStream_t s, long long max_items, const char *who)
@@ -554,9 +443,25 @@ int launch_nt(const FfnArgs &a, hipStream_t s, int S, long long max_items, const
     return launch_one<GATEUP, NT, 1>(a, s, max_items, who);
 }
 
+// Kernel family of the FFN calls (moe_set_ffn_path).
+std::atomic<int> g_ffn_path{MOE_FFN_PATH_AUTO};
+
+// The grouped GEMM once experts average 64 routed pairs or more: then the
+// layer is bound by the matrix cores and the streaming kernel, built to keep
+// HBM busy at a few pairs per expert, would convert every weight tile once
+// per 16 pairs.
+bool use_gemm(const FfnArgs &a)
+{
+    const int p = g_ffn_path.load(std::memory_order_relaxed);
+    if (p == MOE_FFN_PATH_STREAM) return false;
+    if (p == MOE_FFN_PATH_GEMM) return true;
+    return (long long)a.T * a.k >= 64LL * a.E;
+}
+
 template <bool GATEUP>
 int launch_ffn(const FfnArgs &a, hipStream_t s, const char *who)
 {
+    if (use_gemm(a)) return GATEUP ? launch_gemm_gateup(a, s) : launch_gemm_down(a, s);
     const int K = GATEUP ? a.H : a.I;
     const int R = GATEUP ? a.I : a.H;
     const int NT = K / 128, RG = R / 16;
@@ -632,6 +537,15 @@ int launch_down(const FfnArgs &a, hipStream_t s) { return launch_ffn<false>(a, s
 }  // namespace
 
 extern "C" {
+
+int moe_set_ffn_path(int path)
+{
+    moe::clear_error();
+    if (path != MOE_FFN_PATH_AUTO && path != MOE_FFN_PATH_STREAM && path != MOE_FFN_PATH_GEMM)
+        return moe::fail(MOE_ERR_INVALID_ARG, "moe_set_ffn_path: unknown path %d", path);
+    g_ffn_path.store(path, std::memory_order_relaxed);
+    return MOE_OK;
+}
 
 int moe_w4a16_gateup(const void *x_dev, int T, int H, int I, int E, int k,
                      const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,

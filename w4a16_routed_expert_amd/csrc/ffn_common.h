@@ -1,0 +1,152 @@
+// Pieces shared by the two W4A16 expert FFN kernels (the streaming kernel of
+// expert_ffn.hip for small batches, the grouped GEMM of expert_gemm.hip for
+// large ones): launch arguments, buffer resources, the INT4 -> FP16 operand
+// conversion and the per-block table of active experts.  Not part of the C ABI.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace ffn {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit data format (gfx9 family)
+constexpr float kUnit = 1048576.0f;               // 2^20: a code c enters the MFMA as c * 2^-20
+constexpr float kZeroPoint = -8.0f / 1048576.0f;  // -8 * 2^-20
+constexpr uint32_t kNib = 0x00F000F0u;            // bits 4-7 of each half
+
+struct FfnArgs {
+    const uint16_t *x;          // [T][H] FP16
+    int T, H, I, E, k;
+    const uint8_t *rows;
+    size_t stride;
+    const int32_t *slot_map;    // [E] or null
+    const int32_t *offsets;     // [E+1]
+    const int32_t *sorted_pairs;
+    const int32_t *active;      // [E], -1 past the active count
+    const int32_t *n_active;    // [1]
+    uint16_t *h;                // [T*k][I] FP16
+    float *out;                 // [T*k][H] FP32
+    int32_t *status;
+    int row_bytes;
+    int off_q[3], off_s[3];     // gate, up, down sections of a row
+};
+
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ inline u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int nbytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nbytes, kRsrcWord3);
+}
+
+__device__ inline f32x4 mfma(half8 a, half8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline uint16_t float_to_half_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+__device__ inline float half_bits_to_float(uint32_t b)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xFFFFu));
+}
+
+// FP16 scale -> float, converted at this point of the program so the
+// register that held it can be reloaded at once (left to itself the compiler
+// folds the conversion into a later mixed-precision FMA, which keeps the old
+// value alive past the reload and costs a copy and an early wait).
+__device__ inline float scale_f32(_Float16 h)
+{
+    float f;
+    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(h));
+    return f;
+}
+
+// Barrier that orders LDS only: prefetched global loads stay in flight across it
+// (__syncthreads() would also wait for every outstanding global load).
+__device__ inline void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Two FP16 values from the low (lo) or high (hi) halves of two dwords.
+__device__ inline uint32_t lo2(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ inline uint32_t hi2(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+// One MFMA B operand from a word of 8 codes (column 2i in the low nibble of
+// byte i): each nibble moved to bits 4-7 of an FP16 half is the subnormal
+// code * 2^-20.  Halves come out as columns (1, 5), (0, 4), (3, 7), (2, 6).
+__device__ inline half8 codes_to_operand(uint32_t w)
+{
+    return __builtin_bit_cast(half8, u32x4{w & kNib, (w << 4) & kNib, (w >> 8) & kNib, (w >> 4) & kNib});
+}
+
+// Eight FP16 activations (columns 0..7 in natural order) rearranged to the
+// column order of codes_to_operand.
+__device__ inline u32x4 permute_activations(u32x4 d)
+{
+    return u32x4{hi2(d[0], d[2]), lo2(d[0], d[2]), hi2(d[1], d[3]), lo2(d[1], d[3])};
+}
+
+// Per-block table of the active slots, built once in LDS: expert, first
+// grouped pair, pair count, device slot and the first work item of the slot.
+struct SlotTable {
+    int e[MOE_MAX_EXPERTS];
+    int p0[MOE_MAX_EXPERTS];
+    int n[MOE_MAX_EXPERTS];
+    int sl[MOE_MAX_EXPERTS];
+    int first[MOE_MAX_EXPERTS + 1];
+};
+
+// Built by wave 0, one lane per slot; a slot of n pairs has
+// ceil(n / tile) * items_per_tile work items.  Routing metadata outside its
+// valid range (a workspace that was not zero-filled, say) marks the status
+// word and the slot gets no work.
+__device__ inline void build_table(SlotTable &tb, const FfnArgs &a, const int32_t *__restrict__ active,
+                                   const int32_t *__restrict__ offsets, const int32_t *__restrict__ slot_map,
+                                   int nact, int tile, int items_per_tile)
+{
+    const int lane = threadIdx.x;          // wave 0 only
+    int e = -1, p0 = 0, n = 0, sl = -1;
+    if (lane < nact) {
+        e = active[lane];
+        if (e >= 0 && e < a.E) {
+            const int q0 = offsets[e], q1 = offsets[e + 1];
+            if (q0 >= 0 && q1 >= q0 && (long long)q1 <= (long long)a.T * a.k) {
+                p0 = q0;
+                n = q1 - q0;
+                sl = slot_map ? slot_map[e] : e;
+            } else {
+                if (a.status) *a.status = MOE_ERR_INVALID_ARG;
+                e = -1;
+            }
+        } else {
+            e = -1;
+        }
+    }
+    const int cnt = (e >= 0) ? ((n + tile - 1) / tile) * items_per_tile : 0;
+    const int incl = moe::wave_inclusive_sum(cnt);
+    if (lane < MOE_MAX_EXPERTS) {
+        tb.e[lane] = e;
+        tb.p0[lane] = p0;
+        tb.n[lane] = n;
+        tb.sl[lane] = sl;
+        tb.first[lane + 1] = incl;
+    }
+    if (lane == 0) tb.first[0] = 0;
+}
+
+// Compute units of the current device (cached per device).
+int cu_count();
+
+// Grouped-GEMM launches for large batches (expert_gemm.hip).
+int launch_gemm_gateup(const FfnArgs &a, hipStream_t s);
+int launch_gemm_down(const FfnArgs &a, hipStream_t s);
+
+}  // namespace ffn
