@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--kernel-only", default=None, choices=[None, "gateup", "copy"],
+    ap.add_argument("--kernel-only", default=None, choices=[None, "gateup", "down", "copy"],
                     help="profile helper: after setup, launch only this kernel --steps times "
                          "(copy: a 256 MiB device-to-device copy, the counter calibration)")
     ap.add_argument("--traffic-report", nargs=5, metavar=("GU_FETCH", "GU_WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"),
@@ -228,14 +228,23 @@ def main():
 
     names = ["route", "gateup", "down"] + (["shared"] if Is else []) + ["combine"]
 
-    if args.kernel_only == "gateup":
+    if args.kernel_only in ("gateup", "down"):
         lay.route(xs[0])
-        for s in range(args.steps):
-            rows = replicas[s % R]
+
+        def gateup(rows):
             B.moe_w4a16_gateup(xs[0], T, H, I, E, k, rows, lay.row_stride, None, lay.expert_offsets,
                                lay.sorted_pairs, lay.active_list, lay.n_active, lay.h, lay.status)
+        if args.kernel_only == "down":
+            gateup(replicas[0])
+        for s in range(args.steps):
+            rows = replicas[s % R]
+            if args.kernel_only == "gateup":
+                gateup(rows)
+            else:
+                B.moe_w4a16_down(T, H, I, E, k, rows, lay.row_stride, None, lay.expert_offsets, lay.active_list,
+                                 lay.n_active, lay.h, lay.pair_out, lay.status)
         torch.cuda.synchronize()
-        print(json.dumps({"kernel_only": "gateup", "launches": args.steps}))
+        print(json.dumps({"kernel_only": args.kernel_only, "launches": args.steps}))
         return
 
     # ---------------------------------------------------------------- graphs
