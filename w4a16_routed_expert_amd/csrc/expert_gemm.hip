@@ -8,40 +8,42 @@
 //
 // With hundreds of pairs per expert the layer is bound by the matrix cores,
 // not by HBM, so the design maximises MFMA work per converted weight and per
-// LDS byte:
-//   * v_mfma_f32_32x32x16_f16: on the MI355X it sustains about 2 PFLOP/s,
-//     the 16x16x32 form about 1.1 (measured with register-only chains).
+// LDS byte and keeps every global load off the instruction stream:
+//   * v_mfma_f32_32x32x16_f16 (8 passes: the same rate per FLOP as the
+//     16x16x32 form, half the instructions).
 //   * Work item = 128 grouped pairs of one expert x one block of output rows
 //     (gate/up: 128 rows of I for both matrices; down: 256 rows of H).  A
 //     block of 8 wavefronts takes one item; every wavefront owns all 128
-//     pairs (4 m-tiles of 32) x one 32-column n-tile: for gate/up 16 rows of
-//     the gate matrix and the same 16 rows of the up matrix (lane l and lane
-//     l ^ 16 then hold g and u of one output, so SiLU(g) * u needs one lane
-//     swap), for down 32 rows of H.  Each converted weight operand feeds 4
-//     MFMAs.
-//   * Activations: each K-tile (128 columns) of the item's 128 pairs is
-//     staged once in LDS (each wavefront instruction loads 4 whole pair rows
-//     of 256 bytes, rows gathered through sorted_pairs for gate/up), already
-//     permuted to the column order of the INT4 conversion; a ring of 3
-//     K-tiles, staged two K-tiles ahead, so one barrier per K-tile suffices.
-//     LDS layout: 64-byte granules, granule (row / 4, piece ^ (row / 4 % 4))
-//     holds the 16-byte piece of 4 consecutive rows, so the MFMA operand
-//     reads (32 rows x 2 pieces per instruction) and the staging writes are
-//     both free of bank conflicts.  The operand reads run several MFMAs ahead
-//     of their use.
-//   * Weights: per K-tile every lane loads two 16-byte chunks of qpacked
-//     tiles (two K-tiles ahead), chosen so that word w of a lane is the
-//     B operand of one MFMA: lanes 0-31 take columns 8w.., lanes 32-63 the
-//     columns 32 further on, and the activation operand reads the same
-//     columns.  Each 8-code word becomes one operand (7 VALU + 4 packed adds).
+//     pairs (4 m-tiles of 32) x one 32-row n-tile: for gate/up 16 rows of the
+//     gate matrix and the same 16 rows of the up matrix, for down 32 rows of
+//     H.  Each converted weight operand feeds 4 MFMAs.  The weights are the
+//     first MFMA operand, so a lane of the result holds one pair and 4
+//     consecutive output rows per register quad: gate and up of an output
+//     meet in the same lane, and the outputs leave as 8- and 16-byte stores.
+//   * Staging with direct global-to-LDS loads (no registers, no VALU): per
+//     K-tile (128 columns) the item's 128 activation rows (gathered through
+//     sorted_pairs for gate/up), each wavefront's two 1 KB weight tiles and
+//     its 32 row scales, in a ring of 3 K-tiles loaded two K-tiles ahead.
+//     One barrier per K-tile, preceded by a wait that counts the loads
+//     issued since (so the newer K-tile's loads stay in flight).
+//     Activation layout: 64-byte granules, granule (row / 4, piece ^ (row / 4
+//     % 4)) holds the 16-byte piece of 4 consecutive rows, so one direct load
+//     instruction fills a whole 1 KB granule run and the MFMA operand reads
+//     (32 rows x 2 pieces per instruction) are free of bank conflicts.  The
+//     operand reads run several MFMAs ahead of their use.
+//   * Weights: K-step s of a lane uses word s % 4 of chunk s / 4 of its row
+//     (lanes 0-31 columns 32 h2 + 64 (s / 4) + 8 (s % 4).., lanes 32-63 the
+//     columns 32 further on) and the activation reads the same columns.  Each
+//     8-code word becomes one operand in natural column order (7 VALU + 4
+//     packed adds).
 //   * Zero point in the operand: the converted subnormal code * 2^-20 minus
 //     8 * 2^-20 (one packed FP16 add per dword) is (code - 8) * 2^-20 exactly,
 //     so no activation sums are needed.  Per scale block the 8 K-steps
 //     accumulate P = sum x * (code - 8) * 2^-20 on the matrix cores, then
 //     acc += scale * P in FP32 (weights never rounded after scaling); the
 //     result is acc * 2^20.
-//   * An odd number of K-tiles is padded with one K-tile that reads nothing
-//     and computes nothing, so every scale block has two ring slots.
+//   * An odd number of K-tiles is padded with one K-tile whose weight
+//     operands are exactly zero, so every scale block has two ring slots.
 #include "ffn_common.h"
 
 #include <type_traits>
@@ -51,6 +53,7 @@ namespace {
 using namespace ffn;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGWaves = 8;
 constexpr int kGThreads = 64 * kGWaves;
@@ -66,6 +69,8 @@ constexpr uint32_t kNone = 0x40000000u;
 
 struct GLds {
     uint8_t xa[kStages][kStageBytes];    // staged activations (layout: see stage_addr)
+    uint8_t wt[kStages][kGWaves][2048];  // each wavefront's two weight tiles of a K-tile
+    uint8_t sc[kStages][kGWaves][256];   // each wavefront's 32 row scales of the K-tile's scale block (64 bytes used)
     uint32_t src[2][kBM];                // byte offset of each pair's activation row (kNone: none), two items
     SlotTable tb;
 };
@@ -80,6 +85,10 @@ struct GItem {
     int absent;           // the expert has no device row
 };
 
+// Byte offset of 16-byte piece c (columns 8c .. 8c+7 of the K-tile) of
+// staged row r: granule (r / 4) * 16 + (c ^ (r / 4 % 4)) of 64 bytes, slot r % 4.
+__device__ inline int stage_addr(int r, int c) { return (((r >> 2) << 4) + (c ^ ((r >> 2) & 3))) * 64 + (r & 3) * 16; }
+
 __device__ inline f32x16 mfma32(half8 a, half8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -93,10 +102,9 @@ struct Gemm {
     const FfnArgs &a;
     GLds &L;
     int nact;
-    int lane, wave, j32, h2, sc, sr0;
+    int lane, wave, j32, h2;
     int K, NT, NTP, NBK, RG, NBLK;
-    int lrg, lmat;                       // this lane's n-tile column: row group offset and matrix
-    int qsec, ssec;                      // byte offsets of that matrix's codes and scales in a row
+    int wrd;                             // this lane's chunk 0 in a wavefront's weight stage
     int aq[4];                           // stage_addr of this lane's operand pieces, m-tile 0, K-steps q (+ 4n)
 
     __device__ Gemm(const FfnArgs &args, GLds &lds, int nact_) : a(args), L(lds), nact(nact_)
@@ -106,25 +114,18 @@ struct Gemm {
         wave = uni(tid >> 6);
         j32 = lane & 31;                 // MFMA column (output row) of the lane
         h2 = lane >> 5;                  // which 8 of the 16 K values the lane feeds
-        sc = lane >> 2;                  // staging: 16-byte piece of a K-tile row
-        sr0 = 4 * wave + (lane & 3);     // staging: rows sr0 + 32 j (4 whole rows per instruction)
         K = GATEUP ? a.H : a.I;
         NT = K / 128;
         NTP = NT + (NT & 1);
         NBK = (NT + 1) / 2;
         RG = (GATEUP ? a.I : a.H) / 16;
         NBLK = (RG + RGB - 1) / RGB;
-        lrg = GATEUP ? wave : 2 * wave + (j32 >> 4);
-        lmat = GATEUP ? (j32 >> 4) : 2;
         // selected from uniform values: indexing the argument arrays with the
         // per-lane matrix would read them with vector loads
-        qsec = GATEUP ? (lmat ? a.off_q[1] : a.off_q[0]) : a.off_q[2];
-        ssec = GATEUP ? (lmat ? a.off_s[1] : a.off_s[0]) : a.off_s[2];
-        for (int q = 0; q < 4; ++q) aq[q] = stage_addr_(j32, 4 * h2 + q);
+        // tile j32 / 16, row j32 % 16, columns 32 h2 .. +31 (chunk 1: 64 further on)
+        wrd = 1024 * (j32 >> 4) + (16 * h2 + (j32 & 15)) * 16;
+        for (int q = 0; q < 4; ++q) aq[q] = stage_addr(j32, 4 * h2 + q);
     }
-
-    // same as stage_addr below (needed here before its definition)
-    static __device__ int stage_addr_(int r, int c) { return (((r >> 2) << 4) + (c ^ ((r >> 2) & 3))) * 64 + (r & 3) * 16; }
 
     __device__ GItem none() const
     {
@@ -169,42 +170,56 @@ struct Gemm {
         return rsrc(a.h + (size_t)it.p0 * a.I, ok ? it.nval * a.I * 2 : 0);
     }
 
-    // Row offsets of the item's pairs into L.src[par] (threads 0..127).
-    __device__ void write_src(const GItem &it, int par) const
+    // The routed pair behind grouped pair threadIdx % 128 of the item, as
+    // loaded (gate/up only).  Every thread issues exactly one load (a buffer
+    // load that reads nothing past the item's pairs), which the wait counts
+    // rely on.
+    __device__ uint32_t pair_of(const GItem &it) const
     {
-        const int r = threadIdx.x;
-        if (r >= kBM) return;
-        uint32_t o = kNone;
-        if (r < it.nval) {
-            if (GATEUP) {
-                const int tok = a.sorted_pairs[it.p0 + r] / a.k;
-                if (tok >= 0 && tok < a.T) o = (uint32_t)tok * (uint32_t)(a.H * 2);
-            } else {
-                o = (uint32_t)r * (uint32_t)(a.I * 2);
-            }
+        if constexpr (!GATEUP) return 0;
+        const int r = threadIdx.x & (kBM - 1);
+        return __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.sorted_pairs + it.p0, it.nval * 4), (uint32_t)r * 4u, 0, 0);
+    }
+
+    // Row offset of that pair's activation row (kNone: none).
+    __device__ uint32_t src_of(const GItem &it, uint32_t pair) const
+    {
+        const int r = threadIdx.x & (kBM - 1);
+        if constexpr (GATEUP) {
+            const int tok = (int)pair / a.k;
+            return (r < it.nval && tok >= 0 && tok < a.T) ? (uint32_t)tok * (uint32_t)(a.H * 2) : kNone;
+        } else {
+            return r < it.nval ? (uint32_t)r * (uint32_t)(a.I * 2) : kNone;
         }
-        L.src[par][r] = o;
     }
 
-    // Chunk `half` (0, 1) of this lane's weights for K-tile kt: 16 bytes of
-    // row j32 % 16 of its row group, columns 32 (h2 + 2 half) .. +31 of the
-    // K-tile; zeros for a K-tile or row group that does not exist.
-    __device__ u32x4 load_q(const GItem &it, int kt, int half) const
+    __device__ void put_src(int par, uint32_t o) const
     {
-        const int rg = it.rg0 + lrg;
-        const bool ok = kt < NT && rg < RG;
-        const uint32_t off = ok ? (uint32_t)(qsec + (rg * NT + kt) * 1024 + (16 * (h2 + 2 * half) + (j32 & 15)) * 16)
-                                : kNone;
-        return __builtin_amdgcn_raw_buffer_load_b128(rsrc(it.row, it.nrec), off, 0, 0);
+        if (threadIdx.x < kBM) L.src[par][threadIdx.x] = o;
     }
 
-    // FP16 scale of scale block b of this lane's output row.
-    __device__ _Float16 load_s(const GItem &it, int b) const
+    // Byte offset in the weight stage of tile t (0, 1) of this wavefront for
+    // K-tile kt: the qpacked tile of row group rg0 + wave (gate/up: t = the
+    // matrix) or rg0 + 2 wave + t (down); kNone for a K-tile or row group
+    // that does not exist.
+    __device__ uint32_t wtile_off(const GItem &it, int kt, int t) const
     {
-        const int rg = it.rg0 + lrg;
-        const uint32_t off = rg < RG ? (uint32_t)(ssec + ((rg * NBK + b) * 16 + (j32 & 15)) * 2) : kNone;
-        const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(rsrc(it.row, it.nrec), off, 0, 0);
-        return __builtin_bit_cast(_Float16, v);
+        const int rg = it.rg0 + (GATEUP ? wave : 2 * wave + t);
+        const int sec = GATEUP ? (t ? a.off_q[1] : a.off_q[0]) : a.off_q[2];
+        return (kt < NT && rg < RG) ? (uint32_t)(sec + (rg * NT + kt) * 1024) : kNone;
+    }
+
+    // Byte offset, for lane l < 16, of 4 bytes of the wavefront's row scales
+    // of scale block b: lanes 0-7 the 16 scales of its first tile's row group
+    // (gate, or the first down row group), lanes 8-15 those of the second
+    // (up, or the second down row group); kNone for other lanes and for a
+    // row group that does not exist.
+    __device__ uint32_t scale_off(const GItem &it, int b) const
+    {
+        const int t = (lane >> 3) & 1;
+        const int rg = it.rg0 + (GATEUP ? wave : 2 * wave + t);
+        const int sec = GATEUP ? (t ? a.off_s[1] : a.off_s[0]) : a.off_s[2];
+        return (lane < 16 && rg < RG) ? (uint32_t)(sec + (rg * NBK + b) * 32 + 4 * (lane & 7)) : kNone;
     }
 };
 
@@ -219,24 +234,29 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// Byte offset of 16-byte piece c (columns 8c .. 8c+7 of the K-tile) of
-// staged row r: granule (r / 4) * 16 + (c ^ (r / 4 % 4)) of 64 bytes, slot r % 4.
-__device__ inline int stage_addr(int r, int c) { return (((r >> 2) << 4) + (c ^ ((r >> 2) & 3))) * 64 + (r & 3) * 16; }
-
-// permute_activations with one byte permute per dword.
-__device__ inline u32x4 permute_pieces(u32x4 d)
+// One MFMA B operand from a word of 8 codes (column 2i in the low nibble of
+// byte i) with the columns in natural order: half j is code j moved to bits
+// 4-7, the FP16 subnormal code * 2^-20, plus the zero point zp (-8 * 2^-20,
+// which makes (code - 8) * 2^-20 exactly; 0 for a padding K-tile, whose
+// operand is then exactly zero).  Byte j of lo holds code 2j in its high
+// nibble, byte j of hi code 2j + 1; one byte permute per dword places them.
+__device__ inline half8 codes_to_signed_natural(uint32_t w, half8 zp)
 {
-    return u32x4{__builtin_amdgcn_perm(d[2], d[0], 0x07060302u), __builtin_amdgcn_perm(d[2], d[0], 0x05040100u),
-                 __builtin_amdgcn_perm(d[3], d[1], 0x07060302u), __builtin_amdgcn_perm(d[3], d[1], 0x05040100u)};
+    const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+    const u32x4 d = {__builtin_amdgcn_perm(hi, lo, 0x0C040C00u), __builtin_amdgcn_perm(hi, lo, 0x0C050C01u),
+                     __builtin_amdgcn_perm(hi, lo, 0x0C060C02u), __builtin_amdgcn_perm(hi, lo, 0x0C070C03u)};
+    return __builtin_bit_cast(half8, d) + zp;
 }
 
-// codes_to_operand minus 8 * 2^-20 in every half: (code - 8) * 2^-20, exact
-// (FP16 subnormals are kept, and the difference is a multiple of 2^-24).
-__device__ inline half8 codes_to_signed_operand(uint32_t w)
+// End of a K-tile: this wavefront's direct-to-LDS loads older than its
+// newest N vector-memory operations are complete (N counted by the caller),
+// its LDS operations too, then the block barrier.  Written as one asm
+// statement so that no memory fence asks for every outstanding load.
+template <int N>
+__device__ inline void stage_barrier()
 {
-    const _Float16 m8 = (_Float16)(-8.0f / 1048576.0f);
-    const half8 z = {m8, m8, m8, m8, m8, m8, m8, m8};
-    return codes_to_operand(w) + z;
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // SiLU(g) * u in FP32 with the hardware exponential and reciprocal (about
@@ -260,6 +280,9 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
     if (nact <= 0) return;
     const G f(a, L, nact);
     if (threadIdx.x < 64) build_table(L.tb, a, active, offsets, slot_map, nact, kBM, f.NBLK);
+    // Stages start as zeros: rows that no load fills then hold finite values.
+    for (int i = threadIdx.x; i < kStages * kStageBytes / 16; i += kGThreads)
+        reinterpret_cast<u32x4 *>(&L.xa[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     // Items are numbered slot by slot (m-block major, row block minor).  The
     // block runs on die (XCD) blockIdx % 8; each die takes a contiguous
@@ -279,8 +302,10 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
     int ci = 0;                            // item of the current K-tile, counted from the block's first
     GItem cur = f.item(item_no(0), c1, hint);
     GItem nxt = f.item(item_no(1), c1, hint);
-    f.write_src(cur, 0);
-    f.write_src(nxt, 1);
+    f.put_src(0, f.src_of(cur, f.pair_of(cur)));
+    f.put_src(1, f.src_of(nxt, f.pair_of(nxt)));
+    uint32_t pend = 0;                     // pair_of the next item, loaded at the last item end
+    bool pend_put = true;
     if (cur.absent && threadIdx.x == 0 && a.status) *a.status = MOE_ERR_ABSENT_EXPERT;
 
     f32x16 acc[kMT], P[kMT];
@@ -289,41 +314,42 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
         acc[mt] = f32x16{};
         P[mt] = acc[mt];
     }
-    u32x4 wq[2][2];                        // [ring slot][chunk]
-    wq[0][0] = f.load_q(cur, 0, 0);
-    wq[0][1] = f.load_q(cur, 0, 1);
-    wq[1][0] = f.load_q(cur, 1, 0);
-    wq[1][1] = f.load_q(cur, 1, 1);
-    _Float16 ws = f.load_s(cur, 0);       // scale of the block being accumulated
-    float wprev = 0.f;                     // scale of the block being merged
-
-    // Global loads of K-tile kt of item `it` (row offsets in L.src[par]);
-    // a row that reads nothing has offset kNone, which stays out of range
-    // with the column added.
-    auto fetch = [&](const GItem &it, int par, int kt, u32x4 (&d)[4]) {
+    // K-tile kt of item `it` (row offsets in L.src[par]) loaded straight
+    // into stage st: one instruction per row quad g = wave + 8 j fills the
+    // 1 KB granule run of rows 4g .. 4g+3, lane l taking row 4g + l % 4,
+    // piece (l / 4) ^ (g % 4), which lands at stage_addr of that row and
+    // piece.  A row that reads nothing has offset kNone, which stays out of
+    // range with the column added (the lane stores zeros or nothing; such
+    // rows only feed outputs that are never written).
+    // The wavefront's two weight tiles go to its own part of the weight
+    // stage, lane l taking bytes 16 l .. 16 l + 15 of each.
+    auto dma = [&](const GItem &it, int par, int kt, int st) {
         const __amdgpu_buffer_rsrc_t r = f.src_rsrc(it, kt);
-        const uint32_t col = kt * 256 + 16 * f.sc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            d[j] = __builtin_amdgcn_raw_buffer_load_b128(r, L.src[par][f.sr0 + 32 * j] + col, 0, 0);
-    };
-    // Staged K-tile into stage `st`.
-    auto stage = [&](int st, const u32x4 (&d)[4]) {
-        uint8_t *dst = &L.xa[st][0];
+        for (int j = 0; j < 4; ++j) {
+            const int g = f.wave + 8 * j;
+            const uint32_t off = L.src[par][4 * g + (f.lane & 3)] + kt * 256 + 16 * ((f.lane >> 2) ^ (g & 3));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&L.xa[st][1024 * g], 16,
+                                                     off, 0, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t rw = rsrc(it.row, it.nrec);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4 *>(dst + stage_addr(f.sr0 + 32 * j, f.sc)) = permute_pieces(d[j]);
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t woff = f.wtile_off(it, kt, t) + 16 * f.lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)&L.wt[st][f.wave][1024 * t],
+                                                     16, woff, 0, 0, 0);
+        }
+        // the row scales of the K-tile's scale block (both K-tiles of a
+        // block load them; the merge reads those of the second)
+        const uint32_t soff = f.scale_off(it, kt >> 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)&L.sc[st][f.wave][0], 4, soff,
+                                                 0, 0, 0);
     };
 
     __syncthreads();
-    {
-        u32x4 d[4];
-        fetch(cur, 0, 0, d);
-        stage(0, d);
-        fetch(cur, 0, 1, d);
-        stage(1, d);
-    }
-    lds_barrier();
+    dma(cur, 0, 0, 0);
+    dma(cur, 0, 1, 1);
+    stage_barrier<0>();
 
     const int total = nk * NTP;
     int kt = 0;
@@ -335,14 +361,10 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
             const bool anx = kt + 2 >= NTP;
             const int akt = anx ? kt + 2 - NTP : kt + 2;
             const GItem &ait = anx ? nxt : cur;
-            const int sst = (gg + 2) % kStages;
-            u32x4 d[4];
-            fetch(ait, (ci + anx) & 1, akt, d);
-            if (SLOT == 1) {
-                // this block's scale for the merge at its end; the next block's loaded
-                wprev = scale_f32(ws);
-                ws = f.load_s(ait, akt / 2);
-            }
+            dma(ait, (ci + anx) & 1, akt, (gg + 2) % kStages);
+            // the direct-to-LDS loads stay first in the K-tile (the count at
+            // its end relies on it)
+            __builtin_amdgcn_sched_barrier(0);
             {
                 // 32 steps (K-step s of 16 columns, m-tile mt), one MFMA each;
                 // the operand reads from LDS run kPD steps ahead of their use.
@@ -360,21 +382,29 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
 #pragma unroll
                 for (int st = 0; st < kPD; ++st) xr[st] = rd(st);
                 half8 bq;
+                // a padding K-tile's operand is exactly zero (its stage may hold stale codes)
+                const bool real = kt < f.NT;
+                const _Float16 zs = real ? (_Float16)(-8.0f / 1048576.0f) : (_Float16)0.0f;
+                const half8 zp = {zs, zs, zs, zs, zs, zs, zs, zs};
+                const uint32_t wmask = real ? 0xFFFFFFFFu : 0u;
+                const uint8_t *wsrc = &L.wt[gg % kStages][f.wave][f.wrd];
+                u32x4 wq[2];
+                wq[0] = *reinterpret_cast<const u32x4 *>(wsrc);
                 static_for<0, 32>([&](auto c) {
                     constexpr int st = decltype(c)::value;
                     constexpr int s = st >> 2, mt = st & 3;
                     constexpr bool pre = st + kPD < 32;
                     if constexpr (pre) xr[(st + kPD) % (kPD + 1)] = rd(st + kPD);
-                    if constexpr (mt == 0) bq = codes_to_signed_operand(wq[SLOT][s >> 2][s & 3]);
-                    if constexpr (st == 13) wq[SLOT][0] = f.load_q(ait, akt, 0);
-                    if constexpr (st == 29) wq[SLOT][1] = f.load_q(ait, akt, 1);
+                    if constexpr (st == 8) wq[1] = *reinterpret_cast<const u32x4 *>(wsrc + 512);
+                    if constexpr (mt == 0) bq = codes_to_signed_natural(wq[s >> 2][s & 3] & wmask, zp);
                     const half8 xf = xr[st % (kPD + 1)];
+                    // weights as the first operand: lane l of the result then
+                    // holds pair l % 32 of the m-tile (see the epilogue)
                     if constexpr (SLOT == 0 && s == 0) {
-                        P[mt] = mfma32(xf, bq, f32x16{});
+                        P[mt] = mfma32(bq, xf, f32x16{});
                     } else {
-                        P[mt] = mfma32(xf, bq, P[mt]);
+                        P[mt] = mfma32(bq, xf, P[mt]);
                     }
-                    if constexpr (st == 20) stage(sst, d);
                     // keep the schedule in step order: the read kPD steps
                     // ahead, this step's MFMA, a share of the other work
                     __builtin_amdgcn_sched_group_barrier(0x100, pre ? 1 : 0, 0);
@@ -384,49 +414,98 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
             }
 
             if (SLOT == 1) {
-                // the scale block ends: acc += scale * P
+                // The scale block ends: acc += scale * P.  Register r of lane
+                // l holds output row n = 8 (r / 4) + 4 h2 + r % 4 of the
+                // wavefront's 32 (tile n / 16, row n % 16), pair l % 32 of the
+                // m-tile; the scales of rows 8 q + 4 h2 .. +3 are 8 bytes at
+                // 16 q + 8 h2 of the wavefront's scale stage.
+                const uint8_t *sp = &L.sc[gg % kStages][f.wave][8 * f.h2];
+                _Float16 scl[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(sp + 16 * q);
+                    scl[4 * q + 0] = __builtin_bit_cast(_Float16, (uint16_t)(v[0] & 0xFFFFu));
+                    scl[4 * q + 1] = __builtin_bit_cast(_Float16, (uint16_t)(v[0] >> 16));
+                    scl[4 * q + 2] = __builtin_bit_cast(_Float16, (uint16_t)(v[1] & 0xFFFFu));
+                    scl[4 * q + 3] = __builtin_bit_cast(_Float16, (uint16_t)(v[1] >> 16));
+                }
 #pragma unroll
                 for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mt][r] += wprev * P[mt][r];
+                    for (int r = 0; r < 16; ++r) acc[mt][r] += (float)scl[r] * P[mt][r];
             }
             if (SLOT == 1 && kt == NTP - 1) {
-                // item done: write its outputs.  Lane l holds column j32 for
-                // rows 8 (r / 4) + 4 h2 + r % 4 of each 32-pair m-tile.
-                const int rg = cur.rg0 + f.lrg;
-                const bool rows_ok = rg < f.RG;
+                // Item done: write its outputs with buffer stores whose range
+                // ends at the item's last pair (pairs past it are dropped).
+                // Gate/up: rows n < 16 are gate rows, n + 16 the up rows of
+                // the same outputs, so lane l holds g and u of outputs
+                // 4 h2 + 0..3 and 8 + 4 h2 + 0..3 of its row group: two
+                // 8-byte stores per m-tile.  Down: outputs 8 q + 4 h2 + 0..3
+                // of the wavefront's 32 rows of H, four 16-byte stores.
+                if constexpr (GATEUP) {
+                    const int rg = cur.rg0 + f.wave;
+                    {
+                        const __amdgpu_buffer_rsrc_t ro = rsrc(a.h + (size_t)cur.p0 * a.I, cur.nval * a.I * 2);
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
+                        for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int lp = 32 * mt + 8 * (r >> 2) + 4 * f.h2 + (r & 3);
-                        const float v = acc[mt][r] * kUnit;
-                        if constexpr (GATEUP) {
-                            // lanes with j32 < 16 hold g, lanes j32 + 16 the u of the same row
-                            const float u = __builtin_bit_cast(float, moe::partner_u32<true>(__builtin_bit_cast(uint32_t, v)));
-                            if (f.j32 < 16 && rows_ok && lp < cur.nval) {
-                                const size_t pr = (size_t)(cur.p0 + lp);
-                                a.h[pr * a.I + rg * 16 + f.j32] = cur.absent ? (uint16_t)0 : float_to_half_bits(silu_mul(v, u));
+                            for (int q = 0; q < 2; ++q) {
+                                uint32_t w[2];
+#pragma unroll
+                                for (int e = 0; e < 2; ++e) {
+                                    const int r0 = 4 * q + 2 * e;
+                                    const float h0 = silu_mul(acc[mt][r0] * kUnit, acc[mt][r0 + 8] * kUnit);
+                                    const float h1 = silu_mul(acc[mt][r0 + 1] * kUnit, acc[mt][r0 + 9] * kUnit);
+                                    w[e] = cur.absent ? 0u : (uint32_t)float_to_half_bits(h0) | ((uint32_t)float_to_half_bits(h1) << 16);
+                                }
+                                const uint32_t off = rg < f.RG ? (uint32_t)(((32 * mt + f.j32) * a.I + rg * 16 + 8 * q + 4 * f.h2) * 2) : kNone;
+                                __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, ro, off, 0, 0);
                             }
-                        } else {
-                            if (rows_ok && lp < cur.nval) {
-                                const size_t pr = (size_t)(cur.p0 + lp);
-                                a.out[pr * a.H + rg * 16 + (f.j32 & 15)] = cur.absent ? 0.0f : v;
-                            }
-                        }
                     }
+                } else {
+                    const int rg = cur.rg0 + 2 * f.wave;
+                    {
+                        const __amdgpu_buffer_rsrc_t ro = rsrc(a.out + (size_t)cur.p0 * a.H, cur.nval * a.H * 4);
+#pragma unroll
+                        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                f32x4 v;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) v[e] = cur.absent ? 0.0f : acc[mt][4 * q + e] * kUnit;
+                                const uint32_t off = rg < f.RG ? (uint32_t)(((32 * mt + f.j32) * a.H + rg * 16 + 8 * q + 4 * f.h2) * 4) : kNone;
+                                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off, 0, 0);
+                            }
+                    }
+                }
 #pragma unroll
                 for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x16{};
                 ++ci;
                 cur = nxt;
                 nxt = f.item(item_no(ci + 1), c1, hint);
-                f.write_src(nxt, (ci + 1) & 1);
+                // The next item's row offsets: loaded now, written to LDS at
+                // the end of the following K-tile (the first direct loads that
+                // read them come two K-tiles before this item ends; with only
+                // two K-tiles per item, at once).
+                pend = f.pair_of(nxt);
+                pend_put = NTP == 2;
+                if (pend_put) f.put_src((ci + 1) & 1, f.src_of(nxt, pend));
                 if (cur.absent && threadIdx.x == 0 && a.status) *a.status = MOE_ERR_ABSENT_EXPERT;
                 kt = 0;
+                // Issued after the stages read next (loaded at the start of
+                // the previous K-tile): this K-tile's 7 direct loads, the
+                // output stores (gate/up 8, down 16) and the offset load.
+                stage_barrier<GATEUP ? 7 + 8 + 1 : 7 + 16>();
             } else {
+                if (!pend_put) {
+                    f.put_src((ci + 1) & 1, f.src_of(nxt, pend));
+                    pend_put = true;
+                }
                 ++kt;
+                // Issued after the stages read next (loaded at the start of
+                // the previous K-tile): this K-tile's 7 direct loads.
+                stage_barrier<7>();
             }
-            lds_barrier();
         });
     }
 }
