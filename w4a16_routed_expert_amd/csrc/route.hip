@@ -35,6 +35,8 @@ constexpr int kGrpWaves = kGrpThreads / 64;
 constexpr int kMaxH = 4096;
 constexpr int kSplit = 30;               // products with shift < kSplit go to the low integer limb
 
+constexpr int ilog2_ceil(int n) { return n <= 1 ? 0 : 1 + ilog2_ceil((n + 1) / 2); }
+
 // FP16 bits -> signed integer significand m and exponent field q, value = m * 2^(q-25).
 __device__ inline void dec16(uint32_t b, int &m, int &q)
 {
@@ -127,30 +129,41 @@ struct RouteArgs {
 // the products x[h] * wr[h][e], summed in two 64-bit accumulators (each holds
 // fewer than 2^12 terms below 2^51, so neither overflows), then reduced
 // across the block and rounded once.
-__device__ float exact_logit(const RouteArgs &a, int t, int e, long long (*red)[2])
+// x[t, :] is read from sx, the block's row of FP16 values held as doubles
+// (exact); the limb sums are integers, so their order does not matter.  The
+// result is valid in thread 0.
+__device__ float exact_logit(const RouteArgs &a, const double *sx, int e, long long (*red)[2])
 {
     const int tid = threadIdx.x;
     long long hi = 0, lo = 0;
     for (int h = tid; h < a.H; h += kSelThreads) {
         int mx, qx, mw, qw;
-        dec16(a.x[(size_t)t * a.H + h], mx, qx);
+        dec16(__builtin_bit_cast(uint16_t, (_Float16)sx[h]), mx, qx);
         dec16(a.wr[(size_t)h * a.E + e], mw, qw);
         const long long prod = (long long)(mx * mw);               // |prod| < 2^22
         const int sh = qx + qw - 2;                                // product = prod * 2^(sh-48), sh in [0, 58]
         if (sh < kSplit) lo += (long long)((unsigned long long)prod << sh);
         else hi += (long long)((unsigned long long)prod << (sh - kSplit));
     }
-    red[tid][0] = hi;
-    red[tid][1] = lo;
-    __syncthreads();
-    for (int s = kSelThreads / 2; s > 0; s >>= 1) {
-        if (tid < s) {
-            red[tid][0] += red[tid + s][0];
-            red[tid][1] += red[tid + s][1];
-        }
-        __syncthreads();
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        hi += __shfl_xor(hi, off);
+        lo += __shfl_xor(lo, off);
     }
-    const float r = rn32_limbs(red[0][0], red[0][1]);
+    if ((tid & 63) == 0) {
+        red[tid >> 6][0] = hi;
+        red[tid >> 6][1] = lo;
+    }
+    __syncthreads();
+    float r = 0.0f;
+    if (tid == 0) {
+        long long H2 = 0, L2 = 0;
+        for (int w = 0; w < kSelWaves; ++w) {
+            H2 += red[w][0];
+            L2 += red[w][1];
+        }
+        r = rn32_limbs(H2, L2);
+    }
     __syncthreads();                                               // red is reused by the next call
     return r;
 }
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
     __shared__ double s_x[kMaxH];
     __shared__ double s_acc[kSelWaves][64];
     __shared__ float s_bnd[kSelWaves][64];
-    __shared__ long long s_red[kSelThreads][2];
+    __shared__ long long s_red[kSelWaves][2];
     __shared__ float s_logit[64];
     __shared__ unsigned long long s_redo;
 
@@ -380,7 +393,7 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
     while (redo) {                                   // rare: exact recomputation by the whole block
         const int e = __builtin_ctzll(redo);
         redo &= redo - 1ull;
-        const float l = exact_logit(a, t, e, s_red);
+        const float l = exact_logit(a, s_x, e, s_red);
         if (tid == 0) s_logit[e] = l;
     }
     __syncthreads();
@@ -518,6 +531,9 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
     constexpr int RPW = 64 / EQ;
     constexpr int U = VEC >= 8 ? 8 : 32;     // rows in flight per thread (all of H = 2048 in one batch)
     typedef WLoad<VEC> L;
+    constexpr int kPath = kMaxH / (RPW * kSelWaves) + ilog2_ceil(RPW) + kSelWaves;
+    constexpr int kErrExp = ilog2_ceil(kPath) + 1 - 53;
+    static_assert(kErrExp <= -44, "summation paths of at most 256 additions");
     const int G = (a.E + kGroupE - 1) / kGroupE;
     const int t = blockIdx.x / G, g = blockIdx.x % G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -525,7 +541,7 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
     __shared__ double s_x[kMaxH];
     __shared__ double s_acc[kSelWaves][kGroupE];
     __shared__ float s_bnd[kSelWaves][kGroupE];
-    __shared__ long long s_red[kSelThreads][2];
+    __shared__ long long s_red[kSelWaves][2];
     __shared__ float s_logit[kGroupE];
     __shared__ unsigned long long s_redo;
 
@@ -543,14 +559,18 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
             wv[u] = L::ld(wcol + h * (unsigned int)E);
         }
     };
+    // the x row first (it is needed first), then the router rows
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 v[kMaxH / 4 / kSelThreads];
+    {
+        const u32x2 *src = reinterpret_cast<const u32x2 *>(a.x + (size_t)t * H);
+#pragma unroll
+        for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) v[r] = src[min(tid + r * kSelThreads, H / 4 - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);     // keep the x loads ahead of the router loads
     load_rows(h0);
 
     {   // x row -> fp64 in LDS
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 *src = reinterpret_cast<const u32x2 *>(a.x + (size_t)t * H);
-        u32x2 v[kMaxH / 4 / kSelThreads];
-#pragma unroll
-        for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) v[r] = src[min(tid + r * kSelThreads, H / 4 - 1)];
 #pragma unroll
         for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) {
             const int i = tid + r * kSelThreads;
@@ -605,9 +625,12 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
                 B += s_bnd[r][lane];
             }
         }
-        // any summation path above has at most H/(RPW*kSelWaves) + 6 + 8 fp64
-        // additions, far below 2^9
-        const double err = ldexp((double)B, -42);
+        // Any summation path above has at most n = H/(RPW*kSelWaves) +
+        // log2(RPW) + kSelWaves fp64 additions (kPath, H <= kMaxH), so
+        // |v - exact| <= n * 2^-53 * sum|x*w| * (1 + n 2^-53); B (FP32, at
+        // most n roundings) is within a factor 1 + 2^-16 of the true sum|x*w|.
+        // Hence err = 2^(ceil(log2 n) + 1 - 53) * B covers it.
+        const double err = ldexp((double)B, kErrExp);
         const bool certain = lane >= kGroupE || e >= E || (!a.force_exact && rn32_certain(v, err));
         if (lane < kGroupE) s_logit[lane] = (float)v;
         const unsigned long long m = __ballot(!certain);
@@ -618,7 +641,7 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
     while (redo) {                                   // rare: exact recomputation by the whole block
         const int j = __builtin_ctzll(redo);
         redo &= redo - 1ull;
-        const float l = exact_logit(a, t, g * kGroupE + j, s_red);
+        const float l = exact_logit(a, s_x, g * kGroupE + j, s_red);
         if (tid == 0) s_logit[j] = l;
     }
     __syncthreads();
