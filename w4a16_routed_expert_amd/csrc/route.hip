@@ -20,8 +20,9 @@
 //   of 16 experts), spreads the logits over many CUs; route_group_kernel (one
 //   block) then runs top-k + softmax per token (one wavefront per token, lane
 //   = expert) and the stable counting sort of the T*k pairs.
-//   Large batches (prefill): route_select_kernel, one block per token, does
-//   logits, top-k and softmax; route_group_kernel sorts.
+//   Large batches (prefill): route_select_kernel, one block per 4 tokens
+//   (every router row loaded serves the 4), does logits, top-k and softmax;
+//   route_group_kernel sorts.
 #include "moe_internal.h"
 
 #include <climits>
@@ -30,6 +31,7 @@ namespace {
 
 constexpr int kSelThreads = 512;         // 8 waves per token
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelTokens = 4;            // tokens per block of the prefill logits + selection
 constexpr int kGrpThreads = 1024;        // 16 waves for the grouping
 constexpr int kGrpWaves = kGrpThreads / 64;
 constexpr int kMaxH = 4096;
@@ -132,7 +134,8 @@ struct RouteArgs {
 // x[t, :] is read from sx, the block's row of FP16 values held as doubles
 // (exact); the limb sums are integers, so their order does not matter.  The
 // result is valid in thread 0.
-__device__ float exact_logit(const RouteArgs &a, const double *sx, int e, long long (*red)[2])
+template <typename XT>
+__device__ float exact_logit(const RouteArgs &a, const XT *sx, int e, long long (*red)[2])
 {
     const int tid = threadIdx.x;
     long long hi = 0, lo = 0;
@@ -288,49 +291,74 @@ struct WLoad<1> {
 // One block per token.  fp64 pass: lane = (64/VEC)*hp + eq handles experts
 // VEC*eq .. VEC*eq+VEC-1 (one vector load per row) and rows
 // h = PH*(kSelWaves*i + wave) + hp, PH = 64*VEC/64 row phases per wave.
-template <int VEC>
+// Prefill: TB tokens per block share every router row loaded (the router is
+// read once per TB tokens); x rows stay FP16 in LDS (small enough for two
+// blocks per CU).
+template <int VEC, int TB>
 __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
 {
     constexpr int EQ = 64 / VEC;             // lanes sharing one row
     constexpr int PH = VEC;                  // rows per wave step (64 / EQ)
-    constexpr int U = 8;                     // rows in flight per thread
+    constexpr int U = 4;                     // rows in flight per thread
+    constexpr int kPath = kMaxH / (PH * kSelWaves) + ilog2_ceil(PH) + kSelWaves;
+    constexpr int kErrExp = ilog2_ceil(kPath) + 1 - 53;
+    static_assert(TB <= kSelWaves, "one wavefront per token for the selection");
     typedef WLoad<VEC> L;
-    const int t = blockIdx.x;
+    const int t0 = blockIdx.x * TB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int E = a.E, H = a.H;
-    __shared__ double s_x[kMaxH];
-    __shared__ double s_acc[kSelWaves][64];
-    __shared__ float s_bnd[kSelWaves][64];
+    const int E = a.E, H = a.H, T = a.T;
+    __shared__ _Float16 s_x[TB][kMaxH];
+    __shared__ double s_acc[kSelWaves][TB][64];
+    __shared__ float s_wsq[kSelWaves][64];
+    __shared__ float s_xsq[TB];
     __shared__ long long s_red[kSelWaves][2];
-    __shared__ float s_logit[64];
-    __shared__ unsigned long long s_redo;
+    __shared__ float s_logit[TB][64];
+    __shared__ unsigned long long s_redo[TB];
 
-    {   // x row -> fp64 in LDS, 4 values per thread per step, all loads first
+    {   // x rows -> FP32 in LDS, 4 values per thread per step, all loads first
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 *src = reinterpret_cast<const u32x2 *>(a.x + (size_t)t * H);
-        u32x2 v[kMaxH / 4 / kSelThreads];
+        constexpr int R = TB * kMaxH / 4 / kSelThreads;
+        const int q4 = H / 4;
+        u32x2 v[R];
 #pragma unroll
-        for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) {
-            const int i = tid + r * kSelThreads;
-            v[r] = src[min(i, H / 4 - 1)];
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + r * kSelThreads;          // (token i / q4, quad i % q4)
+            const int tt = i / q4, qq = i - tt * q4;
+            const bool ok = tt < TB && t0 + tt < T;
+            v[r] = ok ? reinterpret_cast<const u32x2 *>(a.x + (size_t)(t0 + tt) * H)[qq] : u32x2{0u, 0u};
         }
 #pragma unroll
-        for (int r = 0; r < kMaxH / 4 / kSelThreads; ++r) {
+        for (int r = 0; r < R; ++r) {
             const int i = tid + r * kSelThreads;
-            if (i < H / 4) {
+            const int tt = i / q4, qq = i - tt * q4;
+            if (tt < TB) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s_x[4 * i + j] = h2d((uint16_t)(v[r][j >> 1] >> (16 * (j & 1))));
+                for (int j = 0; j < 4; ++j)
+                    s_x[tt][4 * qq + j] = __builtin_bit_cast(_Float16, (uint16_t)(v[r][j >> 1] >> (16 * (j & 1))));
             }
         }
     }
     __syncthreads();
-
+    if (wave < TB) {
+        // sum of x^2 of token `wave` (squares exact in FP32)
+        float q = 0.0f;
+        for (int h = lane; h < H; h += 64) {
+            const float xf = (float)s_x[wave][h];
+            q = fmaf(xf, xf, q);
+        }
+        q = sum_phases<1>(q);
+        if (lane == 0) s_xsq[wave] = q;
+    }
     const int eq = lane % EQ, hp = lane / EQ;
     const int e0 = VEC * eq;
-    double acc[VEC];
-    float bnd[VEC];
+    double acc[TB][VEC];
+    float wsq[VEC];                           // sum of w^2 per expert (the error bound)
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) { acc[j] = 0.0; bnd[j] = 0.0f; }
+    for (int j = 0; j < VEC; ++j) wsq[j] = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) acc[tt][j] = 0.0;
     if (e0 < E) {
         const uint16_t *wcol = a.wr + e0;
         const int step = PH * kSelWaves;
@@ -345,13 +373,17 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int h = h0 + u * step;
-                const double xv = h < H ? s_x[h] : 0.0;
-                const float xa = fabsf((float)xv);
+                float wf[VEC];
 #pragma unroll
                 for (int j = 0; j < VEC; ++j) {
-                    const float wf = (float)__builtin_bit_cast(_Float16, L::get(wv[u], j));
-                    acc[j] = fma(xv, (double)wf, acc[j]);              // exact product, fp64 sum
-                    bnd[j] = fmaf(xa, fabsf(wf), bnd[j]);              // sum |x*w| (for the error bound)
+                    wf[j] = h < H ? (float)__builtin_bit_cast(_Float16, L::get(wv[u], j)) : 0.0f;
+                    wsq[j] = fmaf(wf[j], wf[j], wsq[j]);
+                }
+#pragma unroll
+                for (int tt = 0; tt < TB; ++tt) {
+                    const double xv = (double)(float)s_x[tt][min(h, H - 1)];
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) acc[tt][j] = fma(xv, (double)wf[j], acc[tt][j]);   // exact product, fp64 sum
                 }
             }
         }
@@ -359,50 +391,59 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(RouteArgs a)
     // sum the PH row phases of each expert within the wave (lanes eq, eq+EQ, ...)
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-        acc[j] = sum_phases<EQ>(acc[j]);
-        bnd[j] = sum_phases<EQ>(bnd[j]);
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) acc[tt][j] = sum_phases<EQ>(acc[tt][j]);
+        wsq[j] = sum_phases<EQ>(wsq[j]);
     }
     if (hp == 0) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
-            s_acc[wave][e0 + j] = acc[j];
-            s_bnd[wave][e0 + j] = bnd[j];
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt) s_acc[wave][tt][e0 + j] = acc[tt][j];
+            s_wsq[wave][e0 + j] = wsq[j];
         }
     }
     __syncthreads();
-    if (wave == 0) {
+    if (wave < TB) {
+        const int tt = wave;
         double v = 0.0;
-        float B = 0.0f;
+        float W = 0.0f;
         for (int r = 0; r < kSelWaves; ++r) {
-            v += s_acc[r][lane];
-            B += s_bnd[r][lane];
+            v += s_acc[r][tt][lane];
+            W += s_wsq[r][lane];
         }
-        // Any summation path above has at most n = H/(PH*kSelWaves) + log2(PH)
-        // + kSelWaves <= 1024 + 3 + 8 fp64 additions, so |v - exact| <=
-        // n * 2^-53 * sum|x*w| (plus higher-order terms) <= 2^-42.9 * sum|x*w|;
-        // B (FP32, under 1050 additions) is within a factor 1.0001 of the true
-        // sum|x*w|, so err = 2^-42 * B covers it.
-        const double err = ldexp((double)B, -42);
-        const bool certain = lane >= E || (!a.force_exact && rn32_certain(v, err));
-        s_logit[lane] = (float)v;
+        // Any summation path above has at most n = H/(PH*kSelWaves) +
+        // log2(PH) + kSelWaves fp64 additions (kPath, H <= kMaxH), so
+        // |v - exact| <= n * 2^-53 * sum|x*w| * (1 + n 2^-53).  By
+        // Cauchy-Schwarz sum|x*w| <= sqrt(sum x^2 * sum w^2); both FP32 sums of
+        // exact squares (at most H roundings, H <= 4096) are within a factor
+        // 1 + 2^-11 of their true values, so B = sqrt(X W) (1 + 2^-10) bounds
+        // sum|x*w|, and err = 2^(ceil(log2 n) + 1 - 53) * B covers the error.
+        const double B = sqrt((double)s_xsq[tt] * (double)W) * (1.0 + 0x1p-10);
+        const double err = ldexp(B, kErrExp);
+        const bool certain = lane >= E || t0 + tt >= T || (!a.force_exact && rn32_certain(v, err));
+        s_logit[tt][lane] = (float)v;
         const unsigned long long m = __ballot(!certain);
-        if (lane == 0) s_redo = m;
+        if (lane == 0) s_redo[tt] = m;
     }
     __syncthreads();
-    unsigned long long redo = s_redo;
-    while (redo) {                                   // rare: exact recomputation by the whole block
-        const int e = __builtin_ctzll(redo);
-        redo &= redo - 1ull;
-        const float l = exact_logit(a, s_x, e, s_red);
-        if (tid == 0) s_logit[e] = l;
+    for (int tt = 0; tt < TB; ++tt) {
+        unsigned long long redo = s_redo[tt];
+        while (redo) {                               // rare: exact recomputation by the whole block
+            const int e = __builtin_ctzll(redo);
+            redo &= redo - 1ull;
+            const float l = exact_logit(a, &s_x[tt][0], e, s_red);
+            if (tid == 0) s_logit[tt][e] = l;
+        }
     }
     __syncthreads();
-    if (wave != 0) return;
+    if (wave >= TB || t0 + wave >= T) return;
 
     // logits (+ bias), then top-k and softmax, lane = expert
+    const int t = t0 + wave;
     float lv = 0.0f;
     if (lane < E) {
-        lv = s_logit[lane];
+        lv = s_logit[wave][lane];
         if (a.bias) lv = lv + a.bias[lane];
         if (a.logits) a.logits[(size_t)t * E + lane] = lv;
     }
@@ -706,8 +747,7 @@ int route_launch(const void *x_dev, const void *w_router_dev, const float *bias_
     a.force_exact = force_exact;
     a.lbuf = lbuf;
     hipStream_t s = (hipStream_t)stream;
-    // widest router-row load the layout allows: 8 or 4 experts per lane, else 1
-    const bool v8 = E % 8 == 0 && moe::aligned(w_router_dev, 16);
+    // widest router-row load the layout allows for the prefill kernel: 4 experts per lane, else 1
     const bool v4 = E % 4 == 0 && moe::aligned(w_router_dev, 8);
     if (small) {
         const unsigned int blocks = (unsigned int)T * (unsigned int)((E + kGroupE - 1) / kGroupE);
@@ -720,9 +760,10 @@ int route_launch(const void *x_dev, const void *w_router_dev, const float *bias_
         hipLaunchKernelGGL(route_group_kernel<true>, dim3(1), dim3(kGrpThreads), 0, s, a);
         return moe::check_launch("moe_route (top-k, group)");
     }
-    if (v8) hipLaunchKernelGGL(route_select_kernel<8>, dim3((unsigned int)T), dim3(kSelThreads), 0, s, a);
-    else if (v4) hipLaunchKernelGGL(route_select_kernel<4>, dim3((unsigned int)T), dim3(kSelThreads), 0, s, a);
-    else hipLaunchKernelGGL(route_select_kernel<1>, dim3((unsigned int)T), dim3(kSelThreads), 0, s, a);
+    const unsigned int sel_blocks = (unsigned int)((T + kSelTokens - 1) / kSelTokens);
+    // four experts per lane: with 4 tokens, 8 per lane would not fit the registers
+    if (v4) hipLaunchKernelGGL((route_select_kernel<4, kSelTokens>), dim3(sel_blocks), dim3(kSelThreads), 0, s, a);
+    else hipLaunchKernelGGL((route_select_kernel<1, kSelTokens>), dim3(sel_blocks), dim3(kSelThreads), 0, s, a);
     rc = moe::check_launch("moe_route (select)");
     if (rc) return rc;
     hipLaunchKernelGGL(route_group_kernel<false>, dim3(1), dim3(kGrpThreads), 0, s, a);
