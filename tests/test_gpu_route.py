@@ -99,3 +99,50 @@ def test_midpoint_and_cancellation_logits_are_exact():
     ids, w = oracle.topk_softmax(ref, 2)
     assert np.array_equal(fast["ids"], ids)
     assert np.allclose(fast["w"], w, rtol=1e-6, atol=0)
+
+
+def check_grouping(got, ids, E, what):
+    """Offsets, sorted pairs, pair positions and the active list against the
+    oracle's stable counting sort of the routed ids."""
+    ref = oracle.group(ids, E)
+    assert np.array_equal(got["offsets"], ref["offsets"]), f"{what}: offsets"
+    assert np.array_equal(got["sorted_pairs"], ref["sorted_pairs"]), f"{what}: sorted pairs"
+    assert np.array_equal(got["pair_pos"], ref["pair_pos"]), f"{what}: pair positions"
+    na = ref["n_active"]
+    assert int(got["n_active"][0]) == na and np.array_equal(got["active"][:na], ref["active"]), f"{what}: active list"
+    assert np.all(got["active"][na:] == -1), f"{what}: active list padding"
+
+
+# Batches above the 256-token switch take the multi-block path (4 tokens per
+# logits block, per-segment counts of 256 pairs, segment-wise scatter): a
+# partial last token block and a partial last segment (T*k not a multiple of
+# 256), several segments per expert, and experts absent from the batch.
+@pytest.mark.parametrize("name,T", [("tiny", 1001), ("olmoe", 300), ("qwen", 257)])
+def test_large_batch_route_and_grouping(name, T):
+    cfg = synth.CONFIGS[name]
+    x, wr = synth.make_x(cfg, T, step=11), synth.make_router(cfg)
+    fast = run_route(x, wr, cfg.k)
+    exact = run_route(x, wr, cfg.k, exact=True)
+    assert_same(fast, exact, f"{name} T={T}")
+    ref = oracle.router_logits(x, wr)
+    assert np.array_equal(fast["logits"].view(np.uint32), ref.view(np.uint32))
+    ids, w = oracle.topk_softmax(ref, cfg.k)
+    assert np.array_equal(fast["ids"], ids)
+    assert np.allclose(fast["w"], w, rtol=1e-5, atol=1e-7)
+    check_grouping(fast, ids, cfg.E, f"{name} T={T}")
+
+
+def test_large_batch_skewed_grouping():
+    # every token prefers experts 5 and 2 (bias): 600 pairs each spread over
+    # five segments, the other experts absent
+    cfg = synth.CONFIGS["tiny"]
+    T = 600
+    x, wr = synth.make_x(cfg, T, step=12), synth.make_router(cfg)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[5], bias[2] = 50.0, 40.0
+    got = run_route(x, wr, cfg.k, bias=bias)
+    ref = oracle.router_logits(x, wr, bias)
+    ids, _ = oracle.topk_softmax(ref, cfg.k)
+    assert np.array_equal(got["ids"], ids)
+    assert set(np.unique(ids)) == {2, 5}
+    check_grouping(got, ids, cfg.E, "skewed T=600")

@@ -22,7 +22,7 @@
 //   = expert) and the stable counting sort of the T*k pairs.
 //   Large batches (prefill): route_select_kernel, one block per 4 tokens
 //   (every router row loaded serves the 4), does logits, top-k and softmax;
-//   route_group_kernel sorts.
+//   route_count_kernel and route_scatter_kernel sort on many blocks.
 #include "moe_internal.h"
 
 #include <climits>
@@ -705,6 +705,99 @@ __global__ __launch_bounds__(kGrpThreads) void route_group_kernel(RouteArgs a)
     group_phase<kGrpWaves, TOPK>(a, s_grp);
 }
 
+// Large batches: the stable counting sort runs on many blocks (one single
+// block would send every scattered store through one CU).  Segment g holds
+// pairs [g kSeg, (g + 1) kSeg); route_count_kernel writes its per-expert
+// counts to the workspace; route_scatter_kernel then gives each segment its
+// starting position per expert (all earlier segments' counts plus the
+// expert's offset) and places the segment's pairs in order.
+constexpr int kSeg = 256;
+
+__global__ __launch_bounds__(kSeg) void route_count_kernel(RouteArgs a)
+{
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    const int g = blockIdx.x, n = a.T * a.k, E = a.E;
+    if (threadIdx.x < MOE_MAX_EXPERTS) cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const int p = g * kSeg + (int)threadIdx.x;
+    if (p < n) {
+        const int e = a.ids[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < E) reinterpret_cast<int *>(a.lbuf)[(size_t)g * E + threadIdx.x] = cnt[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kSeg) void route_scatter_kernel(RouteArgs a, int G)
+{
+    constexpr int NWV = kSeg / 64;
+    __shared__ int s_tot[NWV][64], s_pre[NWV][64];
+    __shared__ int s_base[64];
+    const int g = blockIdx.x, n = a.T * a.k, E = a.E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int *cnt = reinterpret_cast<const int *>(a.lbuf);
+    // expert `lane`: total count and the count of segments before this one
+    // (wavefront w sums the segments g' = w mod NWV)
+    int tot = 0, pre = 0;
+    if (lane < E) {
+#pragma unroll 8
+        for (int q = wave; q < G; q += NWV) {
+            const int c = cnt[(size_t)q * E + lane];
+            tot += c;
+            if (q < g) pre += c;
+        }
+    }
+    s_tot[wave][lane] = tot;
+    s_pre[wave][lane] = pre;
+    __syncthreads();
+    if (wave != 0) return;
+    int c = 0, pr = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+        c += s_tot[w][lane];
+        pr += s_pre[w][lane];
+    }
+    const int incl = moe::wave_inclusive_sum(c);
+    const int excl = incl - c;
+    s_base[lane] = excl + pr;
+    if (g == 0) {
+        const unsigned long long act = __ballot(lane < E && c > 0);
+        const int na = __popcll(act);
+        const unsigned long long below = (1ull << lane) - 1ull;
+        if (lane < E) {
+            a.offsets[lane] = excl;
+            if (c > 0) a.active[__popcll(act & below)] = lane;
+            if (lane >= na) a.active[lane] = -1;
+            if (lane == E - 1) a.offsets[E] = incl;
+        }
+        if (lane == 0) a.n_active[0] = na;
+    }
+    // the segment's pairs 64 at a time, in order; a pair's rank among equal
+    // experts of its chunk comes from a ballot
+    const int b0 = g * kSeg, b1 = min(n, b0 + kSeg);
+    int ids[kSeg / 64];
+#pragma unroll
+    for (int i = 0; i < kSeg / 64; ++i) {
+        const int p = b0 + 64 * i + lane;
+        ids[i] = p < b1 ? a.ids[p] : -1;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < kSeg / 64; ++i) {
+        const int p = b0 + 64 * i + lane;
+        int e = ids[i];
+        if (e >= E) e = -1;
+        const unsigned long long peers = same_expert_lanes(e);
+        if (e >= 0) {
+            const int rank = __popcll(peers & below);
+            const int pos = s_base[e] + rank;
+            a.sorted_pairs[pos] = p;
+            a.pair_pos[p] = pos;
+            if (rank == 0) s_base[e] = pos + __popcll(peers);   // one leader per expert and chunk
+        }
+    }
+}
+
 constexpr int kSmallBatch = 256;           // largest T routed with the split logits kernel
 
 // Workspace: the logits [T][E] handed from the logit blocks to the grouping block.
@@ -766,8 +859,13 @@ int route_launch(const void *x_dev, const void *w_router_dev, const float *bias_
     else hipLaunchKernelGGL((route_select_kernel<1, kSelTokens>), dim3(sel_blocks), dim3(kSelThreads), 0, s, a);
     rc = moe::check_launch("moe_route (select)");
     if (rc) return rc;
-    hipLaunchKernelGGL(route_group_kernel<false>, dim3(1), dim3(kGrpThreads), 0, s, a);
-    return moe::check_launch("moe_route (group)");
+    // segment counts fit the logits workspace: G <= T (kSeg >= k)
+    const int G = (T * k + kSeg - 1) / kSeg;
+    hipLaunchKernelGGL(route_count_kernel, dim3((unsigned int)G), dim3(kSeg), 0, s, a);
+    rc = moe::check_launch("moe_route (count)");
+    if (rc) return rc;
+    hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned int)G), dim3(kSeg), 0, s, a, G);
+    return moe::check_launch("moe_route (scatter)");
 }
 
 }  // namespace
