@@ -408,17 +408,19 @@ int launch_one(const FfnArgs &a, hipStream_t s, long long max_items, const char 
     return moe::check_launch(who);
 }
 
-// Split of the reduction axis: the smallest S that gives about 16 resident
-// wavefronts per CU of work, from the expected number of routed experts of a
-// uniform router (a launch-shape choice only: any S gives the same sums in
-// the same order per slice).
+// Split of the reduction axis: the smallest S that gives about 8 wavefronts
+// per CU of work (one block of 8 per CU is what the kernel's LDS and
+// registers leave resident; measured, more splitting costs more in staging
+// and partial sums than it gains), from the expected number of routed
+// experts of a uniform router (a launch-shape choice only: any S gives the
+// same sums in the same order per slice).
 int choose_split(int NT, int RG, int T, int k, int E)
 {
     const double P = (double)T * k;
     double miss = 1.0;
     for (int i = 0; i < T && miss > 1e-9; ++i) miss *= 1.0 - (double)k / E;
     const double slots = E * (1.0 - miss) + P / 16.0;
-    const double waves = 16.0 * cu_count();
+    const double waves = 8.0 * cu_count();
     int S = 1;
     while (S < 8 && slots * RG * S < waves) {
         const int n = S * 2;
