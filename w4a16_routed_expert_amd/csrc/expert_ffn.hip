@@ -96,9 +96,15 @@ struct Unit {
 
 template <bool GATEUP, int NT, int S>
 struct Ffn {
-    static constexpr int NMAT = GATEUP ? 2 : 1;
+    // Weight streams per wavefront: gate/up the gate and up rows of one row
+    // group; down two adjacent row groups (each activation fragment then
+    // feeds two MFMAs, and a unit streams twice the bytes per overhead) when
+    // the reduction axis has an even number of tiles, else one (measured:
+    // with an odd count the two-stream ring cannot be deep enough).
+    static constexpr int NMAT = (GATEUP || NT % 2 == 0) ? 2 : 1;
+    static constexpr int RPW = GATEUP ? 1 : NMAT;  // output row groups per wavefront
     static constexpr int NTW = NT / S;          // tiles of one wavefront
-    static constexpr int RGB = kWaves / S;      // row groups per item
+    static constexpr int RGB = kWaves / S;      // wavefront row slots per item
     static constexpr int NB = (NT + 1) / 2;     // scale blocks of the reduction axis
     static constexpr int D = ring_depth(NTW, NMAT);
     static_assert(NT >= 1 && NT <= kMaxNT, "reduction axis of 128 .. 2048 columns");
@@ -124,7 +130,7 @@ struct Ffn {
         rgl = wave / S;
         t0 = ks * NTW;
         RG = (GATEUP ? a.I : a.H) / 16;
-        CH = (RG + RGB - 1) / RGB;
+        CH = (RG + RGB * RPW - 1) / (RGB * RPW);
     }
 
     // Unit of this wavefront in item `it` (slot search starts at `hint`).
@@ -142,7 +148,7 @@ struct Ffn {
         const int sl = uni(L.tb.sl[s]);
         u.p0 = uni(L.tb.p0[s]) + 16 * u.mt;
         u.nval = min(16, n - 16 * u.mt);
-        u.rg = c * RGB + rgl;
+        u.rg = (c * RGB + rgl) * RPW;
         u.absent = sl < 0;
         u.write = u.rg < RG;
         const bool reads = u.write && !u.absent;
@@ -167,19 +173,22 @@ struct Ffn {
         return u;
     }
 
-    // Tile j of a unit (row base, readable bytes, row group) of matrix mat.
+    // Tile j of a unit (row base, readable bytes, row group) of stream mat:
+    // gate/up matrix mat of row group rg, down row group rg + mat.
     __device__ u32x4 load_q(const uint8_t *row, int nrec, int rg, int mat, int j) const
     {
         const int qm = GATEUP ? a.off_q[mat] : a.off_q[2];
-        return __builtin_amdgcn_raw_buffer_load_b128(rsrc(row, nrec), lane * 16, qm + ((rg * NT) + t0 + j) * 1024, 0);
+        const int r = GATEUP ? rg : rg + mat;
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc(row, nrec), lane * 16, qm + ((r * NT) + t0 + j) * 1024, 0);
     }
 
     // FP16 scale of the block of tile j, row n16 of the row group.
     __device__ _Float16 load_s(const uint8_t *row, int nrec, int rg, int mat, int j) const
     {
         const int sm = GATEUP ? a.off_s[mat] : a.off_s[2];
+        const int r = GATEUP ? rg : rg + mat;
         const uint16_t b = __builtin_amdgcn_raw_buffer_load_b16(rsrc(row, nrec), n16 * 2,
-                                                                 sm + (rg * NB + (t0 + j) / 2) * 32, 0);
+                                                                 sm + (r * NB + (t0 + j) / 2) * 32, 0);
         return __builtin_bit_cast(_Float16, b);
     }
 
@@ -318,6 +327,7 @@ struct Ffn {
         if (!cur.write) return;
         if (cur.absent && lane == 0 && a.status) *a.status = MOE_ERR_ABSENT_EXPERT;
         // lane (g4, n16) holds tokens 4*g4 + r of row n16 of the row group
+        // (down: of row groups rg and rg + 1, both present: H % 128 == 0)
         const int col = cur.rg * 16 + n16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -328,7 +338,9 @@ struct Ffn {
                     const float g = acc[0][r] * kUnit, u = acc[NMAT - 1][r] * kUnit;
                     a.h[pr * a.I + col] = cur.absent ? (uint16_t)0 : float_to_half_bits(g / (1.0f + expf(-g)) * u);
                 } else {
-                    a.out[pr * a.H + col] = cur.absent ? 0.0f : acc[0][r] * kUnit;
+#pragma unroll
+                    for (int mat = 0; mat < NMAT; ++mat)
+                        a.out[pr * a.H + col + 16 * mat] = cur.absent ? 0.0f : acc[mat][r] * kUnit;
                 }
             }
         }
@@ -466,7 +478,10 @@ int launch_ffn(const FfnArgs &a, hipStream_t s, const char *who)
     if (use_gemm(a)) return GATEUP ? launch_gemm_gateup(a, s) : launch_gemm_down(a, s);
     const int K = GATEUP ? a.H : a.I;
     const int R = GATEUP ? a.I : a.H;
-    const int NT = K / 128, RG = R / 16;
+    // row slots of wavefronts: gate/up one row group each, down two when the
+    // reduction axis has an even number of tiles
+    const int NT = K / 128;
+    const int RG = R / 16 / ((GATEUP || NT % 2) ? 1 : 2);
     const long long pairs = (long long)a.T * a.k;
     const long long max_slots = pairs < a.E ? pairs : a.E;
     const long long max_items = (max_slots + pairs / 16) * ((RG + kWaves - 1) / kWaves);
