@@ -355,11 +355,14 @@ __global__ __launch_bounds__(kThreads) void w4a16_ffn_kernel(FfnArgs a, const in
 {
     using F = Ffn<GATEUP, NT, S>;
     __shared__ typename F::Lds L;
+    // the slot table's inputs first: their loads do not wait for n_active
+    TableIn tin{};
+    if (threadIdx.x < 64) tin = table_loads(a, active, offsets, slot_map);
     int nact = *n_active;
     if (nact > a.E) nact = a.E;
     if (nact <= 0) return;
     const F f(a, L, nact);
-    if (threadIdx.x < 64) build_table(L.tb, a, active, offsets, slot_map, nact, 16, f.CH);
+    if (threadIdx.x < 64) build_table(L.tb, a, tin, nact, 16, f.CH);
     __syncthreads();
     const long long N = L.tb.first[nact];
     const int it0 = (int)(N * blockIdx.x / gridDim.x), it1 = (int)(N * (blockIdx.x + 1) / gridDim.x);

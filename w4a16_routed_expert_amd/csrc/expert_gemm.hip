@@ -275,11 +275,14 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
 {
     using G = Gemm<GATEUP>;
     __shared__ GLds L;
+    // the slot table's inputs first: their loads do not wait for n_active
+    TableIn tin{};
+    if (threadIdx.x < 64) tin = table_loads(a, active, offsets, slot_map);
     int nact = *n_active;
     if (nact > a.E) nact = a.E;
     if (nact <= 0) return;
     const G f(a, L, nact);
-    if (threadIdx.x < 64) build_table(L.tb, a, active, offsets, slot_map, nact, kBM, f.NBLK);
+    if (threadIdx.x < 64) build_table(L.tb, a, tin, nact, kBM, f.NBLK);
     // Stages start as zeros: rows that no load fills then hold finite values.
     for (int i = threadIdx.x; i < kStages * kStageBytes / 16; i += kGThreads)
         reinterpret_cast<u32x4 *>(&L.xa[0][0])[i] = u32x4{0u, 0u, 0u, 0u};

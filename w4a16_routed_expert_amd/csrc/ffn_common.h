@@ -104,31 +104,51 @@ struct SlotTable {
     int first[MOE_MAX_EXPERTS + 1];
 };
 
-// Built by wave 0, one lane per slot; a slot of n pairs has
+// What the slot table needs, loaded by wave 0 in one round trip: lane l
+// holds active[l] and, by expert index l, offsets[l], offsets[l + 1] and the
+// device slot of expert l (so no load waits for another).
+struct TableIn {
+    int e, o0, o1, sl;
+};
+
+__device__ inline TableIn table_loads(const FfnArgs &a, const int32_t *__restrict__ active,
+                                      const int32_t *__restrict__ offsets, const int32_t *__restrict__ slot_map)
+{
+    const int lane = threadIdx.x;          // wave 0 only
+    TableIn t;
+    const bool in = lane < a.E;
+    t.e = in ? active[lane] : -1;
+    t.o0 = in ? offsets[lane] : 0;
+    t.o1 = in ? offsets[lane + 1] : 0;
+    t.sl = in ? (slot_map ? slot_map[lane] : lane) : -1;
+    return t;
+}
+
+// Built by wave 0, one lane per slot (lane s takes expert active[s] and its
+// per-expert values from lane active[s]); a slot of n pairs has
 // ceil(n / tile) * items_per_tile work items.  Routing metadata outside its
 // valid range (a workspace that was not zero-filled, say) marks the status
 // word and the slot gets no work.
-__device__ inline void build_table(SlotTable &tb, const FfnArgs &a, const int32_t *__restrict__ active,
-                                   const int32_t *__restrict__ offsets, const int32_t *__restrict__ slot_map,
-                                   int nact, int tile, int items_per_tile)
+__device__ inline void build_table(SlotTable &tb, const FfnArgs &a, const TableIn &in, int nact, int tile,
+                                   int items_per_tile)
 {
     const int lane = threadIdx.x;          // wave 0 only
-    int e = -1, p0 = 0, n = 0, sl = -1;
-    if (lane < nact) {
-        e = active[lane];
-        if (e >= 0 && e < a.E) {
-            const int q0 = offsets[e], q1 = offsets[e + 1];
-            if (q0 >= 0 && q1 >= q0 && (long long)q1 <= (long long)a.T * a.k) {
-                p0 = q0;
-                n = q1 - q0;
-                sl = slot_map ? slot_map[e] : e;
-            } else {
-                if (a.status) *a.status = MOE_ERR_INVALID_ARG;
-                e = -1;
-            }
+    int e = lane < nact ? in.e : -1;
+    const bool eok = e >= 0 && e < a.E;
+    const int src = eok ? e : 0;
+    const int q0 = __shfl(in.o0, src), q1 = __shfl(in.o1, src), sle = __shfl(in.sl, src);
+    int p0 = 0, n = 0, sl = -1;
+    if (eok) {
+        if (q0 >= 0 && q1 >= q0 && (long long)q1 <= (long long)a.T * a.k) {
+            p0 = q0;
+            n = q1 - q0;
+            sl = sle;
         } else {
+            if (a.status) *a.status = MOE_ERR_INVALID_ARG;
             e = -1;
         }
+    } else {
+        e = -1;
     }
     const int cnt = (e >= 0) ? ((n + tile - 1) / tile) * items_per_tile : 0;
     const int incl = moe::wave_inclusive_sum(cnt);
