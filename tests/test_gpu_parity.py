@@ -84,6 +84,24 @@ def test_absent_expert_sets_status_and_zero_output():
     assert np.all(got["pair_out"][lo:hi] == 0) and np.all(got["h"][lo:hi] == 0)
 
 
+# H, I: reduction axes with an odd tile count (a short last scale block), one
+# tile (I = 128: the down projection reads a single 128-column tile), and
+# output row counts that are not a multiple of the 8 row groups of an item.
+@pytest.mark.parametrize("H,I", [(384, 384), (128, 128), (640, 128), (256, 640)])
+def test_streaming_odd_shapes(H, I):
+    from w4a16_routed_expert_amd import binding as B
+    cfg = synth.LayerConfig(f"odd{H}x{I}", 9, E=4, k=2, H=H, I=I, batches=(40,), resident=4)
+    T = 40
+    rows, wr, x = synth.make_expert_rows(cfg), synth.make_router(cfg), synth.make_x(cfg, T)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
+    B.moe_set_ffn_path(B.MOE_FFN_PATH_STREAM)
+    try:
+        got = gpu_layer(cfg, rows, wr, x)
+    finally:
+        B.moe_set_ffn_path(B.MOE_FFN_PATH_AUTO)
+    check_full(cfg, got, ref, f"streaming H={H} I={I}", rows=rows)
+
+
 def test_run_to_run_bit_identical():
     cfg = synth.CONFIGS["tiny"]
     T = 33
