@@ -328,10 +328,14 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
     // stage, lane l taking bytes 16 l .. 16 l + 15 of each.
     auto dma = [&](const GItem &it, int par, int kt, int st) {
         const __amdgpu_buffer_rsrc_t r = f.src_rsrc(it, kt);
+        // the four row offsets first, so their LDS reads overlap
+        uint32_t so[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) so[j] = L.src[par][4 * (f.wave + 8 * j) + (f.lane & 3)];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int g = f.wave + 8 * j;
-            const uint32_t off = L.src[par][4 * g + (f.lane & 3)] + kt * 256 + 16 * ((f.lane >> 2) ^ (g & 3));
+            const uint32_t off = so[j] + kt * 256 + 16 * ((f.lane >> 2) ^ (g & 3));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&L.xa[st][1024 * g], 16,
                                                      off, 0, 0, 0);
         }
@@ -364,35 +368,39 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
             const bool anx = kt + 2 >= NTP;
             const int akt = anx ? kt + 2 - NTP : kt + 2;
             const GItem &ait = anx ? nxt : cur;
+            // 32 steps (K-step s of 16 columns, m-tile mt), one MFMA each;
+            // the operand reads from LDS run kPD steps ahead of their use.
+            // K-step s uses word s % 4 of chunk s / 4: lanes h2 = 0 take
+            // piece 8 (s / 4) + s % 4, lanes h2 = 1 the piece 4 further on.
+            const uint8_t *xs = &L.xa[gg % kStages][0];
+            // stage_addr(32 mt + j32, 8 (s / 4) + 4 h2 + s % 4) = aq[s % 4] + 8192 mt + 512 (s / 4)
+            auto rd = [&](int st) {
+                const int s = st >> 2, mt = st & 3;
+                return *reinterpret_cast<const half8 *>(xs + f.aq[s & 3] + 8192 * mt + 512 * (s >> 2));
+            };
+            const uint8_t *wsrc = &L.wt[gg % kStages][f.wave][f.wrd];
+            // The first operand reads go out before the staging loads of the
+            // K-tile two ahead (a different stage), so their latency overlaps
+            // the address arithmetic of those loads.
+            half8 xr[kPD + 1];
+#pragma unroll
+            for (int st = 0; st < kPD; ++st) xr[st] = rd(st);
+            u32x4 wq[2];
+            wq[0] = *reinterpret_cast<const u32x4 *>(wsrc);
+            __builtin_amdgcn_sched_barrier(0);
             dma(ait, (ci + anx) & 1, akt, (gg + 2) % kStages);
-            // the direct-to-LDS loads stay first in the K-tile (the count at
-            // its end relies on it)
+            // the direct-to-LDS loads are the K-tile's only vector-memory
+            // operations before its end (the count there relies on it)
             __builtin_amdgcn_sched_barrier(0);
             {
-                // 32 steps (K-step s of 16 columns, m-tile mt), one MFMA each;
-                // the operand reads from LDS run kPD steps ahead of their use.
-                // K-step s uses word s % 4 of chunk s / 4: lanes h2 = 0 take
-                // piece 8 (s / 4) + s % 4, lanes h2 = 1 the piece 4 further on.
                 // Interleaved with the MFMAs: the reloads of the weight chunks
-                // as soon as they are converted, and the staging writes.
-                const uint8_t *xs = &L.xa[gg % kStages][0];
-                // stage_addr(32 mt + j32, 8 (s / 4) + 4 h2 + s % 4) = aq[s % 4] + 8192 mt + 512 (s / 4)
-                auto rd = [&](int st) {
-                    const int s = st >> 2, mt = st & 3;
-                    return *reinterpret_cast<const half8 *>(xs + f.aq[s & 3] + 8192 * mt + 512 * (s >> 2));
-                };
-                half8 xr[kPD + 1];
-#pragma unroll
-                for (int st = 0; st < kPD; ++st) xr[st] = rd(st);
+                // as soon as they are converted.
                 half8 bq;
                 // a padding K-tile's operand is exactly zero (its stage may hold stale codes)
                 const bool real = kt < f.NT;
                 const _Float16 zs = real ? (_Float16)(-8.0f / 1048576.0f) : (_Float16)0.0f;
                 const half8 zp = {zs, zs, zs, zs, zs, zs, zs, zs};
                 const uint32_t wmask = real ? 0xFFFFFFFFu : 0u;
-                const uint8_t *wsrc = &L.wt[gg % kStages][f.wave][f.wrd];
-                u32x4 wq[2];
-                wq[0] = *reinterpret_cast<const u32x4 *>(wsrc);
                 static_for<0, 32>([&](auto c) {
                     constexpr int st = decltype(c)::value;
                     constexpr int s = st >> 2, mt = st & 3;
