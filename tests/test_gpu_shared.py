@@ -46,17 +46,38 @@ def check_shared(x, shared, what):
     assert np.allclose(sig_gpu, sig_ref, rtol=0, atol=1e-6), f"{what}: shared gate"
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 20, 33])
+@pytest.mark.parametrize("T", [1, 5, 16, 20, 33, 70])
 def test_small_shared_expert(T):
-    # H = 256 gives each of the 8 reduction slices of a row group 0 or 1 tile
+    # H = 256: a unit has 2 tiles, so 6 of the 8 wavefronts of a block load
+    # nothing; T = 20 and 33 take 16-row units, T = 70 two token passes of 64
     x = (np.random.default_rng(T).standard_normal((T, 256))).astype(np.float16)
     check_shared(x, small_shared(256, 512, 7), f"small shared T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 16, 64])
+@pytest.mark.parametrize("H,Is,T", [(640, 1408, 20), (384, 2048, 3), (1024, 2816, 40), (8192, 1024, 2),
+                                    (1024, 8192, 1)])
+def test_odd_shared_shapes(H, Is, T):
+    # reduction axes of 3 to 64 tiles: 8-row units with one or two tiles per
+    # wavefront, 16-row units with chunk counts above one (uneven chunks,
+    # one or two token tiles, two tiles per wavefront)
+    x = (np.random.default_rng(H + T).standard_normal((T, H))).astype(np.float16)
+    check_shared(x, small_shared(H, Is, 11), f"shared H={H} Is={Is} T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 16, 64, 100])
 def test_qwen_shared_expert(T):
     cfg = synth.CONFIGS["qwen"]
     check_shared(synth.make_x(cfg, T, step=2), synth.make_shared(cfg), f"qwen shared T={T}")
+
+
+def test_shared_run_to_run_bit_identical():
+    # chunk partial sums meet in a fixed order
+    cfg = synth.CONFIGS["qwen"]
+    x, shared = synth.make_x(cfg, 16, step=6), synth.make_shared(cfg)
+    a_out, a_sig = run_shared(x, shared)
+    b_out, b_sig = run_shared(x, shared)
+    assert np.array_equal(a_out.view(np.uint32), b_out.view(np.uint32))
+    assert np.array_equal(a_sig.view(np.uint32), b_sig.view(np.uint32))
 
 
 def test_qwen_layer_with_shared_expert():

@@ -8,31 +8,47 @@
 // SwiGLU activation rounded to FP16 before the down projection, FP32 outputs.
 //
 // Kernel design (gfx950, wave64).  Decode batches make this a skinny GEMM,
-// bound by HBM (69 MB of FP16 weights for the Qwen shape):
-//   * The weights are plain row-major [R][K] FP16.  A work unit is 16 output
-//     rows x a 1/S slice of the reduction axis x MT token tiles of 16 tokens
-//     (up to 64 tokens share each weight load); the S waves of a row group
-//     reduce their FP32 partials in LDS in a fixed order.  A block holds 8/S
-//     row groups of one pass over MT token tiles.
-//   * Per 128-column tile a lane loads four 16-byte pieces of its row (columns
-//     32s + 8g .. +7, s = 0..3): each is one MFMA B operand as stored, and the
-//     A operand is the same columns of a token's activation row, read straight
-//     from memory (L2-resident; no permutation is needed for FP16 weights).
-//   * A ring of D tiles per wave stays in flight; tiles past the slice and
-//     rows past the matrix use zero-byte buffer resources or out-of-range
-//     offsets, so their loads return zeros without memory traffic.
+// bound by HBM (69 MB of FP16 weights for the Qwen shape), and a CU only
+// streams at its share of HBM bandwidth when it holds an equal share of the
+// bytes, so the work is cut into many equal units:
+//   * The weights are plain row-major [R][K] FP16.  A unit is 16 output rows
+//     (gate/up: the same 16 rows of both matrices) x one chunk of the
+//     reduction axis x one pass of up to 16 MT tokens.  The chunk count NKC
+//     is planned on the host so that the units spread evenly over 256 blocks
+//     and the 8 wavefronts of a block share a chunk's 128-column tiles
+//     (wave w takes tiles w, w + 8 of the chunk, NTW <= 2 per wave).
+//   * Per tile a lane loads four 16-byte pieces of its row (columns 32s +
+//     8g .. +7): each is one MFMA B operand as stored, and the A operand is
+//     the same columns of a token's activation row, read straight from
+//     memory (L2-resident).  Every wave keeps its NTW tiles of the next unit
+//     in flight while it computes the current one.
+//   * The 8 partial sums of a unit meet in LDS and are added in wave order;
+//     the unit's FP32 result goes to partial sums [NKC][T][NMAT R], which a
+//     second kernel adds in chunk order (gate/up: then the SwiGLU into hs,
+//     and the sigmoid gate; down: into shared_out, or written there directly
+//     when NKC = 1).  Summation order is fixed, so results are run-to-run
+//     identical.
+//   * Tiles past a chunk, tokens past the batch and units past the last use
+//     zero-byte buffer resources or out-of-range offsets, so their loads
+//     return zeros without memory traffic.
 #include "moe_internal.h"
+
+namespace ffn {
+int cu_count();   // compute units of the current device (expert_ffn.hip)
+}
 
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kOob = 0x7FFFFFF0;          // lane offset past any buffer: the load returns zeros
+constexpr int kPlanBlocks = 256;          // blocks the chunking is planned for (one per CU)
 
 struct SArgs {
     const uint16_t *x;      // [T][H]
@@ -41,7 +57,8 @@ struct SArgs {
     const uint16_t *wd;     // [H][Is]
     const uint16_t *wgate;  // [H]
     int T, H, Is;
-    uint16_t *hs;           // [T][Is] FP16 activations between the two kernels
+    uint16_t *hs;           // [T][Is] FP16 activations between the projections
+    float *part;            // partial sums [NKC][T][NMAT R]
     float *out;             // [T][H]
     float *sigma;           // [T]
 };
@@ -73,45 +90,62 @@ __device__ inline void lds_barrier()
 
 __device__ inline uint16_t float_to_half_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
-// Block = 8/S row groups of one token tile; wave = (row group, slice of the
-// reduction axis).  GATEUP: the gate and up projections of x and the SwiGLU
-// epilogue into hs; else the down projection of hs into out.  Blocks past the
-// last item compute sigma (GATEUP only).
-template <bool GATEUP, int S, int D, int MT>
-__global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items)
+// Sigmoid gate sigma[t] = sigmoid(wgate . x_t) of tokens t = first, first +
+// stride, ...: one wave per token, FP32 sums; lane l takes columns 512 i +
+// 8 l .. +7, four such steps loaded together (columns past H read as zeros).
+__device__ void sigmoid_gate(const SArgs &a, int first, int stride)
+{
+    const int lane = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t rg = rsrc(a.wgate, a.H * 2);
+    for (int t = first; t < a.T; t += stride) {
+        const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + (size_t)t * a.H, a.H * 2);
+        float z = 0.0f;
+        for (int c0 = 0; c0 < a.H; c0 += 4 * 512) {
+            u32x4 wv[4], xv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wv[i] = bload(rg, lane * 16, (c0 + 512 * i) * 2);
+                xv[i] = bload(rx, lane * 16, (c0 + 512 * i) * 2);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const half8 w8 = __builtin_bit_cast(half8, wv[i]), x8 = __builtin_bit_cast(half8, xv[i]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) z += (float)w8[j] * (float)x8[j];
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+        if (lane == 0) a.sigma[t] = 1.0f / (1.0f + expf(-z));
+    }
+}
+
+// One projection's streaming pass.  GATEUP: g and u of x (K = H, R = Is);
+// else the down projection of hs (K = Is, R = H).  Unit u = (pass p, group
+// rg of RU rows, chunk kc), kc fastest; blocks b < n_main take units b,
+// b + n_main, ...; with RU = 8 the lanes of rows 8..15 of the MFMA tile load
+// nothing.  With nkc = 1 the result is final: gate/up applies the SwiGLU and
+// writes hs, down writes dst = shared_out.  Otherwise dst receives partial
+// sums [nkc][T][NMAT R].  GATEUP blocks from n_main on compute the sigmoid gate.
+template <bool GATEUP, int MT, int NTW, int RU>
+__global__ __launch_bounds__(kThreads) void fp16_stream_kernel(SArgs a, int nkc, int n_main, float *dst)
 {
     constexpr int NMAT = GATEUP ? 2 : 1;
-    constexpr int RGB = kWaves / S;
-    constexpr int NACC = NMAT * MT;
-    __shared__ float red[S > 1 ? S - 1 : 1][S > 1 ? RGB : 1][S > 1 ? NACC : 1][S > 1 ? 4 : 1][S > 1 ? 64 : 1];
+    constexpr int NE = NMAT * MT;                    // accumulator tiles of a wave
+    static_assert(RU == 8 || RU == 16, "row groups of 8 or 16 rows");
+    __shared__ f32x4 red[kWaves][NE][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int g4 = lane >> 4, n16 = lane & 15;
-    const int K = GATEUP ? a.H : a.Is, R = GATEUP ? a.Is : a.H;
-    const int RG = R / 16, NT = K / 128;
-    const int CH = (RG + RGB - 1) / RGB;
-
-    if (GATEUP && (int)blockIdx.x >= n_items) {
-        // sigma[t] = sigmoid(wgate . x_t): one wave per token, FP32 sums
-        for (int t = (blockIdx.x - n_items) * kWaves + wave; t < a.T; t += (gridDim.x - n_items) * kWaves) {
-            float z = 0.0f;
-            for (int c = lane; c < a.H; c += 64)
-                z += (float)__builtin_bit_cast(_Float16, a.wgate[c]) *
-                     (float)__builtin_bit_cast(_Float16, a.x[(size_t)t * a.H + c]);
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
-            if (lane == 0) a.sigma[t] = 1.0f / (1.0f + expf(-z));
-        }
+    if (GATEUP && (int)blockIdx.x >= n_main) {
+        sigmoid_gate(a, (blockIdx.x - n_main) * kWaves + wave, (gridDim.x - n_main) * kWaves);
         return;
     }
+    const int K = GATEUP ? a.H : a.Is, R = GATEUP ? a.Is : a.H;
+    const int RG = R / RU, NT = K / 128;
+    const int passes = (a.T + 16 * MT - 1) / (16 * MT);
+    const int units = passes * RG * nkc;
+    if ((int)blockIdx.x >= units) return;
 
-    const int pass = blockIdx.x / CH, c = blockIdx.x % CH;
-    const int rgl = wave / S, ks = wave % S;
-    const int rg = c * RGB + rgl;
-    const bool row_ok = rg < RG;
-    const int t0 = ks * NT / S, t1 = (ks + 1) * NT / S;      // this wave's tiles
-    const int NR = (t1 - t0 + D - 1) / D;                    // rounds of D tiles (the last may be partial)
-
-    // weights: lane (g4, n16) reads row 16 rg + n16, columns 32s + 8 g4 of each tile
     const uint16_t *wm[NMAT];
     if (GATEUP) {
         wm[0] = a.wg;
@@ -119,132 +153,248 @@ __global__ __launch_bounds__(kThreads) void fp16_ffn_kernel(SArgs a, int n_items
     } else {
         wm[0] = a.wd;
     }
-    const int wbytes = R * K * 2;                            // < 2^31 (checked on the host)
-    const int wvoff = row_ok ? ((rg * 16 + n16) * K + 8 * g4) * 2 : kOob;
-    // activations: lane (g4, n16) of token tile m reads token 16 (MT pass + m) + n16, same columns
+    const int wbytes = R * K * 2;                    // < 2^31 (checked on the host)
     const uint16_t *am = GATEUP ? a.x : a.hs;
     const int abytes = a.T * K * 2;
-    int avoff[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int tok = (pass * MT + m) * 16 + n16;
-        avoff[m] = tok < a.T ? (tok * K + 8 * g4) * 2 : kOob;
-    }
 
-    u32x4 wb[D][NMAT][4], ab[D][MT][4];
-    auto issue = [&](int d, int t) {
-        const bool ok = t < t1;
-        const int soff = (ok ? t : 0) * 256;
+    // Loads of this wave's tile j of unit u (zeros past the chunk or the last unit).
+    struct Src {
+        int wvoff, kt0, kt1;
+        int avoff[MT];
+    };
+    auto src_of = [&](int u) {
+        Src q;
+        const bool any = u < units;
+        const int uu = any ? u : 0;
+        const int kc = uu % nkc, rest = uu / nkc;
+        const int rg = rest % RG, p = rest / RG;
+        q.kt0 = kc * NT / nkc;
+        q.kt1 = any ? (kc + 1) * NT / nkc : q.kt0;
+        q.wvoff = n16 < RU ? ((rg * RU + n16) * K + 8 * g4) * 2 : kOob;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int tok = (p * MT + m) * 16 + n16;
+            q.avoff[m] = tok < a.T ? (tok * K + 8 * g4) * 2 : kOob;
+        }
+        return q;
+    };
+    u32x4 wb[NTW][NMAT][4], ab[NTW][MT][4];
+    auto issue = [&](const Src &q, int j) {
+        const int kt = q.kt0 + wave + 8 * j;
+        const bool ok = kt < q.kt1;
+        const int soff = (ok ? kt : 0) * 256;
 #pragma unroll
         for (int mat = 0; mat < NMAT; ++mat) {
             const __amdgpu_buffer_rsrc_t wr = rsrc(wm[mat], ok ? wbytes : 0);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) wb[d][mat][s] = bload(wr, wvoff, soff + 64 * s);
+            for (int s = 0; s < 4; ++s) wb[j][mat][s] = bload(wr, q.wvoff, soff + 64 * s);
         }
         const __amdgpu_buffer_rsrc_t arr = rsrc(am, ok ? abytes : 0);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ab[d][m][s] = bload(arr, avoff[m], soff + 64 * s);
+            for (int s = 0; s < 4; ++s) ab[j][m][s] = bload(arr, q.avoff[m], soff + 64 * s);
     };
-    // the same load order as the refills in the loop, so the wait before each
-    // slot's first use counts only the loads issued after it
+
+    int u = blockIdx.x;
+    Src cur = src_of(u);
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
+    for (int j = 0; j < NTW; ++j) {
         __builtin_amdgcn_sched_barrier(0);
-        issue(d, t0 + d);
+        issue(cur, j);
     }
     __builtin_amdgcn_sched_barrier(0);
-
-    f32x4 acc[NMAT][MT];
+    for (; u < units; u += n_main) {
+        const Src nxt = src_of(u + n_main);
+        f32x4 acc[NMAT][MT];
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat)
+        for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[mat][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < NR; ++r) {
+            for (int m = 0; m < MT; ++m) acc[mat][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
+        for (int j = 0; j < NTW; ++j) {
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) acc[mat][m] = mfma(ab[d][m][s], wb[d][mat][s], acc[mat][m]);
-            // every read of this slot happens above: reload it in place
+                    for (int m = 0; m < MT; ++m) acc[mat][m] = mfma(ab[j][m][s], wb[j][mat][s], acc[mat][m]);
+            // every read of this slot happens above: refill it with the next unit's tile
             __builtin_amdgcn_sched_barrier(0);
-            issue(d, t0 + (r + 1) * D + d);
+            issue(nxt, j);
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
-
-    if (S > 1) {
-        if (ks > 0) {
+        // the unit's 8 partial sums, added in wave order; lane (g4, n16) of
+        // tile (mat, m) holds tokens 16 (MT p + m) + 4 g4 + q of row RU rg + n16
 #pragma unroll
-            for (int mat = 0; mat < NMAT; ++mat)
+        for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) red[ks - 1][rgl][mat * MT + m][q][lane] = acc[mat][m][q];
-        }
+            for (int m = 0; m < MT; ++m) red[wave][mat * MT + m][lane] = acc[mat][m];
         lds_barrier();
-        if (ks != 0) return;
+        {
+            const int kc = u % nkc, rest = u / nkc;
+            const int rg = rest % RG, p = rest / RG;
+            for (int i = tid; i < MT * 64; i += kThreads) {
+                const int m = i >> 6, l = i & 63;
+                if ((l & 15) >= RU) continue;
+                f32x4 v[NMAT];
 #pragma unroll
-        for (int k2 = 1; k2 < S; ++k2)
+                for (int mat = 0; mat < NMAT; ++mat) {
+                    v[mat] = red[0][mat * MT + m][l];
 #pragma unroll
-            for (int mat = 0; mat < NMAT; ++mat)
+                    for (int w = 1; w < kWaves; ++w) v[mat] += red[w][mat * MT + m][l];
+                }
+                const int col = rg * RU + (l & 15);
 #pragma unroll
-                for (int m = 0; m < MT; ++m)
+                for (int q = 0; q < 4; ++q) {
+                    const int t = (p * MT + m) * 16 + 4 * (l >> 4) + q;
+                    if (t >= a.T) continue;
+                    if (GATEUP && nkc == 1) {
+                        const float g = v[0][q], uv = v[NMAT - 1][q];
+                        a.hs[(size_t)t * a.Is + col] = float_to_half_bits(g / (1.0f + expf(-g)) * uv);
+                    } else {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[mat][m][q] += red[k2 - 1][rgl][mat * MT + m][q][lane];
-    }
-    if (!row_ok) return;
-    // lane (g4, n16) holds tokens 16 (MT pass + m) + 4 g4 + q of row 16 rg + n16
-    const int col = rg * 16 + n16;
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = (pass * MT + m) * 16 + 4 * g4 + q;
-            if (t < a.T) {
-                if constexpr (GATEUP) {
-                    const float g = acc[0][m][q], u = acc[NMAT - 1][m][q];
-                    a.hs[(size_t)t * a.Is + col] = float_to_half_bits(g / (1.0f + expf(-g)) * u);
-                } else {
-                    a.out[(size_t)t * a.H + col] = acc[0][m][q];
+                        for (int mat = 0; mat < NMAT; ++mat)
+                            dst[((size_t)kc * a.T + t) * (size_t)(NMAT * R) + mat * R + col] = v[mat][q];
+                    }
                 }
             }
         }
+        lds_barrier();
+        cur = nxt;
+    }
 }
 
-constexpr int kSplit = 8;
+// hs = RN16(silu(sum_kc g) * sum_kc u), chunks in order, 4 columns per thread.
+__global__ __launch_bounds__(kThreads) void shared_gateup_finish(SArgs a, int nkc)
+{
+    const int n4 = a.Is / 4;
+    const long long total = (long long)a.T * n4;
+    const size_t stride = (size_t)a.T * 2 * a.Is;
+    for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long long)gridDim.x * kThreads) {
+        const int t = (int)(i / n4), c = (int)(i % n4) * 4;
+        const float *pg = a.part + (size_t)t * 2 * a.Is + c;
+        f32x4 g = *reinterpret_cast<const f32x4 *>(pg), u = *reinterpret_cast<const f32x4 *>(pg + a.Is);
+        for (int kc = 1; kc < nkc; ++kc) {
+            g += *reinterpret_cast<const f32x4 *>(pg + kc * stride);
+            u += *reinterpret_cast<const f32x4 *>(pg + kc * stride + a.Is);
+        }
+        uint32_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = float_to_half_bits(g[q] / (1.0f + expf(-g[q])) * u[q]);
+        *reinterpret_cast<u32x2 *>(a.hs + (size_t)t * a.Is + c) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    }
+}
 
-// MT token tiles share every weight load; a pass covers 16*MT tokens.
-template <bool GATEUP, int D, int MT>
-int launch_mt(const SArgs &a, hipStream_t s, const char *who)
+// shared_out = sum_kc of the down projection's partial sums, chunks in order.
+__global__ __launch_bounds__(kThreads) void shared_down_finish(SArgs a, int nkc)
+{
+    const int n4 = a.H / 4;
+    const long long total = (long long)a.T * n4;
+    const size_t stride = (size_t)a.T * a.H;
+    for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long long)gridDim.x * kThreads) {
+        const int t = (int)(i / n4), c = (int)(i % n4) * 4;
+        const float *pp = a.part + (size_t)t * a.H + c;
+        f32x4 v = *reinterpret_cast<const f32x4 *>(pp);
+        for (int kc = 1; kc < nkc; ++kc) v += *reinterpret_cast<const f32x4 *>(pp + kc * stride);
+        *reinterpret_cast<f32x4 *>(a.out + (size_t)t * a.H + c) = v;
+    }
+}
+
+// How one projection is cut: rows per unit (RU), chunks of the reduction
+// axis (NKC), token tiles per pass (MT) and tiles per wavefront per unit (NTW).
+struct Plan {
+    int ru, nkc, mt, ntw;
+};
+
+// Token tiles per pass: one tile for T <= 16, two for T <= 32, else four.
+int plan_mt(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
+
+// Largest NTW the registers allow for the ring of one wave (8-row units
+// only run with one token tile).
+int max_ntw(bool gateup, int ru) { return ru == 8 ? (gateup ? 4 : 6) : 2; }
+
+// Small batches (one token tile): units of 8 rows over the whole reduction
+// axis when a wave's share of it fits the ring, which needs no partial sums
+// (twice the units of 16-row groups spread the bytes evenly over the CUs).
+// Otherwise 16-row units and the chunk count (at least NT / 16) whose units
+// fill 256 blocks best, a unit's efficiency being the share of the 8 NTW
+// tile slots it uses; ties go to fewer chunks (less partial-sum traffic).
+Plan plan_of(bool gateup, int T, int R, int K)
+{
+    const int NT = K / 128;
+    const int mt = plan_mt(T);
+    if (mt == 1 && (NT + 7) / 8 <= max_ntw(gateup, 8)) return Plan{8, 1, 1, (NT + 7) / 8};
+    const int RG = R / 16;
+    const long long passes = (T + 16 * mt - 1) / (16 * mt);
+    const int kmax = max_ntw(gateup, 16);
+    int best = (NT + 8 * kmax - 1) / (8 * kmax);
+    double best_eff = -1.0;
+    for (int nkc = best; nkc <= NT; ++nkc) {
+        const int ntw = ((NT + nkc - 1) / nkc + 7) / 8;
+        if (ntw > kmax) continue;
+        const long long units = passes * RG * nkc;
+        const long long rounds = (units + kPlanBlocks - 1) / kPlanBlocks;
+        const double eff = (double)units / (double)(rounds * kPlanBlocks) * ((double)NT / nkc) / (8.0 * ntw);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = nkc;
+        }
+    }
+    return Plan{16, best, mt, ((NT + best - 1) / best + 7) / 8};
+}
+
+template <bool GATEUP, int MT, int NTW, int RU>
+int launch_stream(const SArgs &a, const Plan &pl, float *dst, hipStream_t s, const char *who)
 {
     const int R = GATEUP ? a.Is : a.H;
-    const int RG = R / 16, RGB = kWaves / kSplit;
-    const int CH = (RG + RGB - 1) / RGB;
-    const int passes = (a.T + 16 * MT - 1) / (16 * MT);
-    const int n_items = CH * passes;
-    const int sig_blocks = GATEUP ? (a.T + kWaves - 1) / kWaves : 0;
-    hipLaunchKernelGGL((fp16_ffn_kernel<GATEUP, kSplit, D, MT>), dim3((unsigned int)(n_items + sig_blocks)),
-                       dim3(kThreads), 0, s, a, n_items);
+    const long long passes = (a.T + 16 * MT - 1) / (16 * MT);
+    const long long units = passes * (R / RU) * pl.nkc;
+    auto kern = fp16_stream_kernel<GATEUP, MT, NTW, RU>;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess || occ <= 0) occ = 1;
+    long long g = (long long)ffn::cu_count() * occ;
+    if (g > units) g = units;
+    // gate/up: one more wave per token for the sigmoid gate
+    const long long gsig = GATEUP ? ((a.T + kWaves - 1) / kWaves < ffn::cu_count() ? (a.T + kWaves - 1) / kWaves
+                                                                                 : ffn::cu_count())
+                                  : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned int)(g + gsig)), dim3(kThreads), 0, s, a, pl.nkc, (int)g, dst);
     return moe::check_launch(who);
 }
 
-template <bool GATEUP>
-int launch(const SArgs &a, hipStream_t s, const char *who)
+template <bool GATEUP, int RU, int MT, int N>
+int launch_ntw(const SArgs &a, const Plan &pl, float *dst, hipStream_t s, const char *who)
 {
-    // (gate/up holds two weight matrices per tile, so its register budget
-    // allows two token tiles per pass)
-    const int tiles = (a.T + 15) / 16;
-    if (tiles <= 1) return launch_mt<GATEUP, GATEUP ? 2 : 3, 1>(a, s, who);
-    if (GATEUP || tiles == 2) return launch_mt<GATEUP, GATEUP ? 1 : 2, 2>(a, s, who);
-    return launch_mt<false, 1, 4>(a, s, who);
+    if constexpr (N > 1) {
+        if (pl.ntw < N) return launch_ntw<GATEUP, RU, MT, N - 1>(a, pl, dst, s, who);
+    }
+    return launch_stream<GATEUP, MT, N, RU>(a, pl, dst, s, who);
 }
 
-size_t ws_bytes(int T, int Is) { return ((size_t)T * Is * 2 + 255) / 256 * 256; }
+template <bool GATEUP>
+int launch_proj(const SArgs &a, const Plan &pl, float *dst, hipStream_t s, const char *who)
+{
+    if (pl.ru == 8) return launch_ntw<GATEUP, 8, 1, GATEUP ? 4 : 6>(a, pl, dst, s, who);
+    if (pl.mt == 1) return launch_ntw<GATEUP, 16, 1, 2>(a, pl, dst, s, who);
+    if (pl.mt == 2) return launch_ntw<GATEUP, 16, 2, 2>(a, pl, dst, s, who);
+    return launch_ntw<GATEUP, 16, 4, 2>(a, pl, dst, s, who);
+}
+
+// Workspace: hs (FP16 [T][Is]), then the partial sums of whichever
+// projection needs more (the down projection's are written after the
+// gate/up ones are consumed).
+size_t hs_bytes(int T, int Is) { return ((size_t)T * Is * 2 + 255) / 256 * 256; }
+
+size_t part_bytes(int T, int H, int Is)
+{
+    const int nkg = plan_of(true, T, Is, H).nkc, nkd = plan_of(false, T, H, Is).nkc;
+    const size_t gu = nkg > 1 ? (size_t)nkg * T * 2 * Is : 0;
+    const size_t dn = nkd > 1 ? (size_t)nkd * T * H : 0;
+    return (gu > dn ? gu : dn) * 4;
+}
+
+size_t ws_bytes(int T, int H, int Is) { return hs_bytes(T, Is) + part_bytes(T, H, Is); }
 
 }  // namespace
 
@@ -252,8 +402,8 @@ extern "C" {
 
 size_t moe_shared_ffn_workspace_size(int T, int H, int Is)
 {
-    if (T < 0 || H <= 0 || Is <= 0 || H % 128 || Is % 128) return 0;
-    return ws_bytes(T, Is);
+    if (T < 0 || T > 65536 || H <= 0 || Is <= 0 || H % 128 || Is % 128) return 0;
+    return ws_bytes(T, H, Is);
 }
 
 int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_dev, const void *w_down_dev,
@@ -273,9 +423,9 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
     if (!moe::aligned(x_dev, 16) || !moe::aligned(w_gate_dev, 16) || !moe::aligned(w_up_dev, 16) ||
         !moe::aligned(w_down_dev, 16) || !moe::aligned(shared_out_dev, 16))
         return moe::fail(MOE_ERR_INVALID_ARG, "moe_shared_ffn: x, weights and shared_out must be 16-byte aligned");
-    if (!ws_dev || ws_bytes_ < ws_bytes(T, Is) || !moe::aligned(ws_dev, 256))
-        return moe::fail(MOE_ERR_WORKSPACE, "moe_shared_ffn: the workspace needs %zu bytes, 256-byte aligned",
-                         ws_bytes(T, Is));
+    const size_t need = ws_bytes(T, H, Is);
+    if (!ws_dev || ws_bytes_ < need || !moe::aligned(ws_dev, 256))
+        return moe::fail(MOE_ERR_WORKSPACE, "moe_shared_ffn: the workspace needs %zu bytes, 256-byte aligned", need);
     SArgs a;
     a.x = (const uint16_t *)x_dev;
     a.wg = (const uint16_t *)w_gate_dev;
@@ -284,12 +434,28 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
     a.wgate = (const uint16_t *)w_sgate_dev;
     a.T = T; a.H = H; a.Is = Is;
     a.hs = (uint16_t *)ws_dev;
+    a.part = reinterpret_cast<float *>((uint8_t *)ws_dev + hs_bytes(T, Is));
     a.out = shared_out_dev;
     a.sigma = shared_gate_dev;
     hipStream_t s = (hipStream_t)stream;
-    int rc = launch<true>(a, s, "moe_shared_ffn (gate/up)");
+    const Plan pg = plan_of(true, T, Is, H), pd = plan_of(false, T, H, Is);
+    int rc = launch_proj<true>(a, pg, a.part, s, "moe_shared_ffn (gate/up)");
     if (rc) return rc;
-    return launch<false>(a, s, "moe_shared_ffn (down)");
+    auto grid_of = [](long long n4) {
+        long long g = (n4 + kThreads - 1) / kThreads;
+        return (unsigned int)(g < 4LL * ffn::cu_count() ? g : 4LL * ffn::cu_count());
+    };
+    if (pg.nkc > 1) {
+        // SwiGLU of the summed chunks, about 4 columns per thread
+        hipLaunchKernelGGL(shared_gateup_finish, dim3(grid_of((long long)T * (Is / 4))), dim3(kThreads), 0, s, a,
+                           pg.nkc);
+        rc = moe::check_launch("moe_shared_ffn (SwiGLU)");
+        if (rc) return rc;
+    }
+    rc = launch_proj<false>(a, pd, pd.nkc > 1 ? a.part : a.out, s, "moe_shared_ffn (down)");
+    if (rc || pd.nkc == 1) return rc;
+    hipLaunchKernelGGL(shared_down_finish, dim3(grid_of((long long)T * (H / 4))), dim3(kThreads), 0, s, a, pd.nkc);
+    return moe::check_launch("moe_shared_ffn (down sums)");
 }
 
 }  // extern "C"
