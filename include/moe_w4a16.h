@@ -200,14 +200,16 @@ int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
  *   shared_gate[t] = 1 / (1 + exp(-(w_sgate . x_t)))  (FP32).
  * The layer output then adds shared_gate[t] * shared_out[t] (moe_combine).
  * Inputs:  x_dev FP16 [T][H]; w_gate_dev, w_up_dev FP16 [Is][H]; w_down_dev
- *          FP16 [H][Is]; w_sgate_dev FP16 [H]; all row-major, 16-byte aligned
- *          (w_sgate 2-byte).  H and Is positive multiples of 128, each
- *          matrix under 2 GiB.
+ *          FP16 [H][Is]; w_sgate_dev FP16 [H]; all row-major, 16-byte
+ *          aligned.  H and Is positive multiples of 128, each matrix under
+ *          2 GiB, 0 <= T <= 65536.
  * Outputs: shared_out_dev FP32 [T][H] (16-byte aligned), shared_gate_dev FP32 [T].
  * ws_dev / ws_bytes: workspace of moe_shared_ffn_workspace_size(T, H, Is)
- *   bytes (256-byte aligned) holding hs between the two kernels; no
+ *   bytes (256-byte aligned) holding hs and, for shapes whose reduction axis
+ *   is cut into chunks, the FP32 partial sums of the chunks; no
  *   initialization; not shared by overlapping calls.
- * Two kernel launches on `stream`; T = 0 enqueues nothing. */
+ * Two to four kernel launches on `stream` (chunk sums are added in a fixed
+ * order: results do not depend on scheduling); T = 0 enqueues nothing. */
 size_t moe_shared_ffn_workspace_size(int T, int H, int Is);
 int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_dev, const void *w_down_dev,
                    const void *w_sgate_dev, int T, int H, int Is, float *shared_out_dev, float *shared_gate_dev,

@@ -421,7 +421,7 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
     if (!x_dev || !w_gate_dev || !w_up_dev || !w_down_dev || !w_sgate_dev || !shared_out_dev || !shared_gate_dev)
         return moe::fail(MOE_ERR_INVALID_ARG, "moe_shared_ffn: null pointer argument");
     if (!moe::aligned(x_dev, 16) || !moe::aligned(w_gate_dev, 16) || !moe::aligned(w_up_dev, 16) ||
-        !moe::aligned(w_down_dev, 16) || !moe::aligned(shared_out_dev, 16))
+        !moe::aligned(w_down_dev, 16) || !moe::aligned(w_sgate_dev, 16) || !moe::aligned(shared_out_dev, 16))
         return moe::fail(MOE_ERR_INVALID_ARG, "moe_shared_ffn: x, weights and shared_out must be 16-byte aligned");
     const size_t need = ws_bytes(T, H, Is);
     if (!ws_dev || ws_bytes_ < need || !moe::aligned(ws_dev, 256))
