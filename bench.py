@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--partial", action="store_true",
+                    help="qwen: keep only the config's resident experts published (39 of 60) and upload the "
+                         "misses of every step before its expert FFN, as olmoe_stack does")
     ap.add_argument("--kernel-only", default=None, choices=[None, "gateup", "down", "copy"],
                     help="profile helper: after setup, launch only this kernel --steps times "
                          "(copy: a 256 MiB device-to-device copy, the counter calibration)")
@@ -146,7 +149,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    if args.config == "olmoe_stack":
+    if args.config == "olmoe_stack" or (args.config == "qwen" and args.partial):
         run_stack(args, torch, dev)
         return
     if args.kernel_only == "copy":
@@ -430,26 +433,31 @@ def main():
 
 
 def run_stack(args, torch, dev):
-    """OLMoE-shaped 16-layer decode stack with partial residency: each layer keeps `resident` of
-    its E experts published in a resident expert table; a step routes each layer (Zipf-skewed
-    router), brings the active expert list to the host, uploads the misses from the layer's
-    immutable host source through pinned staging, runs the expert FFN on the table's rows and
-    combines.  No graphs: every layer of every step has a host round trip."""
+    """Decode with partial residency: each layer keeps `resident` of its E experts published in a
+    resident expert table; a step routes each layer, brings the active expert list to the host,
+    uploads the misses from the layer's immutable host source through pinned staging, runs the
+    expert FFN on the table's rows (and the FP16 shared expert where the layer has one) and
+    combines.  Workloads: the OLMoE-shaped 16-layer stack with a Zipf-skewed router, and the
+    Qwen-shaped layer with 39 of 60 experts resident (--config qwen --partial).  No graphs: every
+    layer of every step has a host round trip."""
     from w4a16_routed_expert_amd import binding as B
     from w4a16_routed_expert_amd import synth
     from w4a16_routed_expert_amd.layer import ResidentExpertTable, RoutedExpertLayer
-    cfg = synth.CONFIGS["olmoe_stack"]
+    cfg = synth.CONFIGS[args.config]
     T = args.tokens or max(cfg.batches)
     L = args.layers or cfg.n_layers
     H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+    Is = cfg.shared_I
     spare = min(E - cfg.resident, T * k)
     S = max(1, args.inputs)
     t0 = time.time()
     host = [synth.make_expert_rows(cfg, layer=l) for l in range(L)]
-    layers, tables, xs = [], [], []
+    layers, tables, xs, shared = [], [], [], []
     for l in range(L):
         wr = torch.from_numpy(synth.make_router(cfg, layer=l)).to(dev)
-        bias = torch.from_numpy(synth.make_zipf_bias(cfg, layer=l)).to(dev)
+        bias = torch.from_numpy(synth.make_zipf_bias(cfg, layer=l)).to(dev) if cfg.zipf_s else None
+        if Is:
+            shared.append([torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in synth.make_shared(cfg, layer=l)])
         tab = ResidentExpertTable(host[l], H, I, cfg.resident, spare, staging_rows=2)
         rows_dev, stride, _ = tab.device()
         lay = RoutedExpertLayer(H, I, E, k, torch.empty((1, stride), dtype=torch.uint8, device=dev), wr, bias,
@@ -459,6 +467,10 @@ def run_stack(args, torch, dev):
         xs.append([torch.from_numpy(synth.make_x(cfg, T, step=s, layer=l)).to(dev) for s in range(S)])
     gen_s = time.time() - t0
     y = torch.empty((T, H), dtype=torch.float16, device=dev)
+    sh_out = torch.empty((T, H), dtype=torch.float32, device=dev) if Is else None
+    sh_gate = torch.empty((T,), dtype=torch.float32, device=dev) if Is else None
+    sh_ws_bytes = B.moe_shared_ffn_workspace_size(T, H, Is) if Is else 0
+    sh_ws = torch.empty((max(sh_ws_bytes, 256),), dtype=torch.uint8, device=dev) if Is else None
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     ffn_us, ffn_bytes = [0.0], [0]
     row_bytes, _ = B.moe_expert_row_bytes(H, I)
@@ -467,6 +479,9 @@ def run_stack(args, torch, dev):
         for l in range(L):
             lay, tab, x = layers[l], tables[l], xs[l][s % S]
             lay.route(x)
+            if Is:
+                Wsg, Wsu, Wsd, wg = shared[l]
+                B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes)
             active = lay.active_experts()
             tab.prepare(active)
             if timed_ffn:
@@ -478,7 +493,7 @@ def run_stack(args, torch, dev):
                 ffn_us[0] += ev[0].elapsed_time(ev[1]) * 1e3
                 ffn_bytes[0] += len(active) * row_bytes
             tab.record_consumers()
-            lay.combine(T, y)
+            lay.combine(T, y, shared_out=sh_out, shared_gate=sh_gate)
 
     for s in range(args.warmup):
         step(s)
@@ -504,9 +519,11 @@ def run_stack(args, torch, dev):
         "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / K,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
-        "config": {"workload": f"olmoe_stack{L}_T{T}_resident{cfg.resident}of{E}", "layers": L, "tokens": T,
+        "config": {"workload": (f"olmoe_stack{L}" if args.config == "olmoe_stack" else f"{args.config}_decode_layer")
+                               + f"_T{T}_resident{cfg.resident}of{E}", "layers": L, "tokens": T,
                    "experts": E, "top_k": k, "hidden": H, "intermediate": I, "resident": cfg.resident,
-                   "spare_rows": spare, "zipf_s": cfg.zipf_s, "input_batches": S},
+                   "spare_rows": spare, "zipf_s": cfg.zipf_s, "shared_expert_intermediate": Is,
+                   "input_batches": S},
         "residency": {
             "hit_rate": delta["hits"] / max(1, delta["hits"] + delta["misses"]),
             "misses_per_step": delta["misses"] / K,

@@ -146,8 +146,10 @@ def run_layer(cfg, rows, wr, xs, bias=None, table=None):
     return ys
 
 
-# spare rows = min(E - capacity, T*k): enough for any step
-@pytest.mark.parametrize("name,capacity,spare,T", [("tiny", 3, 5, 4), ("olmoe_stack", 40, 24, 8)])
+# spare rows = min(E - capacity, T*k): enough for any step; the Qwen-shaped layer keeps 39 of
+# its 60 experts resident
+@pytest.mark.parametrize("name,capacity,spare,T", [("tiny", 3, 5, 4), ("olmoe_stack", 40, 24, 8),
+                                                   ("qwen", 39, 21, 16), ("qwen", 39, 4, 1)])
 def test_partial_residency_output_equals_full_residency(name, capacity, spare, T):
     cfg = synth.CONFIGS[name]
     rows = synth.make_expert_rows(cfg)
