@@ -114,8 +114,9 @@ size_t moe_expert_row_bytes(int H, int I, size_t *off6);
  * Inputs:  x_dev FP16 [T][H] row-major; w_router_dev FP16 [H][E] row-major;
  *          bias_dev FP32 [E] or NULL.
  * ws_dev / ws_bytes: workspace of moe_route_workspace_size(T, H, E) bytes,
- *   256-byte aligned, required; it holds the logits between the two kernels
- *   and needs no initialization.  One workspace must not be used by two calls
+ *   256-byte aligned, required; it holds what passes between the call's
+ *   kernels (the logits for T <= 256, per-segment expert counts above) and
+ *   needs no initialization.  One workspace must not be used by two calls
  *   that can overlap; a workspace sized for T serves any T' <= T.
  * Limits: T <= 65536, H <= 4096 (bounds the exact integer accumulators);
  *   x_dev 8-byte aligned. */
