@@ -178,8 +178,18 @@ __global__ __launch_bounds__(kThreads) void fp16_stream_kernel(SArgs a, int nkc,
         }
         return q;
     };
+    // With one pass over the whole axis a wave's tiles, and so its activation
+    // fragments, are the same in every unit: they are loaded once and kept.
+    const bool act_fixed = nkc == 1 && passes == 1;
     u32x4 wb[NTW][NMAT][4], ab[NTW][MT][4];
-    auto issue = [&](const Src &q, int j) {
+    auto issue_act = [&](const Src &q, int j, bool ok, int soff) {
+        const __amdgpu_buffer_rsrc_t arr = rsrc(am, ok ? abytes : 0);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ab[j][m][s] = bload(arr, q.avoff[m], soff + 64 * s);
+    };
+    auto issue = [&](const Src &q, int j, bool with_act) {
         const int kt = q.kt0 + wave + 8 * j;
         const bool ok = kt < q.kt1;
         const int soff = (ok ? kt : 0) * 256;
@@ -189,11 +199,7 @@ __global__ __launch_bounds__(kThreads) void fp16_stream_kernel(SArgs a, int nkc,
 #pragma unroll
             for (int s = 0; s < 4; ++s) wb[j][mat][s] = bload(wr, q.wvoff, soff + 64 * s);
         }
-        const __amdgpu_buffer_rsrc_t arr = rsrc(am, ok ? abytes : 0);
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) ab[j][m][s] = bload(arr, q.avoff[m], soff + 64 * s);
+        if (with_act) issue_act(q, j, ok, soff);
     };
 
     int u = blockIdx.x;
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void fp16_stream_kernel(SArgs a, int nkc,
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
         __builtin_amdgcn_sched_barrier(0);
-        issue(cur, j);
+        issue(cur, j, true);
     }
     __builtin_amdgcn_sched_barrier(0);
     for (; u < units; u += n_main) {
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void fp16_stream_kernel(SArgs a, int nkc,
                     for (int m = 0; m < MT; ++m) acc[mat][m] = mfma(ab[j][m][s], wb[j][mat][s], acc[mat][m]);
             // every read of this slot happens above: refill it with the next unit's tile
             __builtin_amdgcn_sched_barrier(0);
-            issue(nxt, j);
+            issue(nxt, j, !act_fixed);
             __builtin_amdgcn_sched_barrier(0);
         }
         // the unit's 8 partial sums, added in wave order; lane (g4, n16) of
