@@ -178,9 +178,10 @@ __global__ __launch_bounds__(kThreads) void fp16_stream_kernel(SArgs a, int nkc,
         }
         return q;
     };
-    // With one pass over the whole axis a wave's tiles, and so its activation
-    // fragments, are the same in every unit: they are loaded once and kept.
-    const bool act_fixed = nkc == 1 && passes == 1;
+    // With one token pass and a block stride that is a multiple of nkc, every
+    // unit of a block has the same chunk (kc = u mod nkc), so a wave's tiles
+    // and activation fragments are the same in each: loaded once and kept.
+    const bool act_fixed = passes == 1 && n_main % nkc == 0;
     u32x4 wb[NTW][NMAT][4], ab[NTW][MT][4];
     auto issue_act = [&](const Src &q, int j, bool ok, int soff) {
         const __amdgpu_buffer_rsrc_t arr = rsrc(am, ok ? abytes : 0);
@@ -361,6 +362,7 @@ int launch_stream(const SArgs &a, const Plan &pl, float *dst, hipStream_t s, con
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess || occ <= 0) occ = 1;
     long long g = (long long)ffn::cu_count() * occ;
     if (g > units) g = units;
+    if (g >= pl.nkc) g -= g % pl.nkc;    // each block keeps one chunk
     // gate/up: one more wave per token for the sigmoid gate
     const long long gsig = GATEUP ? ((a.T + kWaves - 1) / kWaves < ffn::cu_count() ? (a.T + kWaves - 1) / kWaves
                                                                                  : ffn::cu_count())
