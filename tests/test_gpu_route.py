@@ -146,3 +146,24 @@ def test_large_batch_skewed_grouping():
     assert np.array_equal(got["ids"], ids)
     assert set(np.unique(ids)) == {2, 5}
     check_grouping(got, ids, cfg.E, "skewed T=600")
+
+
+# Edges of the supported envelope: one expert (k = 1, every weight 1), k = E,
+# an expert count that is not a multiple of 16, the largest hidden size the
+# exact accumulators allow (H = 4096) on both paths, and the largest batch of
+# the split-logits path (T = 256) next to the smallest of the other (257).
+@pytest.mark.parametrize("H,E,k,T", [(256, 1, 1, 7), (256, 3, 3, 20), (512, 37, 5, 300), (4096, 64, 8, 5),
+                                     (4096, 64, 8, 300), (2048, 64, 8, 256), (2048, 64, 8, 257)])
+def test_route_envelope_edges(H, E, k, T):
+    g = np.random.default_rng(H * 131 + E * 7 + T)
+    x = g.standard_normal((T, H)).astype(np.float16)
+    wr = (g.standard_normal((H, E)) * 0.02).astype(np.float16)
+    got = run_route(x, wr, k)
+    ref = oracle.router_logits(x, wr)
+    assert np.array_equal(got["logits"].view(np.uint32), ref.view(np.uint32)), "logits"
+    ids, w = oracle.topk_softmax(ref, k)
+    assert np.array_equal(got["ids"], ids), "ids"
+    assert np.allclose(got["w"], w, rtol=1e-5, atol=1e-7), "weights"
+    if E == 1:
+        assert np.all(got["w"] == 1.0)
+    check_grouping(got, ids, E, f"H={H} E={E} k={k} T={T}")
