@@ -102,6 +102,23 @@ def test_streaming_odd_shapes(H, I):
     check_full(cfg, got, ref, f"streaming H={H} I={I}", rows=rows)
 
 
+# Expert counts at the edges: one expert with k = 1 (every routing weight 1),
+# and 37 experts (not a multiple of 16) with k = 5; both FFN kernel families.
+@pytest.mark.parametrize("E,k,H,I,T", [(1, 1, 256, 128, 3), (37, 5, 384, 256, 50)])
+@pytest.mark.parametrize("path", ["stream", "gemm"])
+def test_expert_count_edges(E, k, H, I, T, path):
+    from w4a16_routed_expert_amd import binding as B
+    cfg = synth.LayerConfig(f"edge{E}x{k}", 10, E=E, k=k, H=H, I=I, batches=(T,), resident=E)
+    rows, wr, x = synth.make_expert_rows(cfg), synth.make_router(cfg), synth.make_x(cfg, T)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
+    B.moe_set_ffn_path(B.MOE_FFN_PATH_STREAM if path == "stream" else B.MOE_FFN_PATH_GEMM)
+    try:
+        got = gpu_layer(cfg, rows, wr, x)
+    finally:
+        B.moe_set_ffn_path(B.MOE_FFN_PATH_AUTO)
+    check_full(cfg, got, ref, f"{path} E={E} k={k}", rows=rows)
+
+
 def test_run_to_run_bit_identical():
     cfg = synth.CONFIGS["tiny"]
     T = 33
