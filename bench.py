@@ -135,7 +135,7 @@ def main():
         traffic_report(*args.traffic_report, cfg.name, args.tokens or max(cfg.batches))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the layer is single-GPU; multi-GPU sharding is described in the design notes, not built).",
               file=sys.stderr)
         sys.exit(2)
