@@ -358,9 +358,9 @@ int launch_stream(const SArgs &a, const Plan &pl, float *dst, hipStream_t s, con
     const long long passes = (a.T + 16 * MT - 1) / (16 * MT);
     const long long units = passes * (R / RU) * pl.nkc;
     auto kern = fp16_stream_kernel<GATEUP, MT, NTW, RU>;
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess || occ <= 0) occ = 1;
-    long long g = (long long)ffn::cu_count() * occ;
+    // one block per CU, as the unit plan assumes (measured: a second resident
+    // block per CU leaves the CUs with uneven unit counts and is slower)
+    long long g = (long long)ffn::cu_count();
     if (g > units) g = units;
     if (g >= pl.nkc) g -= g % pl.nkc;    // each block keeps one chunk
     // gate/up: one more wave per token for the sigmoid gate
