@@ -208,10 +208,21 @@ def main():
     def step_args(s):
         return s % R, xs[(s // R) % S], n_act[(s // R) % S]
 
+    side = torch.cuda.Stream(device=dev) if Is else None
+
     def run_step(s, ev=None):
         r, x, _ = step_args(s)
         rows = replicas[r]
         marks = iter(ev) if ev is not None else None
+        # The shared expert needs x only: the timed steps fork it onto a second
+        # stream beside the routing and the routed experts; the per-kernel event
+        # steps keep everything on one stream so each phase has its own time.
+        concurrent = bool(Is) and ev is None
+        main = torch.cuda.current_stream()
+        if concurrent:
+            side.wait_stream(main)
+            Wsg, Wsu, Wsd, wg = shared_reps[r]
+            B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes, side)
 
         def mark():
             if marks is not None:
@@ -226,9 +237,12 @@ def main():
                          lay.n_active, lay.h, lay.pair_out, lay.status)
         mark()
         if Is:
-            Wsg, Wsu, Wsd, wg = shared_reps[r]
-            B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes)
-            mark()
+            if concurrent:
+                main.wait_stream(side)
+            else:
+                Wsg, Wsu, Wsd, wg = shared_reps[r]
+                B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes)
+                mark()
             lay.combine(T, y, sh_out, sh_gate)
         else:
             lay.combine(T, y)
@@ -392,6 +406,7 @@ def main():
             "workload": workload,
             "experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
             "shared_expert_intermediate": Is,
+            "shared_expert_stream": "second stream, concurrent with routing and the routed experts" if Is else None,
             "weights": "int4 qpacked, 256-value blocks, fp16 scales; fp16 activations, fp32 accumulation",
             "replicas": R, "input_batches": S, "graph_replay": not args.no_graph,
             "mean_active_experts": float(np.mean(n_act)),

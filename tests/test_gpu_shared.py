@@ -102,3 +102,43 @@ def test_qwen_layer_with_shared_expert():
     torch.cuda.synchronize()
     assert np.array_equal(lay.topk_ids.cpu().numpy()[:T], ref["ids"])
     assert_close_rows(y.cpu().numpy().view(np.uint16), ref["y"], "qwen layer with shared expert: y")
+
+
+def test_concurrent_shared_expert_equals_sequential():
+    # The layer can run the shared expert on a second stream beside the routing
+    # and the routed experts; the output must equal the one-stream order bit for
+    # bit, also when the forked step is captured in a graph and replayed between
+    # other (eager) layer calls.
+    from w4a16_routed_expert_amd.layer import RoutedExpertLayer, SharedExpert
+    cfg = synth.CONFIGS["qwen"]
+    T = 16
+    dev = torch.device("cuda:0")
+    rows, wr = synth.make_expert_rows(cfg), synth.make_router(cfg)
+    xa = torch.from_numpy(synth.make_x(cfg, T, step=7)).to(dev)
+    xb = torch.from_numpy(synth.make_x(cfg, T, step=8)).to(dev)
+    Wsg, Wsu, Wsd, wg = (torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in synth.make_shared(cfg))
+    lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev), torch.from_numpy(wr).to(dev),
+                            max_T=T, device=dev)
+    # one stream: shared expert first, then the routed layer
+    seq = SharedExpert(Wsg, Wsu, Wsd, wg, max_T=T, device=dev)
+    want = {}
+    for name, x in (("a", xa), ("b", xb)):
+        seq.run(x)
+        want[name] = lay.forward(x, shared_out=seq.out, shared_gate=seq.gate).clone()
+    torch.cuda.synchronize()
+    conc = SharedExpert(Wsg, Wsu, Wsd, wg, max_T=T, device=dev)
+    y = torch.empty((T, cfg.H), dtype=torch.float16, device=dev)
+    lay.forward(xa, y, shared=conc)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), want["a"].view(torch.int16))
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        lay.forward(xa, y, shared=conc)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), want["a"].view(torch.int16)), "graph replay differs"
+        yb = lay.forward(xb, shared=conc)            # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(yb.view(torch.int16), want["b"].view(torch.int16)), "eager call differs"

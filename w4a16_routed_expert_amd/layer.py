@@ -1,7 +1,8 @@
 """Device-buffer plumbing around the C ABI: one routed-expert layer.
 
 RoutedExpertLayer owns the torch device buffers the C calls write into and
-runs route -> expert FFN -> combine on one stream.  It does no arithmetic of
+runs route -> expert FFN -> combine on one stream (a SharedExpert, if given,
+on a second stream beside them).  It does no arithmetic of
 its own: torch provides memory and streams, the HIP library does the work.
 """
 from __future__ import annotations
@@ -80,26 +81,84 @@ class RoutedExpertLayer:
                       stream)
 
     def forward(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None, rows=None,
-                shared_out=None, shared_gate=None, table=None) -> torch.Tensor:
+                shared_out=None, shared_gate=None, table=None, shared: "SharedExpert | None" = None) -> torch.Tensor:
         """y = layer(x); x float16 [T, H] on the device.  With a ResidentExpertTable the
         routed experts' misses are uploaded (host round trip of the active list) before
-        the expert FFN reads the table's rows."""
+        the expert FFN reads the table's rows.  With a SharedExpert its FFN runs on a
+        second stream, concurrently with the routing and the routed experts (it needs x
+        only), and the combine waits for both."""
         T = x.shape[0]
         if y is None:
             y = torch.empty((T, self.H), dtype=torch.float16, device=self.device)
-        self.route(x, stream)
+        main = _torch_stream(stream)
+        if shared is not None:
+            side = shared.side_stream()
+            side.wait_stream(main)
+            shared.run(x, side)
+            shared_out, shared_gate = shared.out, shared.gate
+        self.route(x, main)
         if table is not None:
-            table.prepare(self.active_experts(), stream)
-        self.ffn(x, stream, rows, table)
+            table.prepare(self.active_experts(), main)
+        self.ffn(x, main, rows, table)
         if table is not None:
-            table.record_consumers(stream)
-        self.combine(T, y, shared_out, shared_gate, stream)
+            table.record_consumers(main)
+        if shared is not None:
+            main.wait_stream(side)
+        self.combine(T, y, shared_out, shared_gate, main)
         return y
 
     def active_experts(self):
         """Active expert ids of the last route, on the host (synchronizes with the device)."""
         n = int(self.n_active.cpu()[0])
         return self.active_list[:n].cpu().numpy()
+
+
+def _torch_stream(stream):
+    """A torch stream object for None (the current stream), a torch stream or a raw handle."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
+class SharedExpert:
+    """FP16 shared expert (moe_shared_ffn) with its output buffers and workspace.
+
+    wg, wu: float16 CUDA tensors [Is, H]; wd: [H, Is]; wgate: [H] (16-byte aligned).
+    out (FP32 [T, H]) and gate (FP32 [T]) hold the last run's shared_out and shared_gate.
+    """
+
+    def __init__(self, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor, wgate: torch.Tensor,
+                 max_T: int = 64, device: str | torch.device = "cuda:0"):
+        self.wg, self.wu, self.wd, self.wgate = wg, wu, wd, wgate
+        self.Is, self.H = wg.shape
+        self.device = torch.device(device)
+        self._side = None
+        self.max_T = 0
+        self.ws = torch.empty(256, dtype=torch.uint8, device=self.device)
+        self._alloc(max_T)
+
+    def _alloc(self, T: int):
+        self.max_T = T
+        self.out = torch.empty((max(T, 1), self.H), dtype=torch.float32, device=self.device)
+        self.gate = torch.empty((max(T, 1),), dtype=torch.float32, device=self.device)
+
+    def side_stream(self) -> torch.cuda.Stream:
+        """The second stream the layer forks this expert onto (default priority)."""
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.device)
+        return self._side
+
+    def run(self, x: torch.Tensor, stream=None):
+        T = x.shape[0]
+        if T > self.max_T:
+            self._alloc(T)
+        need = B.moe_shared_ffn_workspace_size(T, self.H, self.Is)
+        if need > self.ws.numel():
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        B.moe_shared_ffn(x, self.wg, self.wu, self.wd, self.wgate, T, self.H, self.Is, self.out, self.gate,
+                         self.ws, self.ws.numel(), stream)
 
 
 class ResidentExpertTable:
