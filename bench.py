@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens of each batch the CPU baseline routes (0 = all; prefill defaults to 32)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--graph-steps", type=int, default=0,
+                    help="consecutive steps captured in one graph (0 = one full rotation over the weight "
+                         "replicas and input batches; each graph launch costs about 4.5 us, so one step per "
+                         "graph is measurably slower)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--partial", action="store_true",
@@ -270,8 +274,12 @@ def main():
         return
 
     # ---------------------------------------------------------------- graphs
+    # Steps repeat with period R*S (replica, input batch).  A graph holds G
+    # consecutive steps; graph g1[s] starts at step s (mod the period), and
+    # single-step graphs cover a remainder of K that G does not divide.
     n_graph = R * S
-    graphs = []
+    G = args.graph_steps if args.graph_steps > 0 else n_graph
+    g1, gG = {}, {}
     if not args.no_graph:
         for s in range(n_graph):
             run_step(s)                 # warm the step once eagerly before capture
@@ -281,23 +289,42 @@ def main():
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 run_step(s)
-            graphs.append(g)
+            g1[s] = g
+        if G > 1:
+            for b in range(n_graph):
+                s0 = (b * G) % n_graph
+                if s0 in gG:
+                    continue
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for j in range(G):
+                        run_step(s0 + j)
+                gG[s0] = g
         torch.cuda.synchronize()
 
-    def replay(s):
-        graphs[s % n_graph].replay()
+    def run_steps(s_begin, count):
+        """Steps s_begin .. s_begin + count - 1."""
+        if args.no_graph:
+            for s in range(s_begin, s_begin + count):
+                run_step(s)
+            return
+        s, end = s_begin, s_begin + count
+        while s < end:
+            if G > 1 and s + G <= end and (s % n_graph) in gG:
+                gG[s % n_graph].replay()
+                s += G
+            else:
+                g1[s % n_graph].replay()
+                s += 1
 
-    step_fn = run_step if args.no_graph else replay
-    for s in range(args.warmup):
-        step_fn(s)
+    run_steps(0, args.warmup)
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed
     K = args.steps
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(K):
-        step_fn(s)
+    run_steps(args.warmup, K)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / K
@@ -409,6 +436,7 @@ def main():
             "shared_expert_stream": "second stream, concurrent with routing and the routed experts" if Is else None,
             "weights": "int4 qpacked, 256-value blocks, fp16 scales; fp16 activations, fp32 accumulation",
             "replicas": R, "input_batches": S, "graph_replay": not args.no_graph,
+            "steps_per_graph": None if args.no_graph else G,
             "mean_active_experts": float(np.mean(n_act)),
         },
         "roofline": ({
