@@ -17,8 +17,11 @@
 // Host code plus one tiny kernel that writes the published map.
 #include "moe_internal.h"
 
+#include <condition_variable>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <thread>
 #include <vector>
 
 namespace {
@@ -35,6 +38,84 @@ __global__ void publish_map_kernel(int32_t *map, MapArgs m, int E)
     const int e = threadIdx.x;
     if (e < E) map[e] = m.slot[e];
 }
+
+// Host copy of one row into pinned staging, split over a few persistent
+// threads: one thread copying from pageable memory runs at about half the
+// host-to-device link rate, so the link would wait for it.  copy() returns
+// when every part is done; one caller at a time (calls on a table are
+// serialized).
+class CopyPool {
+public:
+    explicit CopyPool(int workers)
+    {
+        for (int i = 0; i < workers; ++i) th_.emplace_back([this, i] { run(i); });
+    }
+    ~CopyPool()
+    {
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (auto &t : th_) t.join();
+    }
+    void copy(uint8_t *dst, const uint8_t *src, size_t n)
+    {
+        const int parts = (int)th_.size() + 1;
+        if (n < kMinSplit || th_.empty()) {
+            std::memcpy(dst, src, n);
+            return;
+        }
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            dst_ = dst;
+            src_ = src;
+            n_ = n;
+            pending_ = (int)th_.size();
+            ++gen_;
+        }
+        cv_.notify_all();
+        part(parts - 1, parts);           // the caller takes the last part
+        std::unique_lock<std::mutex> lk(m_);
+        done_.wait(lk, [this] { return pending_ == 0; });
+    }
+
+private:
+    static constexpr size_t kMinSplit = 256 * 1024;
+
+    void part(int i, int parts)
+    {
+        const size_t chunk = (n_ / parts + 63) / 64 * 64;
+        const size_t b = (size_t)i * chunk, e = b + chunk < n_ ? b + chunk : n_;
+        if (b < e) std::memcpy(dst_ + b, src_ + b, e - b);
+    }
+    void run(int i)
+    {
+        uint64_t seen = 0;
+        std::unique_lock<std::mutex> lk(m_);
+        for (;;) {
+            cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+            if (stop_) return;
+            seen = gen_;
+            lk.unlock();
+            part(i, (int)th_.size() + 1);
+            lk.lock();
+            if (--pending_ == 0) done_.notify_one();
+        }
+    }
+
+    std::vector<std::thread> th_;
+    std::mutex m_;
+    std::condition_variable cv_, done_;
+    uint8_t *dst_ = nullptr;
+    const uint8_t *src_ = nullptr;
+    size_t n_ = 0;
+    int pending_ = 0;
+    uint64_t gen_ = 0;
+    bool stop_ = false;
+};
+
+constexpr int kCopyWorkers = 3;           // plus the calling thread
 
 }  // namespace
 
@@ -58,6 +139,7 @@ struct moe_table {
     bool consumers_recorded = false;
     bool faulted = false;
     moe_table_counters ctr{};
+    CopyPool *pool = nullptr;               // host-side staging copies
 };
 
 namespace {
@@ -78,6 +160,7 @@ void release(moe_table *t)
     if (t->consumers) (void)hipEventDestroy(t->consumers);
     if (t->rows) (void)hipFree(t->rows);
     if (t->map_dev) (void)hipFree(t->map_dev);
+    delete t->pool;
     delete t;
 }
 
@@ -92,7 +175,7 @@ int upload_row(moe_table *t, int e, int slot, hipStream_t s)
         hipError_t err = hipEventSynchronize(t->staging_done[i]);
         if (err != hipSuccess) return table_fail(t, MOE_ERR_FAULTED, "moe_upload_expert_rows (staging)", err);
     }
-    std::memcpy(t->staging[i], t->host + (size_t)e * t->host_stride, t->row_bytes);
+    t->pool->copy(t->staging[i], t->host + (size_t)e * t->host_stride, t->row_bytes);
     hipError_t err = hipMemcpyAsync(t->rows + (size_t)slot * t->row_stride, t->staging[i], t->row_bytes,
                                     hipMemcpyHostToDevice, s);
     if (err == hipSuccess) err = hipEventRecord(t->staging_done[i], s);
@@ -161,6 +244,11 @@ int moe_table_create(moe_table **out, const moe_table_desc *d, void *stream)
     t->row_stride = (rb + 255) / 256 * 256;
     t->host_stride = d->host_row_stride;
     t->host = (const uint8_t *)d->host_source;
+    t->pool = new (std::nothrow) CopyPool(kCopyWorkers);
+    if (!t->pool) {
+        release(t);
+        return moe::fail(MOE_ERR_CAPACITY, "moe_table_create: out of host memory");
+    }
     t->slot_of.assign(t->E, -1);
     t->expert_in.assign(t->nslots, -1);
     t->last_use.assign(t->E, 0);
