@@ -475,6 +475,22 @@ def main():
     print(json.dumps(out))
 
 
+def pinned_h2d_gbs(torch, dev, nbytes=256 << 20, reps=8):
+    """Host-to-device rate from a pinned host buffer (hipMemcpyAsync of 256 MiB, HIP events): the
+    link ceiling the miss uploads are judged against."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def run_stack(args, torch, dev):
     """Decode with partial residency: each layer keeps `resident` of its E experts published in a
     resident expert table; a step routes each layer, brings the active expert list to the host,
@@ -501,7 +517,7 @@ def run_stack(args, torch, dev):
         bias = torch.from_numpy(synth.make_zipf_bias(cfg, layer=l)).to(dev) if cfg.zipf_s else None
         if Is:
             shared.append([torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in synth.make_shared(cfg, layer=l)])
-        tab = ResidentExpertTable(host[l], H, I, cfg.resident, spare, staging_rows=2)
+        tab = ResidentExpertTable(host[l], H, I, cfg.resident, spare, staging_rows=2, top_k=k, max_tokens=T)
         rows_dev, stride, _ = tab.device()
         lay = RoutedExpertLayer(H, I, E, k, torch.empty((1, stride), dtype=torch.uint8, device=dev), wr, bias,
                                 max_T=T, device=dev)
@@ -526,16 +542,17 @@ def run_stack(args, torch, dev):
                 Wsg, Wsu, Wsd, wg = shared[l]
                 B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes)
             active = lay.active_experts()
-            tab.prepare(active)
+            tab.prepare(active)             # copies on the table's copy stream; this stream waits
+            lease = tab.acquire()
             if timed_ffn:
                 ev[0].record()
-            lay.ffn(x, table=tab)
+            lay.ffn(x, lease=lease)
             if timed_ffn:
                 ev[1].record()
                 ev[1].synchronize()
                 ffn_us[0] += ev[0].elapsed_time(ev[1]) * 1e3
                 ffn_bytes[0] += len(active) * row_bytes
-            tab.record_consumers()
+            tab.release(lease)
             lay.combine(T, y, shared_out=sh_out, shared_gate=sh_gate)
 
     for s in range(args.warmup):
@@ -556,6 +573,9 @@ def run_stack(args, torch, dev):
         step(s, timed_ffn=True)
     torch.cuda.synchronize()
     ffn_gbs = ffn_bytes[0] / (ffn_us[0] * 1e-6) / 1e9
+    for lay in layers:
+        lay.check_status()
+    h2d_ceiling = pinned_h2d_gbs(torch, dev)
     out = {
         "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode)",
         "value": T * K / elapsed,
@@ -575,6 +595,8 @@ def run_stack(args, torch, dev):
             "evictions_per_step": delta["evictions"] / K,
             "staging_waits": delta["staging_waits"],
             "expert_d2h_bytes": delta["expert_d2h_bytes"], "host_writes": delta["host_writes"],
+            "pinned_h2d_ceiling_gbs": h2d_ceiling,
+            "h2d_frac_of_pinned_ceiling": delta["h2d_bytes"] / elapsed / 1e9 / h2d_ceiling,
         },
         "ffn_hbm": {"achieved_gbs": ffn_gbs, "frac": ffn_gbs / HBM_PEAK_GBS,
                     "timing": f"HIP events around the expert FFN of {n_ffn} steps x {L} layers"},

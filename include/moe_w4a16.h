@@ -75,6 +75,7 @@ enum moe_status {
     MOE_ERR_HIP = 5,             /* a HIP runtime call or kernel launch failed */
     MOE_ERR_FAULTED = 6,         /* expert table faulted by a failure after publication */
     MOE_ERR_ABSENT_EXPERT = 7,   /* a routed expert has no published device row */
+    MOE_ERR_SOURCE = 8,          /* expert table: host source failed its identity or layout check */
 };
 
 #define MOE_MAX_EXPERTS 64
@@ -161,35 +162,33 @@ int moe_route_exact(const void *x_dev, const void *w_router_dev, const float *bi
  * per-block FP16 scale is applied to the FP32 partial sum of each block, so
  * no expanded weight matrix is ever stored. */
 
-/* Kernel family of the three calls above (process-wide; MOE_FFN_PATH_AUTO by
- * default).  Both families compute the same sums per scale block in FP32 and
- * round at the same points, so their outputs agree to FP32 summation order.
+/* mode: kernel family of the call (a per-call choice; it never changes the
+ * result beyond FP32 summation order).  Both families compute the same sums
+ * per scale block in FP32 and round at the same points.
  *   MOE_FFN_PATH_STREAM: one wavefront per 16 pairs x 16 rows of an expert,
  *     streaming each weight tile once per 16 pairs (built for decode batches,
  *     bound by HBM);
  *   MOE_FFN_PATH_GEMM: a grouped GEMM over 128-pair tiles of each expert
  *     (built for prefill batches, bound by the matrix cores);
  *   MOE_FFN_PATH_AUTO: the GEMM when T*k >= 64*E, else the streaming kernels.
- * Returns MOE_OK, or MOE_ERR_INVALID_ARG for an unknown value.  Not
- * synchronized with calls running on other threads. */
+ * Any other value returns MOE_ERR_INVALID_ARG. */
 enum moe_ffn_path { MOE_FFN_PATH_AUTO = 0, MOE_FFN_PATH_STREAM = 1, MOE_FFN_PATH_GEMM = 2 };
-int moe_set_ffn_path(int path);
 
 int moe_w4a16_gateup(const void *x_dev, int T, int H, int I, int E, int k,
                      const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                      const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
                      const int32_t *active_list_dev, const int32_t *n_active_dev,
-                     void *h_dev, int32_t *status_dev, void *stream);
+                     void *h_dev, int32_t *status_dev, int mode, void *stream);
 int moe_w4a16_down(int T, int H, int I, int E, int k,
                    const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                    const int32_t *expert_offsets_dev, const int32_t *active_list_dev,
                    const int32_t *n_active_dev, const void *h_dev, float *pair_out_dev,
-                   int32_t *status_dev, void *stream);
+                   int32_t *status_dev, int mode, void *stream);
 int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
                          const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                          const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
                          const int32_t *active_list_dev, const int32_t *n_active_dev,
-                         void *h_dev, float *pair_out_dev, int32_t *status_dev, void *stream);
+                         void *h_dev, float *pair_out_dev, int32_t *status_dev, int mode, void *stream);
 
 /* ------------------------------------------------------------ shared expert
  * moe_shared_ffn: the FP16 shared expert of a layer that has one (non-routed
@@ -223,75 +222,113 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
  * publication edition v1", section "Immutable cache — the scope of ADR
  * 0009"):
  *   - the host source holds every expert's qpacked row; it belongs to the
- *     caller, must stay unchanged and outlive the table, and is only read;
- *   - the table owns nslots = capacity + spare_rows device rows (one
- *     allocation, row_stride = row bytes rounded up to 256), a device map
- *     int32 [E] (slot of each expert, -1 = no published row; pass it as
- *     slot_map_dev to the FFN calls) and staging_rows pinned staging buffers;
- *     nothing else is allocated after moe_table_create;
- *   - a miss is copied host source -> pinned staging (host memcpy, after the
- *     staging buffer's previous copy has finished) -> a spare device row
- *     (hipMemcpyAsync on the caller's stream); the new map is published on
- *     the same stream after the copies, so kernels enqueued later see the new
- *     rows and never a partly written one;
- *   - misses go to spare rows (lowest slot first); when there are too few,
- *     least recently used published experts outside the current step give
- *     up their rows first; after the upload, while more than `capacity`
- *     experts are published, the least recently used experts outside the
- *     current step lose their device copy (ties go to the lower expert id);
- *     a row is refilled only after the consumer event last recorded with
- *     moe_table_record_consumers (kernels that may still read it);
+ *     caller, must stay unchanged and outlive the table, and is only read.
+ *     Creation takes a 64-bit digest of every row (its identity; compared
+ *     with desc->row_digests when given) and checks that every FP16 scale is
+ *     finite (its layout); moe_table_verify_source re-checks the digests;
+ *   - the table owns capacity + spare_rows device rows (one allocation,
+ *     row_stride = row bytes rounded up to 256), a ring of 4 device maps
+ *     (int32 [E]: slot of each expert, -1 = no row; one per recent
+ *     generation), staging_rows pinned staging buffers of one row, a copy
+ *     stream (default priority) and a fixed pool of events; nothing else is
+ *     allocated after moe_table_create;
+ *   - a generation is one complete published map.  A consumer captures the
+ *     current generation with moe_table_acquire (a lease: that generation's
+ *     map and the rows it names stay untouched) and ends it with
+ *     moe_table_release on the stream of its last reading kernel;
+ *   - moe_upload_expert_rows is one miss transaction (transactions are
+ *     serialized: a table is used by one host thread at a time).  Each miss
+ *     goes host source -> pinned staging (a host memcpy, after that staging
+ *     buffer's previous copy has retired) -> a spare row (hipMemcpyAsync on
+ *     the copy stream); a spare row is one that neither the current
+ *     generation nor any generation with an open lease names, and the copy
+ *     stream first waits for the released consumers of every generation that
+ *     last named it.  After the copies the next generation's map is written
+ *     (same stream) and becomes current: kernels ordered after it see the new
+ *     rows, never a partly written one, while readers of older generations
+ *     keep theirs;
+ *   - the next generation keeps at most `capacity` experts published: least
+ *     recently used experts outside the current step lose their device copy
+ *     (ties go to the lower expert id);
  *   - no expert bytes ever move device -> host and the host source is never
- *     written (counters expert_d2h_bytes and host_writes stay 0).
+ *     written (counter expert_d2h_bytes stays 0; host_writes counts rows that
+ *     moe_table_verify_source found changed).
+ * Failures: before publication (a copy, a wait, the map write) the call
+ * returns MOE_ERR_HIP and the previous generation stays current and intact;
+ * an ambiguous failure after publication faults the table (every later call
+ * returns MOE_ERR_FAULTED).  MOE_ERR_CAPACITY from an upload means the spare
+ * rows are held by open leases (or the step exceeds max_tokens).
  * Use per step: bring the active expert list to the host, moe_table_misses,
- * moe_upload_expert_rows(misses), the FFN calls with moe_table_device's rows
- * and map, then moe_table_record_consumers on the stream of those calls.
- * A table is used by one host thread at a time.
- * Errors: MOE_ERR_CAPACITY when create cannot allocate or an upload has
- * more misses than spare rows plus rows of experts outside the step;
- * MOE_ERR_FAULTED when a HIP call failed after
- * copies were enqueued (the table then refuses further uploads). */
+ * moe_upload_expert_rows(misses, stream), moe_table_acquire(stream), the FFN
+ * calls with the lease's rows and map, moe_table_release(lease, stream). */
 typedef struct moe_table moe_table;
 
 typedef struct {
     int E, H, I;                       /* experts, hidden size, expert intermediate size */
     int capacity;                      /* experts published between steps (1..E) */
-    int spare_rows;                    /* extra device rows that receive misses */
+    int spare_rows;                    /* extra device rows that receive misses (see below) */
     int staging_rows;                  /* pinned staging buffers of one row each (1..16) */
+    int top_k;                         /* experts per token of the layer (1..min(E, 8)) */
+    int max_tokens;                    /* largest step (tokens) the table serves (1..65536) */
     const void *host_source;           /* host: expert e's row at host_source + e*host_row_stride */
     size_t host_row_stride;            /* >= moe_expert_row_bytes(H, I) */
     const int32_t *initial_resident;   /* host: `capacity` distinct expert ids, or NULL for 0..capacity-1 */
+    const uint64_t *row_digests;       /* host: E expected moe_row_digest values, or NULL */
 } moe_table_desc;
+/* Creation rejects (MOE_ERR_CAPACITY) spare_rows below
+ * min(E - capacity, A + max(0, A - capacity)) with A = min(E, max_tokens *
+ * top_k): after a step at most max(capacity, A) experts stay published, and
+ * the next step's A misses must find rows outside that set. */
 
 typedef struct {
     uint64_t steps;                    /* moe_table_misses calls */
     uint64_t hits, misses;             /* active experts found published / not */
     uint64_t evictions;                /* device copies dropped */
     uint64_t h2d_bytes;                /* expert bytes copied host -> device after creation */
-    uint64_t staging_waits;            /* uploads that waited for a staging buffer */
+    uint64_t staging_waits;            /* copies that waited for a staging buffer */
     uint64_t expert_d2h_bytes;         /* always 0 */
-    uint64_t host_writes;              /* always 0 */
+    uint64_t host_writes;              /* host rows found changed by moe_table_verify_source */
+    uint64_t generation;               /* current generation (1 after creation) */
+    uint64_t open_leases;              /* leases acquired and not released */
+    uint64_t failed_uploads;           /* transactions that failed before publication */
 } moe_table_counters;
 
-/* Creates the table and uploads the initial residents (synchronizes
- * `stream` before returning).  *out receives the table. */
+typedef struct {
+    uint64_t generation;               /* the captured generation */
+    const void *rows_dev;              /* device rows (slot s at rows_dev + s*row_stride) */
+    size_t row_stride;
+    const int32_t *slot_map_dev;       /* that generation's device map, int32 [E] */
+} moe_table_lease;
+
+/* Digest of n host bytes (the identity moe_table_create checks). */
+uint64_t moe_row_digest(const void *p, size_t n);
+/* Creates the table, validates the host source, uploads the initial
+ * residents and publishes generation 1 (waits for it).  *out receives the
+ * table.  `stream` is unused (the table has its own copy stream). */
 int moe_table_create(moe_table **out, const moe_table_desc *desc, void *stream);
-/* Waits for the device to finish with the table, then frees it (NULL is a no-op). */
+/* Waits for the table's copies and for the consumers of released leases,
+ * then frees it (NULL is a no-op).  Leases must have been released. */
 void moe_table_destroy(moe_table *table);
-/* Device rows, their stride and the published device map. */
+/* Device rows, their stride and the current generation's map (no lease). */
 int moe_table_device(const moe_table *table, const void **rows_dev, size_t *row_stride,
                      const int32_t **slot_map_dev);
 /* Starts a step: records the active experts (host array of n ids; duplicates
  * count once) as used now and writes those without a published row to
  * miss_out (capacity n), their number to *n_miss. */
 int moe_table_misses(moe_table *table, const int32_t *active_host, int n, int32_t *miss_out, int *n_miss);
-/* Uploads the n missing experts into spare rows and publishes the new map,
- * both on `stream`.  The ids must not be published already. */
+/* One miss transaction for the n experts (none may be published already);
+ * `stream` (a consumer stream, or NULL) is ordered after the publication.
+ * n = 0 publishes nothing. */
 int moe_upload_expert_rows(moe_table *table, const int32_t *expert_ids, int n, void *stream);
-/* Records, on `stream`, the point after which the rows read so far may be refilled. */
-int moe_table_record_consumers(moe_table *table, void *stream);
+/* Captures the current generation; `stream` is ordered after its publication. */
+int moe_table_acquire(moe_table *table, void *stream, moe_table_lease *lease);
+/* Ends a lease; its consumers are the work enqueued on `stream` so far. */
+int moe_table_release(moe_table *table, const moe_table_lease *lease, void *stream);
+/* Re-checks every host row against its digest from creation
+ * (MOE_ERR_SOURCE if any changed). */
+int moe_table_verify_source(moe_table *table);
 int moe_table_stats(const moe_table *table, moe_table_counters *out);
-/* Host copy of the published map (E entries, slot or -1). */
+/* Host copy of the current generation's map (E entries, slot or -1). */
 int moe_table_published(const moe_table *table, int32_t *slot_map_host);
 
 /* ------------------------------------------------------------ combine

@@ -4,7 +4,7 @@ oracle (routing bit for bit, h / expert outputs / y within tolerance)."""
 import numpy as np
 
 import oracle
-from parity_util import STAGE_FLOOR, assert_close_rows, error_report, f16_to_f64
+from parity_util import STAGE_FLOOR, assert_close_rows, assert_h_close, error_report, f16_to_f64
 from w4a16_routed_expert_amd import synth
 
 _ROWS = {}
@@ -16,26 +16,41 @@ def rows_of(name):
     return _ROWS[name]
 
 
-def gpu_layer(cfg, rows_np, wr, x, bias=None, slot_map=None, rows_dev=None):
+def gpu_layer(cfg, rows_np, wr, x, bias=None, slot_map=None, rows_dev=None, mode=None, shared=None):
+    """One layer call through the C ABI; mode: None (automatic) or a B.MOE_FFN_PATH_* value;
+    shared: None or the FP16 shared expert (Wsg, Wsu, Wsd, wgate) as numpy arrays, run on a
+    second stream beside the routed experts."""
     import torch
-    from w4a16_routed_expert_amd.layer import RoutedExpertLayer
+    from w4a16_routed_expert_amd import binding as B
+    from w4a16_routed_expert_amd.layer import RoutedExpertLayer, SharedExpert
     dev = torch.device("cuda:0")
     T = x.shape[0]
+    sh = None
+    if shared is not None:
+        sh = SharedExpert(*(torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in shared), max_T=max(T, 1),
+                          device=dev)
     if rows_dev is None:
         rows_dev = torch.from_numpy(rows_np).to(dev)
     lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, rows_dev, torch.from_numpy(wr).to(dev),
                             None if bias is None else torch.from_numpy(bias).to(dev),
                             None if slot_map is None else torch.from_numpy(slot_map).to(dev),
                             max_T=max(T, 1), device=dev)
-    y = lay.forward(torch.from_numpy(x).to(dev))
+    y = lay.forward(torch.from_numpy(x).to(dev), mode=B.MOE_FFN_PATH_AUTO if mode is None else mode, shared=sh)
     torch.cuda.synchronize()
     n = T * cfg.k
     na = int(lay.n_active.cpu()[0]) if T else 0
-    return dict(y=y.cpu().numpy(), logits=lay.logits.cpu().numpy()[:T], ids=lay.topk_ids.cpu().numpy()[:T],
+    extra = {}
+    if sh is not None:
+        Is = shared[0].shape[0]
+        extra = dict(shared_os=sh.out.cpu().numpy()[:T].astype(np.float64),
+                     shared_sigma=sh.gate.cpu().numpy()[:T].astype(np.float64),
+                     shared_hs=sh.ws[:T * Is * 2].cpu().numpy().view(np.uint16).reshape(T, Is).copy(),
+                     shared=shared)
+    return dict(**extra, y=y.cpu().numpy(), logits=lay.logits.cpu().numpy()[:T], ids=lay.topk_ids.cpu().numpy()[:T],
                 w=lay.topk_w.cpu().numpy()[:T], offsets=lay.expert_offsets.cpu().numpy(),
                 sorted_pairs=lay.sorted_pairs.cpu().numpy()[:n], pair_pos=lay.pair_pos.cpu().numpy()[:n],
                 active=lay.active_list.cpu().numpy(), n_active=na, h=lay.h.cpu().numpy()[:n],
-                pair_out=lay.pair_out.cpu().numpy()[:n], status=int(lay.status.cpu()[0]), layer=lay)
+                pair_out=lay.pair_out.cpu().numpy()[:n], status=int(lay.status.cpu()[0]), layer=lay, x=x)
 
 
 def stagewise(cfg, got, rows):
@@ -51,7 +66,7 @@ def stagewise(cfg, got, rows):
         _, _, Wd = oracle.dequant_expert(rows[e], cfg.H, cfg.I)
         lo, hi = off[e], off[e + 1]
         o[sp[lo:hi]] = f16_to_f64(got["h"][lo:hi].view(np.uint16)) @ Wd.T
-    return o, oracle.combine(o, got["w"].astype(np.float64))
+    return o, oracle.combine(o, got["w"].astype(np.float64), got.get("shared_os"), got.get("shared_sigma"))
 
 
 def check_full(cfg, got, ref, what, rows=None):
@@ -68,7 +83,8 @@ def check_full(cfg, got, ref, what, rows=None):
     assert np.all(got["active"][ref["n_active"]:] == -1)
     if ref.get("h") is not None:
         # grouped position pos holds pair sorted_pairs[pos]
-        assert_close_rows(got["h"].view(np.uint16), ref["h"][ref["sorted_pairs"]], f"{what}: h")
+        eq = assert_h_close(got["h"].view(np.uint16), ref["h"][ref["sorted_pairs"]], f"{what}: h")
+        print(f"{what}: h bit-identical fraction {eq:.5f}")
     # Per-pair expert outputs are compared normwise (2e-3 of each pair's largest
     # output): a 1-ulp flip of a large FP16 h (ulp 2^-8 for h in [4, 8)) times a
     # large down weight moves single outputs by ~1e-4, which an elementwise test
@@ -82,7 +98,70 @@ def check_full(cfg, got, ref, what, rows=None):
         assert_close_rows(got["pair_out"].astype(np.float64), o_st[got["sorted_pairs"]],
                           f"{what}: expert outputs from the GPU's h", floor=STAGE_FLOOR)
         assert_close_rows(got["y"].view(np.uint16), y_st, f"{what}: y from the GPU's h", floor=STAGE_FLOOR)
+    if ref.get("shared_os") is not None and got.get("shared_os") is not None:
+        check_shared_stages(got, ref, got["shared"], f"{what}: shared expert")
     rel, norm = error_report(got["y"].view(np.uint16), ref["y"])
     print(f"{what}: max rel err (no floor) {rel:.3g}, max normwise {norm:.3g}")
 
 
+def oracle_shared_h(x, shared, workers=None):
+    """The oracle's FP16 shared-expert activations hs [T][Is] (oracle.swiglu_dense on the
+    FP16 weights read exactly as doubles, one token per call, on host threads)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    Wsg, Wsu, Wsd, _ = (f16_to_f64(np.asarray(m).view(np.uint16)) for m in shared)
+    T = x.shape[0]
+    if workers is None:
+        workers = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        hs = list(ex.map(lambda t: oracle.swiglu_dense(Wsg, Wsu, Wsd, x[t])[0], range(T)))
+    return np.stack(hs) if T else np.zeros((0, Wsg.shape[0]), np.uint16)
+
+
+def check_shared_stages(got, ref, shared, what):
+    """Shared expert stage by stage: hs within one FP16 ulp of the oracle's; shared_out
+    against the FP16 down weights applied to the GPU's own hs (elementwise, stage floor);
+    the gate within 1e-6; shared_out against the oracle normwise."""
+    x = got["x"]
+    hs_ref = oracle_shared_h(x, shared)
+    eq = assert_h_close(got["shared_hs"], hs_ref, f"{what}: hs")
+    Wsd = f16_to_f64(np.asarray(shared[2]).view(np.uint16))
+    os_st = f16_to_f64(got["shared_hs"]) @ Wsd.T
+    assert_close_rows(got["shared_os"], os_st, f"{what}: shared_out from the GPU's hs", floor=STAGE_FLOOR)
+    assert_close_rows(got["shared_os"], ref["shared_os"], f"{what}: shared_out", floor=1.0)
+    assert np.allclose(got["shared_sigma"], ref["shared_sigma"], rtol=0, atol=1e-6), f"{what}: gate"
+    print(f"{what}: hs bit-identical fraction {eq:.5f}")
+
+
+
+
+def oracle_tokens(x, wr, rows, cfg, bias=None, shared=None, want_h=False, chunk=8, workers=None):
+    """oracle.layer on a set of tokens, split into chunks run on host threads.
+
+    Every token's route, expert outputs and y depend on that token only, so the
+    per-token results equal one oracle call on all of them (the grouping
+    fields, which depend on the whole batch, are dropped).  The oracle is plain
+    C called through ctypes, which releases the GIL."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    T = x.shape[0]
+    if workers is None:
+        workers = max(1, min(16, os.cpu_count() or 1))
+    parts = [(i, min(T, i + chunk)) for i in range(0, T, chunk)]
+
+    def run(p):
+        a, b = p
+        sh = None if shared is None else shared
+        return oracle.layer(x[a:b], wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, bias=bias, shared=sh, want_h=want_h)
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(run, parts))
+    out = {}
+    for key in ("y", "logits", "ids", "w", "o"):
+        out[key] = np.concatenate([r[key] for r in res], axis=0)
+    if want_h:
+        out["h"] = np.concatenate([r["h"] for r in res], axis=0)
+    if shared is not None:
+        out["shared_os"] = np.concatenate([r["shared_os"] for r in res], axis=0)
+        out["shared_sigma"] = np.concatenate([r["shared_sigma"] for r in res], axis=0)
+    return out

@@ -94,11 +94,7 @@ def test_streaming_odd_shapes(H, I):
     T = 40
     rows, wr, x = synth.make_expert_rows(cfg), synth.make_router(cfg), synth.make_x(cfg, T)
     ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
-    B.moe_set_ffn_path(B.MOE_FFN_PATH_STREAM)
-    try:
-        got = gpu_layer(cfg, rows, wr, x)
-    finally:
-        B.moe_set_ffn_path(B.MOE_FFN_PATH_AUTO)
+    got = gpu_layer(cfg, rows, wr, x, mode=B.MOE_FFN_PATH_STREAM)
     check_full(cfg, got, ref, f"streaming H={H} I={I}", rows=rows)
 
 
@@ -111,11 +107,7 @@ def test_expert_count_edges(E, k, H, I, T, path):
     cfg = synth.LayerConfig(f"edge{E}x{k}", 10, E=E, k=k, H=H, I=I, batches=(T,), resident=E)
     rows, wr, x = synth.make_expert_rows(cfg), synth.make_router(cfg), synth.make_x(cfg, T)
     ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
-    B.moe_set_ffn_path(B.MOE_FFN_PATH_STREAM if path == "stream" else B.MOE_FFN_PATH_GEMM)
-    try:
-        got = gpu_layer(cfg, rows, wr, x)
-    finally:
-        B.moe_set_ffn_path(B.MOE_FFN_PATH_AUTO)
+    got = gpu_layer(cfg, rows, wr, x, mode=B.MOE_FFN_PATH_STREAM if path == "stream" else B.MOE_FFN_PATH_GEMM)
     check_full(cfg, got, ref, f"{path} E={E} k={k}", rows=rows)
 
 
@@ -158,27 +150,45 @@ def test_olmoe_zipf_biased_layer():
     check_full(cfg, gpu_layer(cfg, rows, wr, x, bias=bias), ref, "olmoe zipf T=32", rows=rows)
 
 
-def test_prefill_batch_sampled_tokens():
-    # 4096 tokens: every token's routing depends on that token only, so the
-    # oracle of a sampled subset gives those tokens' ids, weights and outputs.
+def test_prefill_batch_full_routing_and_item_edges():
+    # 4096 tokens, the grouped-GEMM path.  The oracle routes and groups the
+    # whole batch (logits bit for bit, top-k, softmax, the stable grouping);
+    # expert outputs are checked on the tokens of the first and the last pair
+    # of every expert's first and last 128-pair item (every token's output
+    # depends on that token only).
+    from layer_util import oracle_tokens
+    from parity_util import assert_h_close
     cfg = synth.CONFIGS["prefill"]
     T = 4096
     rows, wr, x = rows_of("olmoe"), synth.make_router(cfg), synth.make_x(cfg, T)
     got = gpu_layer(cfg, rows, wr, x)
     k, E = cfg.k, cfg.E
-    ids = got["ids"]
-    # grouping properties on the full batch
-    sp = got["sorted_pairs"]
-    assert np.array_equal(np.sort(sp), np.arange(T * k))
-    assert np.array_equal(got["pair_pos"][sp], np.arange(T * k))
-    flat = ids.reshape(-1)
-    assert np.array_equal(got["offsets"], np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
-    key = flat[sp].astype(np.int64) * (T * k) + sp
-    assert np.all(np.diff(key) > 0), "grouping is not sorted by (expert, pair)"
-    assert np.all(np.sort(ids, axis=1)[:, 1:] != np.sort(ids, axis=1)[:, :-1])
-    sample = np.random.default_rng(0).choice(T, 24, replace=False)
-    ref = oracle.layer(x[sample], wr, rows, cfg.H, cfg.I, E, k)
-    assert np.array_equal(ids[sample], ref["ids"])
-    assert np.array_equal(got["logits"][sample].view(np.uint32), ref["logits"].view(np.uint32))
-    assert np.allclose(got["w"][sample], ref["w"], rtol=1e-5, atol=1e-7)
-    assert_close_rows(got["y"][sample].view(np.uint16), ref["y"], "prefill sampled y")
+    logits = oracle.router_logits(x, wr)
+    assert np.array_equal(got["logits"].view(np.uint32), logits.view(np.uint32)), "prefill logits not bit-exact"
+    ids, w = oracle.topk_softmax(logits, k)
+    assert np.array_equal(got["ids"], ids), "prefill expert ids differ"
+    assert np.allclose(got["w"], w, rtol=1e-5, atol=1e-7), "prefill routing weights differ"
+    grp = oracle.group(ids, E)
+    for key in ("offsets", "sorted_pairs", "pair_pos"):
+        assert np.array_equal(got[key], grp[key]), f"prefill grouping: {key} differs"
+    assert got["n_active"] == grp["n_active"]
+    assert np.array_equal(got["active"][:grp["n_active"]], grp["active"])
+    off, sp = grp["offsets"], grp["sorted_pairs"]
+    pos = set()
+    for e in range(E):
+        n = off[e + 1] - off[e]
+        if n == 0:
+            continue
+        last_item = 128 * ((n - 1) // 128)
+        for q in (0, min(127, n - 1), last_item, n - 1):
+            pos.add(int(off[e] + q))
+    toks = np.array(sorted({int(sp[p]) // k for p in pos}))
+    ref = oracle_tokens(x[toks], wr, rows, cfg, want_h=True)
+    assert np.array_equal(got["ids"][toks], ref["ids"])
+    assert_close_rows(got["y"][toks].view(np.uint16), ref["y"], "prefill item-edge tokens: y")
+    pairs = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    gpu_h = got["h"][got["pair_pos"][pairs]].view(np.uint16)
+    eq = assert_h_close(gpu_h, ref["h"], "prefill item-edge tokens: h")
+    o_gpu = got["pair_out"][got["pair_pos"][pairs]].astype(np.float64)
+    assert_close_rows(o_gpu, ref["o"], "prefill item-edge tokens: expert outputs", floor=1.0)
+    print(f"prefill: {len(toks)} item-edge tokens, h bit-identical {eq:.5f}")

@@ -1,9 +1,11 @@
 """GPU parity of the FP16 shared expert (moe_shared_ffn) and of the layer with it.
 
-The shared expert's outputs are compared with the oracle per token row
-(normwise, like the routed experts' per-pair outputs: its FP16 activation hs is
-rounded, so single outputs move with one-ulp flips of hs); the sigmoid gate to
-1e-6 absolute; the layer output y with the elementwise rule of parity_util.
+The shared expert is checked stage by stage: its FP16 activation hs within one
+FP16 ulp of the oracle's (parity_util.assert_h_close), its output against the
+FP16 down weights applied to the GPU's own hs (elementwise, the stage floor)
+and against the oracle per token row (normwise: single outputs move with
+one-ulp flips of hs); the sigmoid gate to 1e-6 absolute; the layer output y
+with the elementwise rule of parity_util.
 """
 import numpy as np
 import pytest
@@ -35,15 +37,18 @@ def run_shared(x, shared):
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
     B.moe_shared_ffn(xd, Wsg, Wsu, Wsd, wg, T, H, Is, out, sig, ws, nb)
     torch.cuda.synchronize()
-    return out.cpu().numpy()[:T], sig.cpu().numpy()[:T]
+    hs = ws[:T * Is * 2].cpu().numpy().view(np.uint16).reshape(T, Is).copy()    # hs leads the workspace
+    return out.cpu().numpy()[:T], sig.cpu().numpy()[:T], hs
 
 
 def check_shared(x, shared, what):
+    from layer_util import check_shared_stages
     os_ref, sig_ref = oracle.shared_ffn(x, *shared)
-    os_gpu, sig_gpu = run_shared(x, shared)
+    os_gpu, sig_gpu, hs = run_shared(x, shared)
     assert np.all(np.isfinite(os_gpu)) and np.all(np.isfinite(sig_gpu)), f"{what}: unwritten outputs"
-    assert_close_rows(os_gpu.astype(np.float64), os_ref, f"{what}: shared_out", floor=1.0)
-    assert np.allclose(sig_gpu, sig_ref, rtol=0, atol=1e-6), f"{what}: shared gate"
+    check_shared_stages(dict(x=x, shared_hs=hs, shared_os=os_gpu.astype(np.float64),
+                             shared_sigma=sig_gpu.astype(np.float64)),
+                        dict(shared_os=os_ref, shared_sigma=sig_ref), shared, what)
 
 
 @pytest.mark.parametrize("T", [1, 5, 16, 20, 33, 70])
@@ -74,34 +79,23 @@ def test_shared_run_to_run_bit_identical():
     # chunk partial sums meet in a fixed order
     cfg = synth.CONFIGS["qwen"]
     x, shared = synth.make_x(cfg, 16, step=6), synth.make_shared(cfg)
-    a_out, a_sig = run_shared(x, shared)
-    b_out, b_sig = run_shared(x, shared)
+    a_out, a_sig, _ = run_shared(x, shared)
+    b_out, b_sig, _ = run_shared(x, shared)
     assert np.array_equal(a_out.view(np.uint32), b_out.view(np.uint32))
     assert np.array_equal(a_sig.view(np.uint32), b_sig.view(np.uint32))
 
 
-def test_qwen_layer_with_shared_expert():
-    from w4a16_routed_expert_amd import binding as B
-    from w4a16_routed_expert_amd.layer import RoutedExpertLayer
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_qwen_layer_with_shared_expert(T):
+    # The whole Qwen-shaped layer: routed experts, the FP16 shared expert on a
+    # second stream, the gated combine; every stage against the oracle.
+    from layer_util import check_full, gpu_layer, rows_of
     cfg = synth.CONFIGS["qwen"]
-    T = 16
-    dev = torch.device("cuda:0")
-    rows, wr, x = synth.make_expert_rows(cfg), synth.make_router(cfg), synth.make_x(cfg, T, step=4)
+    rows, wr, x = rows_of("qwen"), synth.make_router(cfg), synth.make_x(cfg, T, step=4)
     shared = synth.make_shared(cfg)
-    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, shared=shared)
-    lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev), torch.from_numpy(wr).to(dev),
-                            max_T=T, device=dev)
-    xd = torch.from_numpy(x).to(dev)
-    Wsg, Wsu, Wsd, wg = (torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in shared)
-    os_ = torch.empty((T, cfg.H), dtype=torch.float32, device=dev)
-    sig = torch.empty(T, dtype=torch.float32, device=dev)
-    nb = B.moe_shared_ffn_workspace_size(T, cfg.H, cfg.shared_I)
-    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-    B.moe_shared_ffn(xd, Wsg, Wsu, Wsd, wg, T, cfg.H, cfg.shared_I, os_, sig, ws, nb)
-    y = lay.forward(xd, shared_out=os_, shared_gate=sig)
-    torch.cuda.synchronize()
-    assert np.array_equal(lay.topk_ids.cpu().numpy()[:T], ref["ids"])
-    assert_close_rows(y.cpu().numpy().view(np.uint16), ref["y"], "qwen layer with shared expert: y")
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, shared=shared, want_h=True)
+    got = gpu_layer(cfg, rows, wr, x, shared=shared)
+    check_full(cfg, got, ref, f"qwen layer + shared T={T}", rows=rows)
 
 
 def test_concurrent_shared_expert_equals_sequential():

@@ -1,8 +1,12 @@
 """GPU tests of the resident expert table (moe_table_*): misses travel host ->
-pinned staging -> spare device rows, are published after the copies, least
-recently used experts lose their copy above capacity, and the layer's output
-with partial residency is bit-identical to the output with every expert
-resident (same kernels, same bytes).
+pinned staging -> spare device rows on the table's copy stream, each
+transaction publishes a new generation after its copies, least recently used
+experts lose their copy above capacity, an open lease keeps the rows its
+generation names, and the layer's output with partial residency is
+bit-identical to the output with every expert resident (same kernels, same
+bytes) and matches the oracle, over consecutive layers of the Zipf-biased
+OLMoE-shaped stack and on the Qwen-shaped layer with its shared expert.
+The state machine itself is also tested without a GPU (test_table_cpu.py).
 """
 import ctypes
 
@@ -28,9 +32,9 @@ def read_device(addr: int, nbytes: int) -> np.ndarray:
 
 
 class LruModel:
-    """The table's policy restated in plain Python: spare rows lowest index first; above
-    capacity, the least recently used experts outside the current step lose their copy
-    (ties: lower expert id)."""
+    """The table's policy restated in plain Python: misses take the lowest rows that the
+    current generation does not name (no leases are held here); above capacity, the least
+    recently used experts outside the current step lose their copy (ties: lower expert id)."""
 
     def __init__(self, E, capacity, spare, initial):
         self.E, self.c = E, capacity
@@ -64,9 +68,8 @@ class LruModel:
         return True
 
     def upload(self, misses):
-        while sum(e < 0 for e in self.expert_in) < len(misses):
-            assert self.evict_one()
         spare = [s for s, e in enumerate(self.expert_in) if e < 0]
+        assert len(spare) >= len(misses)
         for e, s in zip(misses, spare):
             self.slot_of[e] = s
             self.expert_in[s] = e
@@ -80,68 +83,117 @@ class LruModel:
         return m
 
 
-def make_table(cfg, rows, capacity, spare, initial=None, staging=2):
+def make_table(cfg, rows, capacity, spare, max_tokens, initial=None, staging=2, digests=None):
     from w4a16_routed_expert_amd.layer import ResidentExpertTable
-    return ResidentExpertTable(rows, cfg.H, cfg.I, capacity, spare, staging, initial)
+    return ResidentExpertTable(rows, cfg.H, cfg.I, capacity, spare, staging, initial, top_k=cfg.k,
+                               max_tokens=max_tokens, row_digests=digests)
 
 
 def test_uploads_publish_lru_and_bytes():
     cfg = synth.CONFIGS["tiny"]
     rows = synth.make_expert_rows(cfg)
     digest = rows.sum(dtype=np.uint64), rows.tobytes()[:4096]
-    tab = make_table(cfg, rows, capacity=3, spare=2)
-    model = LruModel(cfg.E, 3, 2, [0, 1, 2])       # 5 rows: a 5-expert step evicts before uploading
+    # steps of up to 3 tokens x top-2: 5 spare rows (every expert fits)
+    from w4a16_routed_expert_amd import binding as B
+    tab = make_table(cfg, rows, capacity=3, spare=5, max_tokens=3,
+                     digests=[B.moe_row_digest(rows[e]) for e in range(cfg.E)])
+    model = LruModel(cfg.E, 3, 5, [0, 1, 2])
     assert np.array_equal(tab.published(), model.published())
+    n_transactions = 0
     for active in ([0, 5], [1, 2, 6], [6, 7], [3, 3, 4], [3, 0, 1], [2, 4, 5, 6, 7], [0, 1, 3]):
         want = model.misses(active)
+        n_transactions += len(want) > 0
         got = tab.prepare(np.array(active, np.int32))
         model.upload(want)
         assert list(got) == want, f"misses for {active}"
         assert np.array_equal(tab.published(), model.published()), f"published map after {active}"
+        lease = tab.acquire()
         torch.cuda.synchronize()
-        rows_dev, stride, smap = tab.device()
+        rows_dev, stride, smap = lease.rows_dev, lease.row_stride, lease.slot_map_dev
+        assert (rows_dev, stride, smap) == tab.device()
         dev_map = read_device(smap, 4 * cfg.E).view(np.int32)
         assert np.array_equal(dev_map, model.published()), "device map differs from the host mirror"
         row_bytes = synth.expert_row_layout(cfg.H, cfg.I)["row_bytes"]
         for e, s in model.slot_of.items():
             assert np.array_equal(read_device(rows_dev + s * stride, row_bytes), rows[e, :row_bytes]), \
                 f"device row of expert {e} (slot {s}) differs from the host source"
+        tab.release(lease)
     st = tab.stats()
     row_bytes = synth.expert_row_layout(cfg.H, cfg.I)["row_bytes"]
     assert st["misses"] == model.n_misses and st["h2d_bytes"] == st["misses"] * row_bytes
-    assert st["expert_d2h_bytes"] == 0 and st["host_writes"] == 0
+    assert st["expert_d2h_bytes"] == 0 and st["host_writes"] == 0 and st["open_leases"] == 0
     assert st["hits"] + st["misses"] == 2 + 3 + 2 + 2 + 3 + 5 + 3
+    assert st["generation"] == 1 + n_transactions
+    tab.verify_source()
     assert (rows.sum(dtype=np.uint64), rows.tobytes()[:4096]) == digest, "the host source was written"
     tab.close()
 
 
-def test_more_misses_than_spare_rows_is_a_capacity_error():
+def test_open_lease_holds_rows_then_release_frees_them():
+    # 5 rows (capacity 3 + 2 spares, steps of one token x top-2).  A lease on
+    # generation 1 keeps rows 0-2 (experts 0, 1, 2); the first step puts 4, 5
+    # into the spares and drops 0, 1 above capacity; the second step finds no
+    # row its transaction may write until the lease is released.
     from w4a16_routed_expert_amd import binding as B
     cfg = synth.CONFIGS["tiny"]
-    tab = make_table(cfg, synth.make_expert_rows(cfg), capacity=3, spare=1)
-    # 5 active experts need 5 rows; the table has 4 (0, 1, 2 are active, so none can be evicted)
-    misses = B.moe_table_misses(tab.handle, np.array([0, 1, 2, 4, 5], np.int32))
-    assert list(misses) == [4, 5]
+    rows = synth.make_expert_rows(cfg)
+    tab = make_table(cfg, rows, capacity=3, spare=2, max_tokens=1)
+    held = tab.acquire()
+    assert held.generation == 1
+    tab.prepare(np.array([4, 5], np.int32))
+    misses = tab.misses(np.array([6, 7], np.int32))
+    assert list(misses) == [6, 7]
     with pytest.raises(B.MoeError) as ei:
-        B.moe_upload_expert_rows(tab.handle, misses)
+        tab.upload(misses)
     assert ei.value.code == B.MOE_ERR_CAPACITY
+    st = tab.stats()
+    assert st["generation"] == 2 and st["open_leases"] == 1
+    tab.release(held)
+    tab.upload(misses)
+    lease = tab.acquire()
+    torch.cuda.synchronize()
+    m = read_device(lease.slot_map_dev, 4 * cfg.E).view(np.int32)
+    row_bytes = synth.expert_row_layout(cfg.H, cfg.I)["row_bytes"]
+    for e in (6, 7):
+        assert m[e] >= 0
+        assert np.array_equal(read_device(lease.rows_dev + m[e] * lease.row_stride, row_bytes), rows[e, :row_bytes])
+    tab.release(lease)
     with pytest.raises(B.MoeError) as ei:          # an expert already published is not a miss
-        B.moe_upload_expert_rows(tab.handle, np.array([0], np.int32))
+        B.moe_upload_expert_rows(tab.handle, np.array([6], np.int32))
     assert ei.value.code == B.MOE_ERR_INVALID_ARG
     tab.close()
 
 
-def run_layer(cfg, rows, wr, xs, bias=None, table=None):
+def test_source_identity_is_checked():
+    from w4a16_routed_expert_amd import binding as B
+    cfg = synth.CONFIGS["tiny"]
+    rows = synth.make_expert_rows(cfg)
+    dig = [B.moe_row_digest(rows[e]) for e in range(cfg.E)]
+    tab = make_table(cfg, rows, capacity=3, spare=5, max_tokens=4, digests=dig)
+    tab.verify_source()
+    rows[2, 17] ^= 1                                   # the caller breaks its promise
+    with pytest.raises(B.MoeError) as ei:
+        tab.verify_source()
+    assert ei.value.code == B.MOE_ERR_SOURCE and tab.stats()["host_writes"] == 1
+    tab.close()
+
+
+def run_layer(cfg, rows, wr, xs, bias=None, table=None, shared=None):
     from w4a16_routed_expert_amd.layer import RoutedExpertLayer
     dev = torch.device("cuda:0")
     lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev),
                             torch.from_numpy(wr).to(dev), None if bias is None else torch.from_numpy(bias).to(dev),
                             max_T=max(x.shape[0] for x in xs), device=dev)
+    sh = None
+    if shared is not None:
+        from w4a16_routed_expert_amd.layer import SharedExpert
+        sh = SharedExpert(*(torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in shared),
+                          max_T=max(x.shape[0] for x in xs), device=dev)
     ys = []
     for x in xs:
-        y = lay.forward(torch.from_numpy(x).to(dev), table=table)
+        y = lay.forward(torch.from_numpy(x).to(dev), table=table, shared=sh)
         torch.cuda.synchronize()
-        assert int(lay.status.cpu()[0]) == 0, "an active expert had no published row"
+        lay.check_status()
         ys.append(y.cpu().numpy().view(np.uint16).copy())
     return ys
 
@@ -157,7 +209,7 @@ def test_partial_residency_output_equals_full_residency(name, capacity, spare, T
     bias = synth.make_zipf_bias(cfg, layer=1)
     xs = [synth.make_x(cfg, T, step=s, layer=1) for s in range(4)]
     full = run_layer(cfg, rows, wr, xs, bias)
-    tab = make_table(cfg, rows, capacity, spare)
+    tab = make_table(cfg, rows, capacity, spare, max_tokens=T)
     part = run_layer(cfg, rows, wr, xs, bias, table=tab)
     for s, (a, b) in enumerate(zip(full, part)):
         assert np.array_equal(a, b), f"{name} step {s}: output with partial residency differs"
@@ -165,4 +217,51 @@ def test_partial_residency_output_equals_full_residency(name, capacity, spare, T
     assert st["misses"] > 0 and st["expert_d2h_bytes"] == 0
     ref = oracle.layer(xs[0], wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, bias=bias)
     assert_close_rows(part[0], ref["y"], f"{name} partial residency vs oracle")
+    tab.close()
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_olmoe_stack_two_layers_partial_residency_vs_oracle(T):
+    # Two consecutive layers of the OLMoE-shaped stack (own weights, router and
+    # Zipf(1.1) bias each), 40 of 64 experts resident, spare rows by the
+    # create-time rule; three steps per layer; every layer's y against the
+    # oracle and bit-identical to full residency.
+    from layer_util import oracle_tokens
+    cfg = synth.CONFIGS["olmoe_stack"]
+    spare = min(cfg.E - cfg.resident, T * cfg.k)
+    for layer in (5, 6):
+        rows = synth.make_expert_rows(cfg, layer=layer)
+        wr = synth.make_router(cfg, layer=layer)
+        bias = synth.make_zipf_bias(cfg, layer=layer)
+        xs = [synth.make_x(cfg, T, step=s, layer=layer) for s in range(3)]
+        tab = make_table(cfg, rows, cfg.resident, spare, max_tokens=T)
+        part = run_layer(cfg, rows, wr, xs, bias, table=tab)
+        st = tab.stats()
+        full = run_layer(cfg, rows, wr, xs, bias)
+        for s, (a, b) in enumerate(zip(full, part)):
+            assert np.array_equal(a, b), f"layer {layer} step {s}: partial residency differs from full"
+        for s, x in enumerate(xs):
+            ref = oracle_tokens(x, wr, rows, cfg, bias=bias)
+            assert_close_rows(part[s], ref["y"], f"olmoe stack layer {layer} T={T} step {s} vs oracle")
+        assert st["misses"] > 0 and st["expert_d2h_bytes"] == 0 and st["open_leases"] == 0
+        tab.close()
+
+
+def test_qwen_partial_residency_with_shared_expert_T64():
+    # 39 of 60 experts resident, 64 tokens, the FP16 shared expert beside.
+    from layer_util import oracle_tokens
+    cfg = synth.CONFIGS["qwen"]
+    T = 64
+    rows = synth.make_expert_rows(cfg)
+    wr = synth.make_router(cfg)
+    shared = synth.make_shared(cfg)
+    xs = [synth.make_x(cfg, T, step=s, layer=2) for s in range(2)]
+    tab = make_table(cfg, rows, cfg.resident, min(cfg.E - cfg.resident, T * cfg.k), max_tokens=T)
+    part = run_layer(cfg, rows, wr, xs, table=tab, shared=shared)
+    full = run_layer(cfg, rows, wr, xs, shared=shared)
+    for s, x in enumerate(xs):
+        assert np.array_equal(full[s], part[s]), f"step {s}: partial residency differs from full"
+        ref = oracle_tokens(x, wr, rows, cfg, shared=shared)
+        assert_close_rows(part[s], ref["y"], f"qwen partial T=64 step {s} vs oracle")
+    assert tab.stats()["misses"] > 0
     tab.close()

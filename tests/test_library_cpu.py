@@ -78,7 +78,48 @@ def test_host_validation_rejects_bad_arguments(lib):
     with pytest.raises(B.MoeError) as ei:     # I not a multiple of 128
         B.moe_w4a16_expert_ffn(F, 4, 256, 500, 8, 2, F, 1 << 20, None, F, F, F, F, F, F, stream=0)
     assert ei.value.code == B.MOE_ERR_UNSUPPORTED
+    for call in (B.moe_w4a16_expert_ffn, B.moe_w4a16_gateup):   # unknown kernel family
+        with pytest.raises(B.MoeError) as ei:
+            if call is B.moe_w4a16_gateup:
+                call(F, 4, 256, 512, 8, 2, F, 1 << 20, None, F, F, F, F, F, mode=3, stream=0)
+            else:
+                call(F, 4, 256, 512, 8, 2, F, 1 << 20, None, F, F, F, F, F, F, mode=3, stream=0)
+        assert ei.value.code == B.MOE_ERR_INVALID_ARG and "mode" in B.moe_last_error()
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_w4a16_down(4, 256, 512, 8, 2, F, 1 << 20, None, F, F, F, F, F, mode=-1, stream=0)
+    assert ei.value.code == B.MOE_ERR_INVALID_ARG
     with pytest.raises(B.MoeError) as ei:     # only one of the shared-expert pointers
         B.moe_combine(F, F, F, F, None, 4, 256, 2, F, stream=0)
     assert ei.value.code == B.MOE_ERR_INVALID_ARG
     assert "shared" in B.moe_last_error()
+
+
+def test_table_create_rejects_before_touching_the_gpu(lib):
+    # moe_table_create validates the descriptor and the host source's identity
+    # and layout before any device call, so these run without a GPU.
+    import numpy as np
+    cfg = synth.CONFIGS["tiny"]
+    rows = synth.make_expert_rows(cfg)
+    stride = rows.strides[0]
+    # steps of 2 tokens x top-2 with capacity 3 need min(5, 4 + 1) = 5 spare rows
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_table_create(cfg.E, cfg.H, cfg.I, 3, 4, 2, cfg.k, 2, rows, stride, stream=0)
+    assert ei.value.code == B.MOE_ERR_CAPACITY and "spare" in B.moe_last_error()
+    with pytest.raises(B.MoeError) as ei:          # no staging
+        B.moe_table_create(cfg.E, cfg.H, cfg.I, 3, 5, 0, cfg.k, 2, rows, stride, stream=0)
+    assert ei.value.code == B.MOE_ERR_CAPACITY
+    dig = np.array([B.moe_row_digest(rows[e]) for e in range(cfg.E)], np.uint64)
+    bad = dig.copy()
+    bad[6] ^= np.uint64(1)
+    with pytest.raises(B.MoeError) as ei:          # identity: the digest of expert 6 does not match
+        B.moe_table_create(cfg.E, cfg.H, cfg.I, 3, 5, 2, cfg.k, 2, rows, stride, row_digests=bad, stream=0)
+    assert ei.value.code == B.MOE_ERR_SOURCE and "6" in B.moe_last_error()
+    broken = rows.copy()
+    off = synth.expert_row_layout(cfg.H, cfg.I)["down_s"]
+    broken[1, off:off + 2] = np.frombuffer(np.float16(np.inf).tobytes(), np.uint8)
+    with pytest.raises(B.MoeError) as ei:          # layout: a non-finite FP16 scale
+        B.moe_table_create(cfg.E, cfg.H, cfg.I, 3, 5, 2, cfg.k, 2, broken, stride, stream=0)
+    assert ei.value.code == B.MOE_ERR_SOURCE and "scale" in B.moe_last_error()
+    # the digest is a plain function of the bytes
+    assert B.moe_row_digest(rows[3]) == B.moe_row_digest(rows[3].copy())
+    assert B.moe_row_digest(rows[3]) != B.moe_row_digest(rows[4])

@@ -23,6 +23,7 @@ MOE_ERR_CAPACITY = 4
 MOE_ERR_HIP = 5
 MOE_ERR_FAULTED = 6
 MOE_ERR_ABSENT_EXPERT = 7
+MOE_ERR_SOURCE = 8
 
 MOE_FFN_PATH_AUTO = 0
 MOE_FFN_PATH_STREAM = 1
@@ -32,22 +33,31 @@ MOE_FFN_PATH_GEMM = 2
 EXPORTS = (
     "moe_version", "moe_last_error", "moe_expert_row_bytes",
     "moe_route_workspace_size", "moe_route", "moe_route_exact",
-    "moe_set_ffn_path", "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
+    "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
     "moe_combine", "moe_shared_ffn_workspace_size", "moe_shared_ffn",
-    "moe_table_create", "moe_table_destroy", "moe_table_device", "moe_table_misses", "moe_upload_expert_rows",
-    "moe_table_record_consumers", "moe_table_stats", "moe_table_published",
+    "moe_row_digest", "moe_table_create", "moe_table_destroy", "moe_table_device", "moe_table_misses",
+    "moe_upload_expert_rows", "moe_table_acquire", "moe_table_release", "moe_table_verify_source",
+    "moe_table_stats", "moe_table_published",
 )
 
 
 class TableDesc(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int), ("H", ctypes.c_int), ("I", ctypes.c_int), ("capacity", ctypes.c_int),
-                ("spare_rows", ctypes.c_int), ("staging_rows", ctypes.c_int), ("host_source", ctypes.c_void_p),
-                ("host_row_stride", ctypes.c_size_t), ("initial_resident", ctypes.c_void_p)]
+                ("spare_rows", ctypes.c_int), ("staging_rows", ctypes.c_int), ("top_k", ctypes.c_int),
+                ("max_tokens", ctypes.c_int), ("host_source", ctypes.c_void_p),
+                ("host_row_stride", ctypes.c_size_t), ("initial_resident", ctypes.c_void_p),
+                ("row_digests", ctypes.c_void_p)]
 
 
 class TableCounters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("steps", "hits", "misses", "evictions", "h2d_bytes", "staging_waits",
-                                               "expert_d2h_bytes", "host_writes")]
+                                               "expert_d2h_bytes", "host_writes", "generation", "open_leases",
+                                               "failed_uploads")]
+
+
+class TableLease(ctypes.Structure):
+    _fields_ = [("generation", ctypes.c_uint64), ("rows_dev", ctypes.c_void_p), ("row_stride", ctypes.c_size_t),
+                ("slot_map_dev", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -84,20 +94,20 @@ def load(path: str = LIB_PATH):
     L.moe_route_exact.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                   _vp]
     L.moe_w4a16_gateup.restype = _i
-    L.moe_set_ffn_path.argtypes = [_i]
-    L.moe_set_ffn_path.restype = _i
-    L.moe_w4a16_gateup.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.moe_w4a16_gateup.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp]
     L.moe_w4a16_down.restype = _i
-    L.moe_w4a16_down.argtypes = [_i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.moe_w4a16_down.argtypes = [_i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp]
     L.moe_w4a16_expert_ffn.restype = _i
     L.moe_w4a16_expert_ffn.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                       _vp]
+                                       _i, _vp]
     L.moe_combine.restype = _i
     L.moe_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]
     L.moe_shared_ffn_workspace_size.restype = _sz
     L.moe_shared_ffn_workspace_size.argtypes = [_i, _i, _i]
     L.moe_shared_ffn.restype = _i
     L.moe_shared_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]
+    L.moe_row_digest.restype = ctypes.c_uint64
+    L.moe_row_digest.argtypes = [_vp, _sz]
     L.moe_table_create.restype = _i
     L.moe_table_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(TableDesc), _vp]
     L.moe_table_destroy.restype = None
@@ -108,8 +118,12 @@ def load(path: str = LIB_PATH):
     L.moe_table_misses.argtypes = [_vp, _vp, _i, _vp, ctypes.POINTER(_i)]
     L.moe_upload_expert_rows.restype = _i
     L.moe_upload_expert_rows.argtypes = [_vp, _vp, _i, _vp]
-    L.moe_table_record_consumers.restype = _i
-    L.moe_table_record_consumers.argtypes = [_vp, _vp]
+    L.moe_table_acquire.restype = _i
+    L.moe_table_acquire.argtypes = [_vp, _vp, ctypes.POINTER(TableLease)]
+    L.moe_table_release.restype = _i
+    L.moe_table_release.argtypes = [_vp, ctypes.POINTER(TableLease), _vp]
+    L.moe_table_verify_source.restype = _i
+    L.moe_table_verify_source.argtypes = [_vp]
     L.moe_table_stats.restype = _i
     L.moe_table_stats.argtypes = [_vp, ctypes.POINTER(TableCounters)]
     L.moe_table_published.restype = _i
@@ -177,27 +191,24 @@ def moe_route_exact(x, w_router, bias, T, H, E, k, logits, topk_ids, topk_w, exp
                                   _p(n_active), _p(ws), ws_bytes, _s(stream)))
 
 
-def moe_set_ffn_path(path: int) -> None:
-    _check(load().moe_set_ffn_path(path))
-
-
 def moe_w4a16_gateup(x, T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, sorted_pairs, active_list,
-                     n_active, h, status=None, stream=None):
+                     n_active, h, status=None, mode=MOE_FFN_PATH_AUTO, stream=None):
     _check(load().moe_w4a16_gateup(_p(x), T, H, I, E, k, _p(rows), row_stride, _p(slot_map), _p(expert_offsets),
-                                   _p(sorted_pairs), _p(active_list), _p(n_active), _p(h), _p(status), _s(stream)))
+                                   _p(sorted_pairs), _p(active_list), _p(n_active), _p(h), _p(status), mode,
+                                   _s(stream)))
 
 
 def moe_w4a16_down(T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, active_list, n_active, h, pair_out,
-                   status=None, stream=None):
+                   status=None, mode=MOE_FFN_PATH_AUTO, stream=None):
     _check(load().moe_w4a16_down(T, H, I, E, k, _p(rows), row_stride, _p(slot_map), _p(expert_offsets),
-                                 _p(active_list), _p(n_active), _p(h), _p(pair_out), _p(status), _s(stream)))
+                                 _p(active_list), _p(n_active), _p(h), _p(pair_out), _p(status), mode, _s(stream)))
 
 
 def moe_w4a16_expert_ffn(x, T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, sorted_pairs, active_list,
-                         n_active, h, pair_out, status=None, stream=None):
+                         n_active, h, pair_out, status=None, mode=MOE_FFN_PATH_AUTO, stream=None):
     _check(load().moe_w4a16_expert_ffn(_p(x), T, H, I, E, k, _p(rows), row_stride, _p(slot_map),
                                        _p(expert_offsets), _p(sorted_pairs), _p(active_list), _p(n_active), _p(h),
-                                       _p(pair_out), _p(status), _s(stream)))
+                                       _p(pair_out), _p(status), mode, _s(stream)))
 
 
 def moe_combine(pair_out, pair_pos, topk_w, shared_out, shared_gate, T, H, k, y, stream=None):
@@ -215,14 +226,22 @@ def moe_shared_ffn(x, w_gate, w_up, w_down, w_sgate, T, H, Is, shared_out, share
 
 
 # ------------------------------------------------------------------ resident expert table
-def moe_table_create(E, H, I, capacity, spare_rows, staging_rows, host_source, host_row_stride,
-                     initial_resident=None, stream=None):
+def moe_row_digest(a) -> int:
+    """Digest of a host buffer (numpy array), the identity moe_table_create checks."""
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    return int(load().moe_row_digest(a.ctypes.data, a.nbytes))
+
+
+def moe_table_create(E, H, I, capacity, spare_rows, staging_rows, top_k, max_tokens, host_source, host_row_stride,
+                     initial_resident=None, row_digests=None, stream=None):
     """host_source: a C-contiguous uint8 numpy array [E, host_row_stride] that must outlive the table.
     Returns the table handle (an int)."""
     import numpy as np
     init = None if initial_resident is None else np.ascontiguousarray(initial_resident, dtype=np.int32)
-    d = TableDesc(E, H, I, capacity, spare_rows, staging_rows, host_source.ctypes.data, host_row_stride,
-                  None if init is None else init.ctypes.data)
+    dig = None if row_digests is None else np.ascontiguousarray(row_digests, dtype=np.uint64)
+    d = TableDesc(E, H, I, capacity, spare_rows, staging_rows, top_k, max_tokens, host_source.ctypes.data,
+                  host_row_stride, None if init is None else init.ctypes.data, None if dig is None else dig.ctypes.data)
     out = _vp()
     _check(load().moe_table_create(ctypes.byref(out), ctypes.byref(d), _s(stream)))
     return out.value
@@ -256,8 +275,18 @@ def moe_upload_expert_rows(table, expert_ids, stream=None):
     _check(load().moe_upload_expert_rows(table, ids.ctypes.data if len(ids) else None, len(ids), _s(stream)))
 
 
-def moe_table_record_consumers(table, stream=None):
-    _check(load().moe_table_record_consumers(table, _s(stream)))
+def moe_table_acquire(table, stream=None) -> TableLease:
+    lease = TableLease()
+    _check(load().moe_table_acquire(table, _s(stream), ctypes.byref(lease)))
+    return lease
+
+
+def moe_table_release(table, lease: TableLease, stream=None):
+    _check(load().moe_table_release(table, ctypes.byref(lease), _s(stream)))
+
+
+def moe_table_verify_source(table):
+    _check(load().moe_table_verify_source(table))
 
 
 def moe_table_stats(table) -> dict:

@@ -15,6 +15,8 @@ void set_error(const char *fmt, ...)
     va_end(ap);
 }
 
+void vset_error(const char *fmt, va_list ap) { vsnprintf(g_err, sizeof(g_err), fmt, ap); }
+
 void clear_error() { g_err[0] = '\0'; }
 
 int fail(int code, const char *fmt, ...)

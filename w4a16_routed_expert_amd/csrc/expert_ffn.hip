@@ -46,8 +46,6 @@
 //     acc * 2^20.
 #include "ffn_common.h"
 
-#include <atomic>
-
 namespace {
 
 using namespace ffn;
@@ -460,25 +458,21 @@ int launch_nt(const FfnArgs &a, hipStream_t s, int S, long long max_items, const
     return launch_one<GATEUP, NT, 1>(a, s, max_items, who);
 }
 
-// Kernel family of the FFN calls (moe_set_ffn_path).
-std::atomic<int> g_ffn_path{MOE_FFN_PATH_AUTO};
-
 // The grouped GEMM once experts average 64 routed pairs or more: then the
 // layer is bound by the matrix cores and the streaming kernel, built to keep
 // HBM busy at a few pairs per expert, would convert every weight tile once
-// per 16 pairs.
-bool use_gemm(const FfnArgs &a)
+// per 16 pairs.  `mode` (MOE_FFN_PATH_*) forces either family.
+bool use_gemm(const FfnArgs &a, int mode)
 {
-    const int p = g_ffn_path.load(std::memory_order_relaxed);
-    if (p == MOE_FFN_PATH_STREAM) return false;
-    if (p == MOE_FFN_PATH_GEMM) return true;
+    if (mode == MOE_FFN_PATH_STREAM) return false;
+    if (mode == MOE_FFN_PATH_GEMM) return true;
     return (long long)a.T * a.k >= 64LL * a.E;
 }
 
 template <bool GATEUP>
-int launch_ffn(const FfnArgs &a, hipStream_t s, const char *who)
+int launch_ffn(const FfnArgs &a, int mode, hipStream_t s, const char *who)
 {
-    if (use_gemm(a)) return GATEUP ? launch_gemm_gateup(a, s) : launch_gemm_down(a, s);
+    if (use_gemm(a, mode)) return GATEUP ? launch_gemm_gateup(a, s) : launch_gemm_down(a, s);
     const int K = GATEUP ? a.H : a.I;
     const int R = GATEUP ? a.I : a.H;
     // row slots of wavefronts: gate/up one row group each, down two when the
@@ -513,10 +507,12 @@ int launch_ffn(const FfnArgs &a, hipStream_t s, const char *who)
 int make_args(FfnArgs &a, const void *x_dev, int T, int H, int I, int E, int k, const void *rows_dev,
               size_t row_stride, const int32_t *slot_map_dev, const int32_t *expert_offsets_dev,
               const int32_t *sorted_pairs_dev, const int32_t *active_list_dev, const int32_t *n_active_dev,
-              void *h_dev, float *pair_out_dev, int32_t *status_dev, const char *who)
+              void *h_dev, float *pair_out_dev, int32_t *status_dev, int mode, const char *who)
 {
     int rc = moe::check_shape(T, H, I, E, k, true);
     if (rc) return rc;
+    if (mode != MOE_FFN_PATH_AUTO && mode != MOE_FFN_PATH_STREAM && mode != MOE_FFN_PATH_GEMM)
+        return moe::fail(MOE_ERR_INVALID_ARG, "%s: unknown mode %d", who, mode);
     if (T == 0) return -1;          // nothing to do; callers return MOE_OK
     if (H > kMaxNT * 128 || I > kMaxNT * 128)
         return moe::fail(MOE_ERR_UNSUPPORTED, "%s: H and I must be <= %d", who, kMaxNT * 128);
@@ -550,72 +546,63 @@ int make_args(FfnArgs &a, const void *x_dev, int T, int H, int I, int E, int k, 
     return MOE_OK;
 }
 
-int launch_gateup(const FfnArgs &a, hipStream_t s) { return launch_ffn<true>(a, s, "moe_w4a16_gateup"); }
+int launch_gateup(const FfnArgs &a, int mode, hipStream_t s) { return launch_ffn<true>(a, mode, s, "moe_w4a16_gateup"); }
 
-int launch_down(const FfnArgs &a, hipStream_t s) { return launch_ffn<false>(a, s, "moe_w4a16_down"); }
+int launch_down(const FfnArgs &a, int mode, hipStream_t s) { return launch_ffn<false>(a, mode, s, "moe_w4a16_down"); }
 
 }  // namespace
 
 extern "C" {
 
-int moe_set_ffn_path(int path)
-{
-    moe::clear_error();
-    if (path != MOE_FFN_PATH_AUTO && path != MOE_FFN_PATH_STREAM && path != MOE_FFN_PATH_GEMM)
-        return moe::fail(MOE_ERR_INVALID_ARG, "moe_set_ffn_path: unknown path %d", path);
-    g_ffn_path.store(path, std::memory_order_relaxed);
-    return MOE_OK;
-}
-
 int moe_w4a16_gateup(const void *x_dev, int T, int H, int I, int E, int k,
                      const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                      const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
                      const int32_t *active_list_dev, const int32_t *n_active_dev,
-                     void *h_dev, int32_t *status_dev, void *stream)
+                     void *h_dev, int32_t *status_dev, int mode, void *stream)
 {
     moe::clear_error();
     FfnArgs a;
     int rc = make_args(a, x_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev, expert_offsets_dev,
-                       sorted_pairs_dev, active_list_dev, n_active_dev, h_dev, nullptr, status_dev,
+                       sorted_pairs_dev, active_list_dev, n_active_dev, h_dev, nullptr, status_dev, mode,
                        "moe_w4a16_gateup");
     if (rc) return rc < 0 ? MOE_OK : rc;
     if (!x_dev || !sorted_pairs_dev) return moe::fail(MOE_ERR_INVALID_ARG, "moe_w4a16_gateup: null pointer argument");
-    return launch_gateup(a, (hipStream_t)stream);
+    return launch_gateup(a, mode, (hipStream_t)stream);
 }
 
 int moe_w4a16_down(int T, int H, int I, int E, int k,
                    const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                    const int32_t *expert_offsets_dev, const int32_t *active_list_dev,
                    const int32_t *n_active_dev, const void *h_dev, float *pair_out_dev,
-                   int32_t *status_dev, void *stream)
+                   int32_t *status_dev, int mode, void *stream)
 {
     moe::clear_error();
     FfnArgs a;
     int rc = make_args(a, nullptr, T, H, I, E, k, rows_dev, row_stride, slot_map_dev, expert_offsets_dev,
                        nullptr, active_list_dev, n_active_dev, const_cast<void *>(h_dev), pair_out_dev, status_dev,
-                       "moe_w4a16_down");
+                       mode, "moe_w4a16_down");
     if (rc) return rc < 0 ? MOE_OK : rc;
     if (!pair_out_dev) return moe::fail(MOE_ERR_INVALID_ARG, "moe_w4a16_down: null pointer argument");
-    return launch_down(a, (hipStream_t)stream);
+    return launch_down(a, mode, (hipStream_t)stream);
 }
 
 int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
                          const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                          const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
                          const int32_t *active_list_dev, const int32_t *n_active_dev,
-                         void *h_dev, float *pair_out_dev, int32_t *status_dev, void *stream)
+                         void *h_dev, float *pair_out_dev, int32_t *status_dev, int mode, void *stream)
 {
     moe::clear_error();
     FfnArgs a;
     int rc = make_args(a, x_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev, expert_offsets_dev,
-                       sorted_pairs_dev, active_list_dev, n_active_dev, h_dev, pair_out_dev, status_dev,
+                       sorted_pairs_dev, active_list_dev, n_active_dev, h_dev, pair_out_dev, status_dev, mode,
                        "moe_w4a16_expert_ffn");
     if (rc) return rc < 0 ? MOE_OK : rc;
     if (!x_dev || !sorted_pairs_dev || !pair_out_dev)
         return moe::fail(MOE_ERR_INVALID_ARG, "moe_w4a16_expert_ffn: null pointer argument");
-    rc = launch_gateup(a, (hipStream_t)stream);
+    rc = launch_gateup(a, mode, (hipStream_t)stream);
     if (rc) return rc;
-    return launch_down(a, (hipStream_t)stream);
+    return launch_down(a, mode, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -89,6 +89,7 @@ __device__ inline V sum_phases(V v)
 
 // Thread-local message behind moe_last_error().
 void set_error(const char *fmt, ...);
+void vset_error(const char *fmt, va_list ap);
 void clear_error();
 
 // Returns `code` after recording the formatted message.

@@ -65,26 +65,29 @@ class RoutedExpertLayer:
                         self.topk_w, self.expert_offsets, self.sorted_pairs, self.pair_pos, self.active_list,
                         self.n_active, self.ws, self.ws_bytes, stream)
 
-    def ffn(self, x: torch.Tensor, stream=None, rows=None, table=None):
-        """Expert FFN over the rows tensor (or `rows`), or over a ResidentExpertTable's device rows."""
+    def ffn(self, x: torch.Tensor, stream=None, rows=None, lease=None, mode: int = B.MOE_FFN_PATH_AUTO):
+        """Expert FFN over the rows tensor (or `rows`), or over the rows and map of a table lease
+        (ResidentExpertTable.acquire).  mode: kernel family (B.MOE_FFN_PATH_AUTO / _STREAM / _GEMM)."""
         T = x.shape[0]
-        if table is not None:
-            rows_dev, stride, smap = table.device()
+        if lease is not None:
+            rows_dev, stride, smap = lease.rows_dev, lease.row_stride, lease.slot_map_dev
         else:
             rows_dev, stride, smap = (self.rows if rows is None else rows), self.row_stride, self.slot_map
         B.moe_w4a16_expert_ffn(x, T, self.H, self.I, self.E, self.k, rows_dev, stride, smap, self.expert_offsets,
                                self.sorted_pairs, self.active_list, self.n_active, self.h, self.pair_out,
-                               self.status, stream)
+                               status=self.status, mode=mode, stream=stream)
 
     def combine(self, T: int, y: torch.Tensor, shared_out=None, shared_gate=None, stream=None):
         B.moe_combine(self.pair_out, self.pair_pos, self.topk_w, shared_out, shared_gate, T, self.H, self.k, y,
                       stream)
 
     def forward(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None, rows=None,
-                shared_out=None, shared_gate=None, table=None, shared: "SharedExpert | None" = None) -> torch.Tensor:
+                shared_out=None, shared_gate=None, table=None, shared: "SharedExpert | None" = None,
+                mode: int = B.MOE_FFN_PATH_AUTO) -> torch.Tensor:
         """y = layer(x); x float16 [T, H] on the device.  With a ResidentExpertTable the
-        routed experts' misses are uploaded (host round trip of the active list) before
-        the expert FFN reads the table's rows.  With a SharedExpert its FFN runs on a
+        routed experts' misses are uploaded (host round trip of the active list; the copies
+        run on the table's copy stream) and the expert FFN reads the rows and map of a lease
+        on the new generation, released after it.  With a SharedExpert its FFN runs on a
         second stream, concurrently with the routing and the routed experts (it needs x
         only), and the combine waits for both."""
         T = x.shape[0]
@@ -97,20 +100,35 @@ class RoutedExpertLayer:
             shared.run(x, side)
             shared_out, shared_gate = shared.out, shared.gate
         self.route(x, main)
+        lease = None
         if table is not None:
-            table.prepare(self.active_experts(), main)
-        self.ffn(x, main, rows, table)
-        if table is not None:
-            table.record_consumers(main)
+            table.prepare(self.active_experts(main), main)
+            lease = table.acquire(main)
+        self.ffn(x, main, rows, lease, mode)
+        if lease is not None:
+            table.release(lease, main)
         if shared is not None:
             main.wait_stream(side)
         self.combine(T, y, shared_out, shared_gate, main)
         return y
 
-    def active_experts(self):
-        """Active expert ids of the last route, on the host (synchronizes with the device)."""
-        n = int(self.n_active.cpu()[0])
-        return self.active_list[:n].cpu().numpy()
+    def active_experts(self, stream=None):
+        """Active expert ids of the last route, on the host.  The copies are ordered after
+        the work already enqueued on `stream` (the stream the route ran on; None = the
+        current stream), and the call waits for them."""
+        with torch.cuda.stream(_torch_stream(stream)):
+            n = int(self.n_active.cpu()[0])
+            return self.active_list[:n].cpu().numpy()
+
+    def check_status(self, stream=None):
+        """Raises MoeError if an expert FFN call since this layer's buffers were made
+        found a routed expert without a device row (the status word is sticky; waits
+        for `stream`)."""
+        with torch.cuda.stream(_torch_stream(stream)):
+            st = int(self.status.cpu()[0])
+        if st != B.MOE_OK:
+            raise B.MoeError(st, "expert FFN status word: a routed expert had no published device row"
+                             if st == B.MOE_ERR_ABSENT_EXPERT else "expert FFN status word set")
 
 
 def _torch_stream(stream):
@@ -166,29 +184,45 @@ class ResidentExpertTable:
 
     host_rows: uint8 numpy array [E, stride] holding every expert's row; kept referenced (and
     never written) for the table's lifetime.  capacity experts stay published between steps;
-    spare_rows device rows receive misses.
+    spare_rows device rows receive misses (at least what steps of max_tokens tokens with top_k
+    experts need; moe_table_create checks it).
     """
 
     def __init__(self, host_rows, H: int, I: int, capacity: int, spare_rows: int, staging_rows: int = 2,
-                 initial_resident=None, stream=None):
+                 initial_resident=None, top_k: int = 1, max_tokens: int = 1, row_digests=None):
         import numpy as np
         self.host_rows = np.ascontiguousarray(host_rows)
         self.E = self.host_rows.shape[0]
-        self.handle = B.moe_table_create(self.E, H, I, capacity, spare_rows, staging_rows, self.host_rows,
-                                         self.host_rows.strides[0], initial_resident, stream)
+        self.handle = B.moe_table_create(self.E, H, I, capacity, spare_rows, staging_rows, top_k, max_tokens,
+                                         self.host_rows, self.host_rows.strides[0], initial_resident, row_digests)
 
     def device(self):
+        """(rows, stride, map) of the current generation, without a lease."""
         return B.moe_table_device(self.handle)
+
+    def misses(self, active):
+        return B.moe_table_misses(self.handle, active)
+
+    def upload(self, misses, stream=None):
+        """One miss transaction; `stream` is ordered after the new generation's publication."""
+        if len(misses):
+            B.moe_upload_expert_rows(self.handle, misses, stream)
 
     def prepare(self, active, stream=None):
         """Start a step with these active experts: upload and publish the misses. Returns the misses."""
-        misses = B.moe_table_misses(self.handle, active)
-        if len(misses):
-            B.moe_upload_expert_rows(self.handle, misses, stream)
+        misses = self.misses(active)
+        self.upload(misses, stream)
         return misses
 
-    def record_consumers(self, stream=None):
-        B.moe_table_record_consumers(self.handle, stream)
+    def acquire(self, stream=None):
+        """Lease on the current generation (stream ordered after its publication)."""
+        return B.moe_table_acquire(self.handle, stream)
+
+    def release(self, lease, stream=None):
+        B.moe_table_release(self.handle, lease, stream)
+
+    def verify_source(self):
+        B.moe_table_verify_source(self.handle)
 
     def stats(self) -> dict:
         return B.moe_table_stats(self.handle)
