@@ -25,8 +25,15 @@ gate/up launch is a matrix-core bound contraction and the roofline reports its
 useful FLOPs (2 * T*k * H * 2I per launch) against the 2.5 PFLOP/s dense FP16
 MFMA peak instead.
 
-The CPU baseline times the oracle (single-threaded C, fp64) on a bounded
-sample of the same workload.
+The timed K steps run in three blocks (graph replays of chunks of consecutive
+steps); the line reports the pooled rate (all tokens over all block time) and
+the blocks' spread.  For the OLMoE-shaped layer the line also carries the
+prefill-sized layer on the same expert shape (T = 4096, grouped GEMM): each
+phase timed with HIP events over back-to-back launches, the FFN's useful FLOPs
+against the FP16 MFMA peak.
+
+The CPU baseline times the oracle (C, fp64) on a bounded sample of the same
+workload, on one thread and on every host thread (at most 16).
 """
 from __future__ import annotations
 
@@ -69,6 +76,8 @@ def parse():
                          "graph is measurably slower)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="olmoe: skip the prefill measurement (T=4096, grouped GEMM) that the line carries")
     ap.add_argument("--partial", action="store_true",
                     help="qwen: keep only the config's resident experts published (39 of 60) and upload the "
                          "misses of every step before its expert FFN, as olmoe_stack does")
@@ -274,32 +283,38 @@ def main():
         return
 
     # ---------------------------------------------------------------- graphs
-    # Steps repeat with period R*S (replica, input batch).  A graph holds G
-    # consecutive steps; graph g1[s] starts at step s (mod the period), and
-    # single-step graphs cover a remainder of K that G does not divide.
+    # Steps repeat with period R*S (replica, input batch).  The K timed steps
+    # run in three blocks (their spread is reported); each block is cut into
+    # chunks of at most G consecutive steps and each chunk is one graph launch
+    # (one graph per distinct first step modulo the period and length).  The
+    # warm-up replays the same kind of chunks.
     n_graph = R * S
+    K = args.steps
     G = args.graph_steps if args.graph_steps > 0 else n_graph
-    g1, gG = {}, {}
+    nb = 3 if K >= 3 else 1
+    blocks = [(args.warmup + K * b // nb, K * (b + 1) // nb - K * b // nb) for b in range(nb)]
+
+    def chunks(s0, count):
+        out, s = [], s0
+        while s < s0 + count:
+            n = min(G, s0 + count - s)
+            out.append((s, n))
+            s += n
+        return out
+
+    graphs = {}
     if not args.no_graph:
         for s in range(n_graph):
-            run_step(s)                 # warm the step once eagerly before capture
+            run_step(s)                 # warm every step once eagerly before capture
         torch.cuda.synchronize()
         cap = torch.cuda.Stream()
-        for s in range(n_graph):
+        keys = sorted({(s % n_graph, n) for b0, bn in [(0, args.warmup)] + blocks for s, n in chunks(b0, bn)})
+        for s0, n in keys:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                run_step(s)
-            g1[s] = g
-        if G > 1:
-            for b in range(n_graph):
-                s0 = (b * G) % n_graph
-                if s0 in gG:
-                    continue
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cap):
-                    for j in range(G):
-                        run_step(s0 + j)
-                gG[s0] = g
+                for j in range(n):
+                    run_step(s0 + j)
+            graphs[(s0, n)] = g
         torch.cuda.synchronize()
 
     def run_steps(s_begin, count):
@@ -308,27 +323,26 @@ def main():
             for s in range(s_begin, s_begin + count):
                 run_step(s)
             return
-        s, end = s_begin, s_begin + count
-        while s < end:
-            if G > 1 and s + G <= end and (s % n_graph) in gG:
-                gG[s % n_graph].replay()
-                s += G
-            else:
-                g1[s % n_graph].replay()
-                s += 1
+        for s, n in chunks(s_begin, count):
+            graphs[(s % n_graph, n)].replay()
 
     run_steps(0, args.warmup)
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed
-    K = args.steps
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    run_steps(args.warmup, K)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    block_s = []
+    for b0, bn in blocks:
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        run_steps(b0, bn)
+        torch.cuda.synchronize()
+        block_s.append(time.perf_counter() - tb)
+    elapsed = sum(block_s)
     ms_per_step = elapsed * 1e3 / K
     tokens_per_s = T * K / elapsed
+    block_rates = [T * bn / t for (_, bn), t in zip(blocks, block_s)]
+    block_spread = (max(block_rates) - min(block_rates)) / (sum(block_rates) / len(block_rates))
+    graph_chunks = [n for b0, bn in blocks for _, n in chunks(b0, bn)] if not args.no_graph else []
 
     # ---------------------------------------------------------------- per-kernel events (eager, same steps)
     n_ev = min(K, 400)
@@ -392,32 +406,18 @@ def main():
     y_gpu = y.cpu().numpy()
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
-    cpu = None
+    cpu = cpu_all = None
     if not args.skip_cpu:
-        import oracle
-        n_calls, cpu_s, tok = 0, 0.0, 0
-        parity_norm = None
-        Tc = args.cpu_tokens or (32 if args.config == "prefill" else T)
-        Tc = min(Tc, T)
-        while cpu_s < args.cpu_seconds and n_calls < S:
-            tc = time.perf_counter()
-            ref = oracle.layer(xs_np[n_calls][:Tc], wr_np, rows_np, H, I, E, k, shared=shared_np)
-            cpu_s += time.perf_counter() - tc
-            tok += Tc
-            if n_calls == 0:
-                # every token's output depends on that token only: compare the sampled rows
-                yr = ref["y"].view(np.float16).astype(np.float64)
-                d = np.abs(yr - y_gpu[:Tc].astype(np.float64))
-                parity_norm = float((d / np.abs(yr).max(axis=1, keepdims=True)).max())
-            n_calls += 1
-        cpu = {"value": tok / cpu_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_calls} oracle layer call(s) of {Tc} of the batch's {T} tokens on the same inputs "
-                         f"({cpu_s:.1f} s, single-threaded C, fp64)",
-               "gpu_vs_oracle_normwise_err": parity_norm}
+        cpu, cpu_all = cpu_baselines(args, xs_np, wr_np, rows_np, shared_np, H, I, E, k, T, S, y_gpu)
+
+    # ---------------------------------------------------------------- prefill, same expert shape
+    prefill = None
+    if args.config == "olmoe" and not args.no_prefill:
+        prefill = measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev)
 
     workload = f"{cfg.name}_decode_layer_T{T}" if args.config != "prefill" else f"prefill_T{T}"
     out = {
-        "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode)",
+        "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode) / MFMA % (prefill)",
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -437,8 +437,12 @@ def main():
             "weights": "int4 qpacked, 256-value blocks, fp16 scales; fp16 activations, fp32 accumulation",
             "replicas": R, "input_batches": S, "graph_replay": not args.no_graph,
             "steps_per_graph": None if args.no_graph else G,
+            "graph_chunks_timed": graph_chunks,
             "mean_active_experts": float(np.mean(n_act)),
         },
+        "blocks": {"steps": [bn for _, bn in blocks], "tokens_per_s": block_rates,
+                   "spread": block_spread, "pooled_tokens_per_s": tokens_per_s,
+                   "spread_definition": "(max - min) / mean of the blocks' rates"},
         "roofline": ({
             "bound": "hbm",
             "kernel": "w4a16_ffn_kernel<gate/up> (W4A16 gate/up + SiLU*up)",
@@ -467,12 +471,119 @@ def main():
                     "timing": "per-kernel HIP events, eager steps"},
         "kernel_us": mean_us,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
+        "prefill": prefill,
         "setup_s": {"generate_inputs": gen_s},
     }
     if Is:
         out["shared_hbm"] = {"bytes_per_step": shared_bytes,
                              "achieved_gbs": shared_bytes / (mean_us["shared"] * 1e-6) / 1e9}
     print(json.dumps(out))
+
+
+def host_threads() -> int:
+    """Host threads the baselines use: the CPUs this process may run on, at most 16 (the
+    CPU share of one GPU on the benchmark machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baselines(args, xs_np, wr_np, rows_np, shared_np, H, I, E, k, T, S, y_gpu):
+    """The oracle (plain C, fp64) on a bounded sample of the workload's input batches: one
+    thread, then every host thread on the same batches (each thread runs whole tokens; a
+    token's output depends on that token only, so the arithmetic is the same)."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    n_calls, cpu_s, tok = 0, 0.0, 0
+    parity_norm = None
+    Tc = args.cpu_tokens or (32 if args.config == "prefill" else T)
+    Tc = min(Tc, T)
+    while cpu_s < args.cpu_seconds and n_calls < S:
+        tc = time.perf_counter()
+        ref = oracle.layer(xs_np[n_calls][:Tc], wr_np, rows_np, H, I, E, k, shared=shared_np)
+        cpu_s += time.perf_counter() - tc
+        tok += Tc
+        if n_calls == 0:
+            # every token's output depends on that token only: compare the sampled rows
+            yr = ref["y"].view(np.float16).astype(np.float64)
+            d = np.abs(yr - y_gpu[:Tc].astype(np.float64))
+            parity_norm = float((d / np.abs(yr).max(axis=1, keepdims=True)).max())
+        n_calls += 1
+    one = {"value": tok / cpu_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"{n_calls} oracle layer call(s) of {Tc} of the batch's {T} tokens on the same inputs "
+                     f"({cpu_s:.1f} s, single-threaded C, fp64)",
+           "gpu_vs_oracle_normwise_err": parity_norm}
+    nt = host_threads()
+    per = max(1, -(-Tc // nt))
+    tasks = [(b, a, min(Tc, a + per)) for b in range(n_calls) for a in range(0, Tc, per)]
+
+    def run(task):
+        b, a, e = task
+        oracle.layer(xs_np[b][a:e], wr_np, rows_np, H, I, E, k, shared=shared_np)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        list(ex.map(run, tasks))
+    wall = time.perf_counter() - t0
+    allc = {"value": tok / wall, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"the same {n_calls} batch(es) of {Tc} tokens, {len(tasks)} token chunks on {nt} host "
+                      f"threads ({wall:.1f} s wall)"}
+    return one, allc
+
+
+def measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, rounds=3):
+    """Prefill-sized layer on the same expert shape (T = 4096, uniform router init, the
+    grouped-GEMM path): HIP events around back-to-back launches of each phase over the weight
+    replicas, on the launch stream.  Useful FLOPs: gate/up 2*T*k*H*2I, down 2*T*k*I*H."""
+    cfg = synth.CONFIGS["prefill"]
+    T, H, I, E, k = max(cfg.batches), cfg.H, cfg.I, cfg.E, cfg.k
+    router = torch.from_numpy(synth.make_router(cfg)).to(dev)
+    x = torch.from_numpy(synth.make_x(cfg, T)).to(dev)
+    lay = RoutedExpertLayer(H, I, E, k, replicas[0], router, max_T=T, device=dev)
+    y = torch.empty((T, H), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    R = len(replicas)
+
+    def gateup(r):
+        B.moe_w4a16_gateup(x, T, H, I, E, k, replicas[r], lay.row_stride, None, lay.expert_offsets,
+                           lay.sorted_pairs, lay.active_list, lay.n_active, lay.h, lay.status)
+
+    def down(r):
+        B.moe_w4a16_down(T, H, I, E, k, replicas[r], lay.row_stride, None, lay.expert_offsets, lay.active_list,
+                         lay.n_active, lay.h, lay.pair_out, lay.status)
+
+    phases = {"route": lambda r: lay.route(x), "gateup": gateup, "down": down,
+              "combine": lambda r: lay.combine(T, y)}
+    for f in phases.values():           # warm each phase (and leave valid routing behind)
+        f(0)
+    torch.cuda.synchronize()
+    us = {}
+    for name, f in phases.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(rounds * R):
+            f(i % R)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us[name] = e0.elapsed_time(e1) * 1e3 / (rounds * R)
+    lay.check_status()
+    fl_gu, fl_dn = 2.0 * T * k * H * 2 * I, 2.0 * T * k * I * H
+    tf = lambda fl, t: fl / (t * 1e-6) / 1e12
+    layer_us = sum(us.values())
+    return {
+        "workload": f"prefill_T{T} (E {E}, top-{k}, H {H}, I {I})",
+        "kernel_us": us,
+        "gateup": {"tflops": tf(fl_gu, us["gateup"]), "frac": tf(fl_gu, us["gateup"]) / FP16_MFMA_PEAK_TFLOPS},
+        "down": {"tflops": tf(fl_dn, us["down"]), "frac": tf(fl_dn, us["down"]) / FP16_MFMA_PEAK_TFLOPS},
+        "ffn": {"us": us["gateup"] + us["down"], "tflops": tf(fl_gu + fl_dn, us["gateup"] + us["down"]),
+                "frac": tf(fl_gu + fl_dn, us["gateup"] + us["down"]) / FP16_MFMA_PEAK_TFLOPS},
+        "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
+        "layer_us": layer_us, "layer_tokens_per_s": T / (layer_us * 1e-6),
+        "timing": f"HIP events around {rounds * R} back-to-back launches of each phase over {R} weight replicas",
+    }
 
 
 def pinned_h2d_gbs(torch, dev, nbytes=256 << 20, reps=8):

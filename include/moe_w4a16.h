@@ -317,7 +317,7 @@ int moe_table_device(const moe_table *table, const void **rows_dev, size_t *row_
  * miss_out (capacity n), their number to *n_miss. */
 int moe_table_misses(moe_table *table, const int32_t *active_host, int n, int32_t *miss_out, int *n_miss);
 /* One miss transaction for the n experts (none may be published already);
- * `stream` (a consumer stream, or NULL) is ordered after the publication.
+ * `stream` (NULL = the default stream) is ordered after the publication.
  * n = 0 publishes nothing. */
 int moe_upload_expert_rows(moe_table *table, const int32_t *expert_ids, int n, void *stream);
 /* Captures the current generation; `stream` is ordered after its publication. */

@@ -146,7 +146,7 @@ public:
     int h2d_async(void *dst, const void *src, size_t n, void *s) override
     {
         if (++n_h2d == fail_h2d_at) return err("simulated copy failure");
-        Op op{Op::COPY};
+        Op op{Op::COPY, nullptr, nullptr, 0, nullptr, 0, {}, {}};
         op.dst = dst;
         op.src = src;
         op.n = n;
@@ -158,7 +158,7 @@ public:
         if (++n_record == fail_record_at) return err("simulated record failure");
         SimEvent *ev = static_cast<SimEvent *>(e);
         ev->owner = st(s);
-        Op op{Op::RECORD};
+        Op op{Op::RECORD, nullptr, nullptr, 0, nullptr, 0, {}, {}};
         op.ev = ev;
         op.seq = ++ev->recorded;
         st(s)->ops.push_back(op);
@@ -179,7 +179,7 @@ public:
     {
         if (++n_wait == fail_wait_at) return err("simulated wait failure");
         SimEvent *ev = static_cast<SimEvent *>(e);
-        Op op{Op::WAIT};
+        Op op{Op::WAIT, nullptr, nullptr, 0, nullptr, 0, {}, {}};
         op.ev = ev;
         op.seq = ev->recorded;               // the latest record at the time of the call
         st(s)->ops.push_back(op);
@@ -193,7 +193,7 @@ public:
     int publish(int32_t *map_dev, const int32_t *slots, int E, void *s) override
     {
         if (++n_publish == fail_publish_at) return err("simulated publish failure");
-        Op op{Op::PUBLISH};
+        Op op{Op::PUBLISH, nullptr, nullptr, 0, nullptr, 0, {}, {}};
         op.dst = map_dev;
         op.slots.assign(slots, slots + E);
         st(s)->ops.push_back(op);
@@ -210,17 +210,21 @@ public:
     }
     void call(SimStream *s, std::function<void()> fn)
     {
-        Op op{Op::CALL};
+        Op op{Op::CALL, nullptr, nullptr, 0, nullptr, 0, {}, {}};
         op.fn = std::move(fn);
-        s->ops.push_back(op);
+        st(s)->ops.push_back(op);
     }
     void run_all()
     {
         for (auto &s : streams) run_stream(s.get(), nullptr);
+        run_stream(&default_stream, nullptr);
     }
 
+    // the stream a null handle stands for (HIP's default stream)
+    SimStream default_stream;
+
 private:
-    static SimStream *st(void *s) { return static_cast<SimStream *>(s); }
+    SimStream *st(void *s) { return s ? static_cast<SimStream *>(s) : &default_stream; }
     int alloc(void **p, size_t n)
     {
         *p = std::malloc(n ? n : 1);
@@ -324,6 +328,8 @@ struct Stepper {
     tcore::Table &t;
     const Source &src;
     SimStream *consumer;
+    SimStream *uploader = nullptr;            // stream passed to the upload (consumer if null)
+    bool own_uploader = false;
     int bad_reads = 0, reads = 0;
     int step(const std::vector<int32_t> &active, bool run_consumer)
     {
@@ -331,7 +337,7 @@ struct Stepper {
         int nm = 0;
         int rc = t.misses(active.data(), (int)active.size(), miss.data(), &nm);
         if (rc) return rc;
-        rc = t.upload(miss.data(), nm, consumer);
+        rc = t.upload(miss.data(), nm, own_uploader ? uploader : consumer);
         if (rc) return rc;
         moe_table_lease lease;
         rc = t.acquire(consumer, &lease);
@@ -393,11 +399,13 @@ void scenario_steps()
             const int n = 1 + (int)(rng() % (uint32_t)(max_tokens * k));
             auto act = random_active(rng, 16, n, s & 1);
             active_total += act.size();
-            const int rc = st.step(act, (s % 7) == 0);
+            // either the consumer runs at once and the copy stream only when
+            // forced, or the copy stream runs ahead of a lazy consumer
+            const bool consumer_first = rng() & 1;
+            const int rc = st.step(act, consumer_first);
             CHECK(rc == MOE_OK, "step %d rc %d", s, rc);
             if (rc) break;
-            // the copy stream runs ahead of the consumers
-            tr.stream_sync(tr.streams[0].get());
+            if (!consumer_first) tr.stream_sync(tr.streams[0].get());
         }
         tr.run_all();
         CHECK(st.bad_reads == 0, "%d bad reads of %d", st.bad_reads, st.reads);
@@ -416,6 +424,33 @@ void scenario_steps()
         CHECK(pub <= (capacity > max_tokens * k ? capacity : max_tokens * k), "published %d", pub);
         delete t;
     }
+}
+
+void scenario_default_stream_consumer()
+{
+    // The consumer passes the null handle (the default stream): it must still
+    // be ordered after each publication and its reads covered by its release.
+    const Source src({16, 256, 512}, 9);
+    SimTransport tr;
+    moe_table_desc d = desc_of(src, 5, 7, 2, 2, 3);
+    tcore::Table *t = nullptr;
+    CHECK(tcore::Table::create(&tr, &d, &t) == MOE_OK, "create");
+    if (!t) return;
+    // the transactions order another stream; the lease alone must order
+    // the default stream after the publication
+    Stepper st{tr, *t, src, nullptr, tr.new_stream(), true};
+    std::mt19937 rng(3);
+    for (int s = 0; s < 100; ++s) {
+        // the consumer runs as soon as it is enqueued, the copy stream only
+        // when a wait forces it (or every third step)
+        const int rc = st.step(random_active(rng, 16, 1 + (int)(rng() % 6u), 1), true);
+        CHECK(rc == MOE_OK, "step %d rc %d", s, rc);
+        if (rc) break;
+        if (s % 3 == 2) tr.stream_sync(tr.streams[0].get());
+    }
+    tr.run_all();
+    CHECK(st.bad_reads == 0 && st.reads == 100, "%d bad reads of %d", st.bad_reads, st.reads);
+    delete t;
 }
 
 void scenario_staging_reuse()
@@ -638,6 +673,7 @@ int main(int argc, char **argv)
     const std::string which = argc > 1 ? argv[1] : "all";
     const std::pair<const char *, void (*)()> all[] = {
         {"steps", scenario_steps},
+        {"default_stream", scenario_default_stream_consumer},
         {"staging", scenario_staging_reuse},
         {"lease", scenario_open_lease_holds_rows},
         {"fail_before", scenario_failure_before_publication},

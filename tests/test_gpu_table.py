@@ -115,7 +115,7 @@ def test_uploads_publish_lru_and_bytes():
         assert np.array_equal(dev_map, model.published()), "device map differs from the host mirror"
         row_bytes = synth.expert_row_layout(cfg.H, cfg.I)["row_bytes"]
         for e, s in model.slot_of.items():
-            assert np.array_equal(read_device(rows_dev + s * stride, row_bytes), rows[e, :row_bytes]), \
+            assert np.array_equal(read_device(rows_dev + int(s) * stride, row_bytes), rows[e, :row_bytes]), \
                 f"device row of expert {e} (slot {s}) differs from the host source"
         tab.release(lease)
     st = tab.stats()
@@ -156,7 +156,8 @@ def test_open_lease_holds_rows_then_release_frees_them():
     row_bytes = synth.expert_row_layout(cfg.H, cfg.I)["row_bytes"]
     for e in (6, 7):
         assert m[e] >= 0
-        assert np.array_equal(read_device(lease.rows_dev + m[e] * lease.row_stride, row_bytes), rows[e, :row_bytes])
+        assert np.array_equal(read_device(lease.rows_dev + int(m[e]) * lease.row_stride, row_bytes),
+                              rows[e, :row_bytes])
     tab.release(lease)
     with pytest.raises(B.MoeError) as ei:          # an expert already published is not a miss
         B.moe_upload_expert_rows(tab.handle, np.array([6], np.int32))

@@ -294,8 +294,8 @@ public:
     }
 
     // One miss transaction: copies the n experts' rows into free spare rows
-    // and publishes the next generation; `consumer` (may be null) is ordered
-    // after the publication.
+    // and publishes the next generation; `consumer` is ordered after the
+    // publication (a null handle is the default stream, as in HIP).
     int upload(const int32_t *ids, int n, void *consumer)
     {
         if (faulted_) return fail(MOE_ERR_FAULTED, "moe_upload_expert_rows: the table faulted earlier");
@@ -376,7 +376,7 @@ public:
         for (int i = 0; i < n; ++i) expert_in_[target[i]] = ids[i];
         slot_of_.swap(next);
         ctr_.generation = gen_;
-        if (consumer && tr_->stream_wait(consumer, published_[gen_ % kMaps]) != 0) {
+        if (tr_->stream_wait(consumer, published_[gen_ % kMaps]) != 0) {
             faulted_ = true;
             return fail(MOE_ERR_FAULTED, "moe_upload_expert_rows: ordering the consumer stream after publication "
                         "failed (%s); the table is faulted", tr_->message());
@@ -385,11 +385,11 @@ public:
     }
 
     // Captures the current generation for a consumer on `stream` (ordered
-    // after its publication).
+    // after its publication; a null handle is the default stream).
     int acquire(void *stream, moe_table_lease *out)
     {
         if (faulted_) return fail(MOE_ERR_FAULTED, "moe_table_acquire: the table faulted earlier");
-        if (stream && tr_->stream_wait(stream, published_[gen_ % kMaps]) != 0)
+        if (tr_->stream_wait(stream, published_[gen_ % kMaps]) != 0)
             return fail(MOE_ERR_HIP, "moe_table_acquire: %s", tr_->message());
         GenRec &g = rec(gen_);
         g.open++;
