@@ -140,6 +140,23 @@ int moe_route_exact(const void *x_dev, const void *w_router_dev, const float *bi
                     int32_t *active_list_dev, int32_t *n_active_dev,
                     void *ws_dev, size_t ws_bytes, void *stream);
 
+/* moe_route_static: moe_route without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a fixed array of
+ * moe_route_static_max_bytes() bytes (1 MiB) inside this library, one per
+ * device, held until the process ends; the call itself allocates nothing.
+ * Shapes whose workspace would exceed it (moe_route_workspace_size(T, H, E)
+ * > the maximum, e.g. T > 4096 at E = 64) return MOE_ERR_WORKSPACE.  Every
+ * call on a device shares that device's array: calls that can overlap on one
+ * GPU (other streams, other threads) race and must not be issued.  Results
+ * are bit-identical to moe_route's. */
+size_t moe_route_static_max_bytes(void);
+int moe_route_static(const void *x_dev, const void *w_router_dev, const float *bias_dev,
+                     int T, int H, int E, int k,
+                     float *logits_dev, int32_t *topk_ids_dev, float *topk_w_dev,
+                     int32_t *expert_offsets_dev, int32_t *sorted_pairs_dev, int32_t *pair_pos_dev,
+                     int32_t *active_list_dev, int32_t *n_active_dev, void *stream);
+
 /* ------------------------------------------------------------ expert FFN
  * Expert rows are addressed as rows_dev + slot_map_dev[e] * row_stride
  * (slot_map_dev NULL means slot e for expert e).  row_stride >=

@@ -32,7 +32,7 @@ MOE_FFN_PATH_GEMM = 2
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
     "moe_version", "moe_last_error", "moe_expert_row_bytes",
-    "moe_route_workspace_size", "moe_route", "moe_route_exact",
+    "moe_route_workspace_size", "moe_route", "moe_route_exact", "moe_route_static_max_bytes", "moe_route_static",
     "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
     "moe_combine", "moe_shared_ffn_workspace_size", "moe_shared_ffn",
     "moe_row_digest", "moe_table_create", "moe_table_destroy", "moe_table_device", "moe_table_misses",
@@ -93,6 +93,10 @@ def load(path: str = LIB_PATH):
     L.moe_route_exact.restype = _i
     L.moe_route_exact.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                   _vp]
+    L.moe_route_static_max_bytes.restype = _sz
+    L.moe_route_static_max_bytes.argtypes = []
+    L.moe_route_static.restype = _i
+    L.moe_route_static.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.moe_w4a16_gateup.restype = _i
     L.moe_w4a16_gateup.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp]
     L.moe_w4a16_down.restype = _i
@@ -189,6 +193,17 @@ def moe_route_exact(x, w_router, bias, T, H, E, k, logits, topk_ids, topk_w, exp
     _check(load().moe_route_exact(_p(x), _p(w_router), _p(bias), T, H, E, k, _p(logits), _p(topk_ids), _p(topk_w),
                                   _p(expert_offsets), _p(sorted_pairs), _p(pair_pos), _p(active_list),
                                   _p(n_active), _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_route_static_max_bytes() -> int:
+    return int(load().moe_route_static_max_bytes())
+
+
+def moe_route_static(x, w_router, bias, T, H, E, k, logits, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                     pair_pos, active_list, n_active, stream=None):
+    _check(load().moe_route_static(_p(x), _p(w_router), _p(bias), T, H, E, k, _p(logits), _p(topk_ids),
+                                   _p(topk_w), _p(expert_offsets), _p(sorted_pairs), _p(pair_pos),
+                                   _p(active_list), _p(n_active), _s(stream)))
 
 
 def moe_w4a16_gateup(x, T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, sorted_pairs, active_list,

@@ -26,6 +26,7 @@
 #include "moe_internal.h"
 
 #include <climits>
+#include <mutex>
 
 namespace {
 
@@ -900,6 +901,66 @@ int moe_route_exact(const void *x_dev, const void *w_router_dev, const float *bi
     return route_launch(x_dev, w_router_dev, bias_dev, T, H, E, k, logits_dev, topk_ids_dev, topk_w_dev,
                         expert_offsets_dev, sorted_pairs_dev, pair_pos_dev, active_list_dev, n_active_dev, ws_dev,
                         ws_bytes, 1, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ allocation-free routing
+// moe_route_static: moe_route with its workspace in a fixed device array of
+// this library instead of a caller buffer, for callers that cannot allocate.
+namespace {
+
+constexpr size_t kStaticScratchBytes = (size_t)1 << 20;     // logits of 4096 tokens x 64 experts
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_dev[64];             // device address of `scratch`, per device ordinal
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there (host code must not use the array's name as an address).
+int scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return moe::fail(MOE_ERR_HIP, "moe_route_static: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return moe::fail(MOE_ERR_UNSUPPORTED, "moe_route_static: device ordinal %d", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return moe::fail(MOE_ERR_HIP, "moe_route_static: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_route_static_max_bytes(void) { return kStaticScratchBytes; }
+
+int moe_route_static(const void *x_dev, const void *w_router_dev, const float *bias_dev,
+                     int T, int H, int E, int k,
+                     float *logits_dev, int32_t *topk_ids_dev, float *topk_w_dev,
+                     int32_t *expert_offsets_dev, int32_t *sorted_pairs_dev, int32_t *pair_pos_dev,
+                     int32_t *active_list_dev, int32_t *n_active_dev, void *stream)
+{
+    moe::clear_error();
+    int rc = moe::check_shape(T, H, 0, E, k, false);
+    if (rc) return rc;
+    const size_t need = route_ws_bytes(T, E);
+    if (need > kStaticScratchBytes)
+        return moe::fail(MOE_ERR_WORKSPACE, "moe_route_static: T=%d, E=%d need %zu bytes of scratch; the fixed "
+                         "array holds %zu (use moe_route with a workspace)", T, E, need, kStaticScratchBytes);
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    return route_launch(x_dev, w_router_dev, bias_dev, T, H, E, k, logits_dev, topk_ids_dev, topk_w_dev,
+                        expert_offsets_dev, sorted_pairs_dev, pair_pos_dev, active_list_dev, n_active_dev, ws,
+                        kStaticScratchBytes, 0, stream);
 }
 
 }  // extern "C"
