@@ -75,9 +75,18 @@ def parse():
                          "replicas and input batches; each graph launch costs about 4.5 us, so one step per "
                          "graph is measurably slower)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--fused", action="store_true",
+                    help="run each step through the one-call layer (moe_layer_forward) instead of the separate calls")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="olmoe: skip the prefill measurement (T=4096, grouped GEMM) that the line carries")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="olmoe_stack: load each next layer's predicted experts while the current layer computes")
+    ap.add_argument("--staging", type=int, default=2, help="pinned staging rows per table (stack and partial)")
+    ap.add_argument("--fp16-slots", action="store_true",
+                    help="offload-qpacked profile: experts in FP16 execution slots (dequantized on the GPU).  With "
+                         "olmoe/qwen: the decode layer's expert FFN over qpacked rows and over FP16 slots, side by "
+                         "side; with olmoe_stack: the tables hold FP16 slots")
     ap.add_argument("--partial", action="store_true",
                     help="qwen: keep only the config's resident experts published (39 of 60) and upload the "
                          "misses of every step before its expert FFN, as olmoe_stack does")
@@ -164,6 +173,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.config == "olmoe_stack" or (args.config == "qwen" and args.partial):
         run_stack(args, torch, dev)
+        return
+    if args.fp16_slots:
+        run_compact_vs_expanded(args, torch, dev)
         return
     if args.kernel_only == "copy":
         # before any other device copy, so the copy kernels profiled are exactly these
@@ -263,6 +275,32 @@ def main():
 
     names = ["route", "gateup", "down"] + (["shared"] if Is else []) + ["combine"]
 
+    shared_done = torch.cuda.Event() if Is else None
+
+    def run_step_fused(s, ev=None):
+        """One step through the one-call layer (moe_layer_forward); the shared expert, where
+        the layer has one, runs on the second stream and the call's combine waits for it."""
+        r, x, _ = step_args(s)
+        rows = replicas[r]
+        main = torch.cuda.current_stream()
+        if ev is not None:
+            ev[0].record(stream)
+        if Is:
+            side.wait_stream(main)
+            Wsg, Wsu, Wsd, wg = shared_reps[r]
+            B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes, side)
+            shared_done.record(side)
+        B.moe_layer_forward(x, router, None, T, H, I, E, k, rows, lay.row_stride, None, sh_out if Is else None,
+                            sh_gate if Is else None, shared_done, y, lay._bufs, B.MOE_FFN_PATH_AUTO, main)
+        if Is:
+            main.wait_stream(side)
+        if ev is not None:
+            ev[1].record(stream)
+
+    if args.fused:
+        run_step = run_step_fused       # noqa: F811 (the timed steps and the event steps use the one call)
+        names = ["layer"]
+
     if args.kernel_only in ("gateup", "down"):
         lay.route(xs[0])
 
@@ -354,8 +392,8 @@ def main():
     mean_us = {n: float(dur[:, i].mean()) for i, n in enumerate(names)}
     gu_bytes_step = np.array([gateup_unit * step_args(s)[2] for s in range(n_ev)], dtype=np.float64)
     dn_bytes_step = np.array([down_unit * step_args(s)[2] for s in range(n_ev)], dtype=np.float64)
-    ffn_gbs = float((gu_bytes_step.mean() + dn_bytes_step.mean()) /
-                    ((mean_us["gateup"] + mean_us["down"]) * 1e-6) / 1e9)
+    ffn_us = mean_us["layer"] if args.fused else mean_us["gateup"] + mean_us["down"]
+    ffn_gbs = float((gu_bytes_step.mean() + dn_bytes_step.mean()) / (ffn_us * 1e-6) / 1e9)
 
     # ---------------------------------------------------------------- gate/up roofline: back-to-back launches
     lay.route(xs[0])
@@ -434,6 +472,7 @@ def main():
             "experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
             "shared_expert_intermediate": Is,
             "shared_expert_stream": "second stream, concurrent with routing and the routed experts" if Is else None,
+            "layer_call": "moe_layer_forward (one call)" if args.fused else "separate calls",
             "weights": "int4 qpacked, 256-value blocks, fp16 scales; fp16 activations, fp32 accumulation",
             "replicas": R, "input_batches": S, "graph_replay": not args.no_graph,
             "steps_per_graph": None if args.no_graph else G,
@@ -468,14 +507,15 @@ def main():
         }),
         "ffn_hbm": {"achieved_gbs": ffn_gbs, "frac": ffn_gbs / HBM_PEAK_GBS,
                     "qpacked_bytes_per_step": float(gu_bytes_step.mean() + dn_bytes_step.mean()),
-                    "timing": "per-kernel HIP events, eager steps"},
+                    "timing": ("HIP events around whole one-call layer steps (routing and combine included), "
+                               "eager" if args.fused else "per-kernel HIP events, eager steps")},
         "kernel_us": mean_us,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
         "prefill": prefill,
         "setup_s": {"generate_inputs": gen_s},
     }
-    if Is:
+    if Is and not args.fused:
         out["shared_hbm"] = {"bytes_per_step": shared_bytes,
                              "achieved_gbs": shared_bytes / (mean_us["shared"] * 1e-6) / 1e9}
     print(json.dumps(out))
@@ -586,6 +626,85 @@ def measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, rounds=3)
     }
 
 
+def run_compact_vs_expanded(args, torch, dev):
+    """The decode layer's expert FFN over qpacked rows (W4A16, converted in registers) and over
+    FP16 execution slots (the offload-qpacked profile: the same experts dequantized on the GPU
+    into FP16, read as stored), side by side on the same routing.  Each format rotates over enough
+    replicas for >= 1 GiB, so the weights stream from HBM; HIP events around each FFN call, and
+    around whole steps (route, FFN, combine) eager."""
+    from w4a16_routed_expert_amd import binding as B
+    from w4a16_routed_expert_amd import synth
+    from w4a16_routed_expert_amd.layer import RoutedExpertLayer
+    cfg = synth.CONFIGS[args.config]
+    T = args.tokens or max(cfg.batches)
+    H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+    S = args.inputs
+    rows_np = synth.make_expert_rows(cfg)
+    router = torch.from_numpy(synth.make_router(cfg)).to(dev)
+    xs = [torch.from_numpy(synth.make_x(cfg, T, step=s)).to(dev) for s in range(S)]
+    rows0 = torch.from_numpy(rows_np).to(dev)
+    qb, _ = B.moe_expert_row_bytes(H, I)
+    fb = B.moe_expert_row_bytes_fp16(H, I)
+    fstride = (fb + 255) // 256 * 256
+    slots0 = torch.empty((E, fstride), dtype=torch.uint8, device=dev)
+    B.moe_dequant_expert_rows(rows0, rows0.stride(0), slots0, fstride, E, H, I)
+    fmts = {"qpacked": (rows0, qb), "fp16_slots": (slots0, fb)}
+    reps = {}
+    for name, (r0, per) in fmts.items():
+        R = max(1, -(-(1 << 30) // (per * E)))
+        reps[name] = [r0] + [r0.clone() for _ in range(R - 1)]
+    lay = RoutedExpertLayer(H, I, E, k, rows0, router, max_T=T, device=dev)
+    y = torch.empty((T, H), dtype=torch.float16, device=dev)
+    n_act = []
+    for x in xs:
+        lay.route(x)
+        n_act.append(int(lay.n_active.cpu()[0]))
+    steps = max(args.steps // 10, 50)
+    out_f = {}
+    for name, rr in reps.items():
+        f16 = name == "fp16_slots"
+        e = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for s in range(args.warmup + steps):
+            x = xs[s % S]
+            ev = e[s - args.warmup] if s >= args.warmup else None
+            if ev:
+                ev[0].record()
+            lay.route(x)
+            if ev:
+                ev[1].record()
+            lay.ffn(x, rows=rr[s % len(rr)], fp16_slots=f16, mode=B.MOE_FFN_PATH_STREAM)
+            if ev:
+                ev[2].record()
+            lay.combine(T, y)
+            if ev:
+                ev[3].record()
+        torch.cuda.synchronize()
+        lay.check_status()
+        ffn_us = float(np.mean([v[1].elapsed_time(v[2]) for v in e])) * 1e3
+        step_us = float(np.mean([v[0].elapsed_time(v[3]) for v in e])) * 1e3
+        act = float(np.mean([n_act[(args.warmup + i) % S] for i in range(steps)]))
+        per = fmts[name][1]
+        out_f[name] = {"ffn_us": ffn_us, "step_us_eager": step_us, "tokens_per_s_eager": T / (step_us * 1e-6),
+                       "bytes_per_active_expert": per, "ffn_bytes_per_step": act * per,
+                       "ffn_gbs": act * per / (ffn_us * 1e-6) / 1e9,
+                       "ffn_frac_of_hbm_peak": act * per / (ffn_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                       "replicas": len(rr), "device_bytes_per_expert": per}
+    q, f = out_f["qpacked"], out_f["fp16_slots"]
+    out = {
+        "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode) / MFMA % (prefill)",
+        "value": q["tokens_per_s_eager"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": q["step_us_eager"] * 1e-3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}_decode_layer_T{T}_compact_vs_expanded", "experts": E, "top_k": k,
+                   "hidden": H, "intermediate": I, "tokens": T, "mean_active_experts": float(np.mean(n_act))},
+        "compact_vs_expanded": {"qpacked": q, "fp16_slots": f,
+                                "bytes_ratio": f["bytes_per_active_expert"] / q["bytes_per_active_expert"],
+                                "ffn_time_ratio": f["ffn_us"] / q["ffn_us"],
+                                "timing": f"HIP events, {steps} eager steps per format (route, expert FFN, combine)"},
+    }
+    print(json.dumps(out))
+
+
 def pinned_h2d_gbs(torch, dev, nbytes=256 << 20, reps=8):
     """Host-to-device rate from a pinned host buffer (hipMemcpyAsync of 256 MiB, HIP events): the
     link ceiling the miss uploads are judged against."""
@@ -604,15 +723,17 @@ def pinned_h2d_gbs(torch, dev, nbytes=256 << 20, reps=8):
 
 def run_stack(args, torch, dev):
     """Decode with partial residency: each layer keeps `resident` of its E experts published in a
-    resident expert table; a step routes each layer, brings the active expert list to the host,
-    uploads the misses from the layer's immutable host source through pinned staging, runs the
-    expert FFN on the table's rows (and the FP16 shared expert where the layer has one) and
-    combines.  Workloads: the OLMoE-shaped 16-layer stack with a Zipf-skewed router, and the
-    Qwen-shaped layer with 39 of 60 experts resident (--config qwen --partial).  No graphs: every
-    layer of every step has a host round trip."""
+    resident expert table.  Workloads: the OLMoE-shaped 16-layer stack with a Zipf-skewed router,
+    its layers chained by the residual stream (x_{l+1} = x_l + y_l), and the Qwen-shaped layer with
+    39 of 60 experts resident and its shared expert (--config qwen --partial).  A step routes each
+    layer, brings the active experts to the host, runs one miss transaction (the table's copy
+    stream), a lease on the new generation, the expert FFN on its rows, and the combine (layer.py
+    DecodeStack).  With --prefetch, layer l+1's router is also applied to x_l and its predicted
+    experts are loaded while layer l computes.  No graphs: every layer of every step has a host
+    round trip."""
     from w4a16_routed_expert_amd import binding as B
     from w4a16_routed_expert_amd import synth
-    from w4a16_routed_expert_amd.layer import ResidentExpertTable, RoutedExpertLayer
+    from w4a16_routed_expert_amd.layer import DecodeStack, ResidentExpertTable, RoutedExpertLayer, SharedExpert
     cfg = synth.CONFIGS[args.config]
     T = args.tokens or max(cfg.batches)
     L = args.layers or cfg.n_layers
@@ -622,88 +743,84 @@ def run_stack(args, torch, dev):
     S = max(1, args.inputs)
     t0 = time.time()
     host = [synth.make_expert_rows(cfg, layer=l) for l in range(L)]
-    layers, tables, xs, shared = [], [], [], []
+    layers, tables, shared = [], [], []
     for l in range(L):
         wr = torch.from_numpy(synth.make_router(cfg, layer=l)).to(dev)
         bias = torch.from_numpy(synth.make_zipf_bias(cfg, layer=l)).to(dev) if cfg.zipf_s else None
         if Is:
-            shared.append([torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in synth.make_shared(cfg, layer=l)])
-        tab = ResidentExpertTable(host[l], H, I, cfg.resident, spare, staging_rows=2, top_k=k, max_tokens=T)
+            shared.append(SharedExpert(*(torch.from_numpy(np.ascontiguousarray(m)).to(dev)
+                                         for m in synth.make_shared(cfg, layer=l)), max_T=T, device=dev))
+        tab = ResidentExpertTable(host[l], H, I, cfg.resident, spare, staging_rows=args.staging, top_k=k,
+                                  max_tokens=T, fp16_slots=args.fp16_slots)
         rows_dev, stride, _ = tab.device()
         lay = RoutedExpertLayer(H, I, E, k, torch.empty((1, stride), dtype=torch.uint8, device=dev), wr, bias,
                                 max_T=T, device=dev)
         layers.append(lay)
         tables.append(tab)
-        xs.append([torch.from_numpy(synth.make_x(cfg, T, step=s, layer=l)).to(dev) for s in range(S)])
+    x0s = [torch.from_numpy(synth.make_x(cfg, T, step=s)).to(dev) for s in range(S)]
     gen_s = time.time() - t0
-    y = torch.empty((T, H), dtype=torch.float16, device=dev)
-    sh_out = torch.empty((T, H), dtype=torch.float32, device=dev) if Is else None
-    sh_gate = torch.empty((T,), dtype=torch.float32, device=dev) if Is else None
-    sh_ws_bytes = B.moe_shared_ffn_workspace_size(T, H, Is) if Is else 0
-    sh_ws = torch.empty((max(sh_ws_bytes, 256),), dtype=torch.uint8, device=dev) if Is else None
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    ffn_us, ffn_bytes = [0.0], [0]
+    stack = DecodeStack(layers, tables, shared=shared if Is else None, prefetch=args.prefetch)
     row_bytes, _ = B.moe_expert_row_bytes(H, I)
+    if args.fp16_slots:
+        row_bytes = B.moe_expert_row_bytes_fp16(H, I)           # what the FFN reads per active expert
+    ffn_ev = []
 
-    def step(s, timed_ffn=False):
-        for l in range(L):
-            lay, tab, x = layers[l], tables[l], xs[l][s % S]
-            lay.route(x)
-            if Is:
-                Wsg, Wsu, Wsd, wg = shared[l]
-                B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes)
-            active = lay.active_experts()
-            tab.prepare(active)             # copies on the table's copy stream; this stream waits
-            lease = tab.acquire()
-            if timed_ffn:
-                ev[0].record()
-            lay.ffn(x, lease=lease)
-            if timed_ffn:
-                ev[1].record()
-                ev[1].synchronize()
-                ffn_us[0] += ev[0].elapsed_time(ev[1]) * 1e3
-                ffn_bytes[0] += len(active) * row_bytes
-            tab.release(lease)
-            lay.combine(T, y, shared_out=sh_out, shared_gate=sh_gate)
+    def timer(l, phase):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        ffn_ev.append((l, phase, e))
 
     for s in range(args.warmup):
-        step(s)
+        stack.step(x0s[s % S])
     torch.cuda.synchronize()
     base = [t.stats() for t in tables]
     K = args.steps
     t_start = time.perf_counter()
     for s in range(K):
-        step(args.warmup + s)
+        stack.step(x0s[(args.warmup + s) % S])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     after = [t.stats() for t in tables]
     delta = {n: sum(a[n] - b[n] for a, b in zip(after, base)) for n in after[0]}
-    # a separate pass with the expert FFN timed by events (adds a host wait per layer)
-    n_ffn = min(K, 16)
+    # a separate pass with the expert FFN of every layer timed by events
+    n_ffn = min(K, 8)
+    ffn_us = ffn_bytes = 0.0
     for s in range(n_ffn):
-        step(s, timed_ffn=True)
-    torch.cuda.synchronize()
-    ffn_gbs = ffn_bytes[0] / (ffn_us[0] * 1e-6) / 1e9
+        ffn_ev.clear()
+        stack.step(x0s[s % S], timer=timer)
+        torch.cuda.synchronize()
+        for l in range(L):
+            b = [e for (ll, ph, e) in ffn_ev if ll == l]
+            ffn_us += b[0].elapsed_time(b[1]) * 1e3
+            ffn_bytes += int(layers[l].n_active.cpu()[0]) * row_bytes
+    ffn_gbs = ffn_bytes / (ffn_us * 1e-6) / 1e9
     for lay in layers:
         lay.check_status()
     h2d_ceiling = pinned_h2d_gbs(torch, dev)
+    demand = delta["hits"] + delta["misses"]
     out = {
-        "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode)",
+        "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode) / MFMA % (prefill)",
         "value": T * K / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / K,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
         "config": {"workload": (f"olmoe_stack{L}" if args.config == "olmoe_stack" else f"{args.config}_decode_layer")
-                               + f"_T{T}_resident{cfg.resident}of{E}", "layers": L, "tokens": T,
-                   "experts": E, "top_k": k, "hidden": H, "intermediate": I, "resident": cfg.resident,
-                   "spare_rows": spare, "zipf_s": cfg.zipf_s, "shared_expert_intermediate": Is,
-                   "input_batches": S},
+                               + f"_T{T}_resident{cfg.resident}of{E}" + ("_prefetch" if args.prefetch else ""),
+                   "layers": L, "tokens": T, "experts": E, "top_k": k, "hidden": H, "intermediate": I,
+                   "resident": cfg.resident, "spare_rows": spare, "staging_rows": args.staging, "zipf_s": cfg.zipf_s,
+                   "shared_expert_intermediate": Is, "input_batches": S,
+                   "chain": "residual stream x_{l+1} = RN16(x_l + y_l)" if L > 1 else None,
+                   "prefetch": "next layer's router on x_l, loaded while layer l computes" if args.prefetch else None,
+                   "device_rows": "FP16 execution slots (offload-qpacked)" if args.fp16_slots else "qpacked"},
         "residency": {
-            "hit_rate": delta["hits"] / max(1, delta["hits"] + delta["misses"]),
+            "hit_rate": delta["hits"] / max(1, demand),
             "misses_per_step": delta["misses"] / K,
             "h2d_bytes_per_step": delta["h2d_bytes"] / K,
             "h2d_gbs": delta["h2d_bytes"] / elapsed / 1e9,
             "evictions_per_step": delta["evictions"] / K,
+            "prefetched_per_step": delta["prefetched"] / K,
+            "prefetch_hits_per_step": delta["prefetch_hits"] / K,
+            "prefetch_unused_per_step": delta["prefetch_unused"] / K,
             "staging_waits": delta["staging_waits"],
             "expert_d2h_bytes": delta["expert_d2h_bytes"], "host_writes": delta["host_writes"],
             "pinned_h2d_ceiling_gbs": h2d_ceiling,

@@ -207,6 +207,50 @@ int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
                          const int32_t *active_list_dev, const int32_t *n_active_dev,
                          void *h_dev, float *pair_out_dev, int32_t *status_dev, int mode, void *stream);
 
+/* ------------------------------------------------------------ whole layer
+ * moe_layer_forward: route -> gate/up + SiLU*up -> down -> combine in one call,
+ * with the results of moe_route, the FFN calls and moe_combine (the same
+ * kernels after the routing; y is bit-identical to the separate calls).
+ * Decode batches (the streaming kernels: mode STREAM, or AUTO with
+ * T*k < 64*E, and T <= 256) route in one launch instead of two: the block
+ * that finishes its logits last runs the top-k and the grouping (no block
+ * waits for another), so the layer is four launches with no host round trip
+ * (the pages' "top4-fused-v1" executor is prior art for fusing the layer:
+ * "Horizon RunMap - architecture", section "Regimes and executor
+ * boundaries").  Other batches run moe_route, moe_w4a16_expert_ffn and
+ * moe_combine in order.
+ * Buffers (device, caller-owned, sized for T): the routing outputs and the
+ * FFN intermediates of moe_route / moe_w4a16_expert_ffn, plus
+ *   ws / ws_bytes: moe_layer_workspace_size(T, H, E) bytes, 256-byte aligned,
+ *     ZERO-FILLED BEFORE ITS FIRST USE; every call leaves its counter zero
+ *     again (a workspace sized for T serves any T' <= T); not shared by calls
+ *     that can overlap.
+ * shared_out / shared_gate: the shared-expert terms (moe_shared_ffn) or both
+ * NULL; shared_ready_event: a hipEvent_t recorded after the shared expert (on
+ * another stream), waited for before the combine, or NULL when the shared
+ * terms are already ordered before the call on `stream`.
+ * mode: MOE_FFN_PATH_* as for the FFN calls. */
+typedef struct {
+    float *logits;                     /* FP32 [T][E] or NULL */
+    int32_t *topk_ids;                 /* [T][k] */
+    float *topk_w;                     /* [T][k] */
+    int32_t *expert_offsets;           /* [E+1] */
+    int32_t *sorted_pairs, *pair_pos;  /* [T*k] */
+    int32_t *active_list;              /* [E] */
+    int32_t *n_active;                 /* [1] */
+    void *h;                           /* FP16 [T*k][I], 16-byte aligned */
+    float *pair_out;                   /* FP32 [T*k][H], 16-byte aligned */
+    int32_t *status;                   /* [1] or NULL, as for the FFN calls */
+    void *ws;
+    size_t ws_bytes;
+} moe_layer_buffers;
+
+size_t moe_layer_workspace_size(int T, int H, int E);
+int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int I,
+                      int E, int k, const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                      const float *shared_out_dev, const float *shared_gate_dev, void *shared_ready_event,
+                      void *y_dev, const moe_layer_buffers *buffers, int mode, void *stream);
+
 /* ------------------------------------------------------------ shared expert
  * moe_shared_ffn: the FP16 shared expert of a layer that has one (non-routed
  * weights stay FP16: "horizonrunmap.com/en", section "08 / Precision &
@@ -291,7 +335,13 @@ typedef struct {
     size_t host_row_stride;            /* >= moe_expert_row_bytes(H, I) */
     const int32_t *initial_resident;   /* host: `capacity` distinct expert ids, or NULL for 0..capacity-1 */
     const uint64_t *row_digests;       /* host: E expected moe_row_digest values, or NULL */
+    int slot_format;                   /* MOE_SLOT_QPACKED: device rows are qpacked copies (the
+                                          resident-qpacked cache); MOE_SLOT_FP16: FP16 execution slots
+                                          (offload-qpacked: each miss is copied qpacked, then
+                                          dequantized on the GPU into its slot; the FFN reads the slots
+                                          with moe_fp16_expert_ffn) */
 } moe_table_desc;
+enum moe_slot_format { MOE_SLOT_QPACKED = 0, MOE_SLOT_FP16 = 1 };
 /* Creation rejects (MOE_ERR_CAPACITY) spare_rows below
  * min(E - capacity, A + max(0, A - capacity)) with A = min(E, max_tokens *
  * top_k): after a step at most max(capacity, A) experts stay published, and
@@ -308,6 +358,9 @@ typedef struct {
     uint64_t generation;               /* current generation (1 after creation) */
     uint64_t open_leases;              /* leases acquired and not released */
     uint64_t failed_uploads;           /* transactions that failed before publication */
+    uint64_t prefetched;               /* rows uploaded by moe_table_prefetch */
+    uint64_t prefetch_hits;            /* prefetched experts that a later step routed */
+    uint64_t prefetch_unused;          /* prefetched experts evicted before any step routed them */
 } moe_table_counters;
 
 typedef struct {
@@ -337,6 +390,18 @@ int moe_table_misses(moe_table *table, const int32_t *active_host, int n, int32_
  * `stream` (NULL = the default stream) is ordered after the publication.
  * n = 0 publishes nothing. */
 int moe_upload_expert_rows(moe_table *table, const int32_t *expert_ids, int n, void *stream);
+/* Speculative load of n experts a later step is expected to route (e.g. the
+ * next layer's experts predicted from the current activations): starts a
+ * step whose active set is these ids (the transaction's eviction keeps them)
+ * and uploads those without a published row as one transaction that no
+ * stream waits for, so the copies overlap whatever the GPU is running; the
+ * next moe_table_acquire orders its consumer after the publication.  Counted
+ * in prefetched / prefetch_hits / prefetch_unused, not as misses.  (The pages
+ * list speculative next-layer loading among related systems' staging
+ * semantics: "Horizon RunMap - Architecture, Experimental Evidence and
+ * Scope", "Architecture comparison matrix", row "Publication/staging
+ * semantics".) */
+int moe_table_prefetch(moe_table *table, const int32_t *expert_ids, int n);
 /* Captures the current generation; `stream` is ordered after its publication. */
 int moe_table_acquire(moe_table *table, void *stream, moe_table_lease *lease);
 /* Ends a lease; its consumers are the work enqueued on `stream` so far. */
@@ -356,6 +421,38 @@ int moe_table_published(const moe_table *table, int32_t *slot_map_host);
 int moe_combine(const float *pair_out_dev, const int32_t *pair_pos_dev, const float *topk_w_dev,
                 const float *shared_out_dev, const float *shared_gate_dev,
                 int T, int H, int k, void *y_dev, void *stream);
+
+/* ------------------------------------------------------------ FP16 execution slots
+ * The offload-qpacked profile ("Horizon RunMap - architecture", section
+ * "Historical contracts remain distinct"; "Horizon technical notes —
+ * publication edition v1", section "Precision is profile-specific"): a
+ * low-bit source dequantized into bounded FP16 execution slots.  Each weight
+ * of a slot is the FP16 value nearest (code - 8) * scale (rounded once; this
+ * profile's numbers differ from the exact W4A16 layer by that rounding).
+ * Slot row: gate [I][H], up [I][H], down [H][I] FP16, each matrix in
+ * 4096-byte tiles: tile (rg, kt) = rows 16rg..16rg+15 x columns
+ * 128kt..128kt+127 at byte (rg*K/128 + kt)*4096; its piece q (1024 bytes at
+ * q*1024) holds, at byte (16g + r)*16, row 16rg + r, columns
+ * 128kt + 32g + 8q .. +7 in order.  moe_expert_row_bytes_fp16(H, I) =
+ * 3*I*H*2 bytes.
+ * moe_dequant_expert_rows: n qpacked rows (stride q_stride) -> n slot rows
+ *   (stride f_stride); both 256-byte aligned, strides multiples of 256.
+ * moe_fp16_expert_ffn: moe_w4a16_expert_ffn over slot rows (same routing
+ *   inputs, rounding points, outputs and status; the streaming kernels). */
+size_t moe_expert_row_bytes_fp16(int H, int I);
+int moe_dequant_expert_rows(const void *q_rows_dev, size_t q_stride, void *f_rows_dev, size_t f_stride, int n, int H,
+                            int I, void *stream);
+int moe_fp16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
+                        const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                        const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
+                        const int32_t *active_list_dev, const int32_t *n_active_dev,
+                        void *h_dev, float *pair_out_dev, int32_t *status_dev, void *stream);
+
+/* ------------------------------------------------------------ residual stream
+ * out[i] = RN16(a[i] + b[i]) for FP16 a, b (n elements; out may alias a or
+ * b): the residual connection that chains layers of a stack, x_{l+1} = x_l +
+ * y_l (the sum of two FP16 values is exact in fp64 and rounded once). */
+int moe_residual_add(const void *a_dev, const void *b_dev, void *out_dev, long long n, void *stream);
 
 #ifdef __cplusplus
 }

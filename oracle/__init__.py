@@ -68,6 +68,9 @@ def lib():
         L.oracle_layer.argtypes = [_u16p, _u16p, _fp, _u8p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp, _u16p, _fp, _i32p,
                                    _dp, _u16p, _dp]
+        L.oracle_layer_fp16_slots.restype = ctypes.c_int
+        L.oracle_layer_fp16_slots.argtypes = L.oracle_layer.argtypes
+        L.oracle_dequant_expert_fp16.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
         L.oracle_halves_to_doubles.argtypes = [_u16p, _dp, ctypes.c_size_t]
         L.oracle_doubles_to_halves.argtypes = [_dp, _u16p, ctypes.c_size_t]
         _lib = L
@@ -133,11 +136,14 @@ def dequant_matrix(nib: np.ndarray, scales, R: int, K: int) -> np.ndarray:
     return out
 
 
-def dequant_expert(row: np.ndarray, H: int, I: int):
+def dequant_expert(row: np.ndarray, H: int, I: int, fp16: bool = False):
+    """The three matrices of a qpacked expert row as doubles; fp16=True gives the offload-qpacked
+    profile's FP16 execution-slot values (each weight rounded to FP16)."""
     row = np.ascontiguousarray(row, dtype=np.uint8)
     Wg = np.empty((I, H)); Wu = np.empty((I, H)); Wd = np.empty((H, I))
-    lib().oracle_dequant_expert(_ptr(row, ctypes.c_uint8), H, I, _ptr(Wg, ctypes.c_double),
-                                _ptr(Wu, ctypes.c_double), _ptr(Wd, ctypes.c_double))
+    f = lib().oracle_dequant_expert_fp16 if fp16 else lib().oracle_dequant_expert
+    f(_ptr(row, ctypes.c_uint8), H, I, _ptr(Wg, ctypes.c_double), _ptr(Wu, ctypes.c_double),
+      _ptr(Wd, ctypes.c_double))
     return Wg, Wu, Wd
 
 
@@ -225,11 +231,13 @@ def combine(o, w, os_=None, sigma=None):
 
 
 # ------------------------------------------------------------ whole layer
-def layer(x, wr, rows: np.ndarray, H: int, I: int, E: int, k: int, bias=None, shared=None, want_h=False):
+def layer(x, wr, rows: np.ndarray, H: int, I: int, E: int, k: int, bias=None, shared=None, want_h=False,
+          fp16_slots=False):
     """Oracle of the whole routed-expert layer.
 
     rows: uint8 [E, row_bytes] qpacked expert rows (expert e = rows[e]).
     shared: None or (Wsg, Wsu, Wsd, wgate) FP16 shared expert.
+    fp16_slots: the offload-qpacked profile (expert weights rounded to FP16 before use).
     Returns dict(y=FP16 bits [T,H], logits, ids, w, o [T*k,H] by pair t*k+j, h (opt.), and grouping).
     """
     x = _h(x); wr = _h(wr)
@@ -245,7 +253,8 @@ def layer(x, wr, rows: np.ndarray, H: int, I: int, E: int, k: int, bias=None, sh
     w = np.empty((T, k), dtype=np.float64)
     o = np.empty((n, H), dtype=np.float64)
     h = np.empty((n, I), dtype=np.uint16) if want_h else None
-    rc = lib().oracle_layer(_ptr(x, ctypes.c_uint16), _ptr(wr, ctypes.c_uint16), _ptr(b, ctypes.c_float),
+    f = lib().oracle_layer_fp16_slots if fp16_slots else lib().oracle_layer
+    rc = f(_ptr(x, ctypes.c_uint16), _ptr(wr, ctypes.c_uint16), _ptr(b, ctypes.c_float),
                             _ptr(rows, ctypes.c_uint8), row_bytes, T, H, I, E, k,
                             _ptr(os_, ctypes.c_double), _ptr(sig, ctypes.c_double),
                             _ptr(y, ctypes.c_uint16), _ptr(logits, ctypes.c_float), _ptr(ids, ctypes.c_int32),

@@ -278,6 +278,23 @@ void oracle_dequant_expert(const uint8_t *row, int H, int I, double *Wg, double 
     oracle_dequant_matrix(row + off[2], (const uint16_t *)(row + off[5]), H, I, Wd);
 }
 
+/* The offload-qpacked profile ("Horizon RunMap - architecture", section
+ * "Historical contracts remain distinct"; "Horizon technical notes —
+ * publication edition v1", section "Precision is profile-specific"): the
+ * low-bit source is dequantized into FP16 execution slots, so every weight is
+ * the FP16 value nearest (code - 8) * scale.  Same matrices as
+ * oracle_dequant_expert, each weight rounded to FP16. */
+void oracle_dequant_expert_fp16(const uint8_t *row, int H, int I, double *Wg, double *Wu, double *Wd)
+{
+    oracle_dequant_expert(row, H, I, Wg, Wu, Wd);
+    size_t n = (size_t)I * H;
+    for (size_t i = 0; i < n; ++i) {
+        Wg[i] = oracle_half_to_double(oracle_double_to_half(Wg[i]));
+        Wu[i] = oracle_half_to_double(oracle_double_to_half(Wu[i]));
+        Wd[i] = oracle_half_to_double(oracle_double_to_half(Wd[i]));
+    }
+}
+
 /* ------------------------------------------------ FP16 shared expert (A8) */
 
 /* Shared expert with FP16 weights, same rounding points as a routed expert:
@@ -338,11 +355,11 @@ void oracle_combine(const double *o, const double *w, const double *os, const do
  * w double [T][k], h FP16 [T*k][I] and o double [T*k][H] indexed by pair
  * p = t*k + j.  shared_os / shared_sigma: optional shared-expert terms
  * (double [T][H] and [T]).  Returns 0, or -1 on allocation failure. */
-int oracle_layer(const uint16_t *x, const uint16_t *wr, const float *bias, const uint8_t *rows,
-                 size_t row_bytes, int T, int H, int I, int E, int k,
-                 const double *shared_os, const double *shared_sigma,
-                 uint16_t *y, float *logits_out, int32_t *ids_out, double *w_out,
-                 uint16_t *h_out, double *o_out)
+static int layer_impl(const uint16_t *x, const uint16_t *wr, const float *bias, const uint8_t *rows,
+                      size_t row_bytes, int T, int H, int I, int E, int k,
+                      const double *shared_os, const double *shared_sigma,
+                      uint16_t *y, float *logits_out, int32_t *ids_out, double *w_out,
+                      uint16_t *h_out, double *o_out, int fp16_weights)
 {
     int n = T * k;
     float *logits = (float *)malloc(sizeof(float) * (size_t)T * E);
@@ -362,7 +379,8 @@ int oracle_layer(const uint16_t *x, const uint16_t *wr, const float *bias, const
         int used = 0;
         for (int p = 0; p < n; ++p) used |= (ids[p] == e);
         if (!used) continue;
-        oracle_dequant_expert(rows + (size_t)e * row_bytes, H, I, Wg, Wu, Wd);
+        if (fp16_weights) oracle_dequant_expert_fp16(rows + (size_t)e * row_bytes, H, I, Wg, Wu, Wd);
+        else oracle_dequant_expert(rows + (size_t)e * row_bytes, H, I, Wg, Wu, Wd);
         for (int p = 0; p < n; ++p) {
             if (ids[p] != e) continue;
             oracle_swiglu_dense(Wg, Wu, Wd, H, I, x + (size_t)(p / k) * H, h, o + (size_t)p * H);
@@ -378,6 +396,28 @@ int oracle_layer(const uint16_t *x, const uint16_t *wr, const float *bias, const
 done:
     free(logits); free(ids); free(w); free(o); free(h); free(Wg); free(Wu); free(Wd);
     return rc;
+}
+
+int oracle_layer(const uint16_t *x, const uint16_t *wr, const float *bias, const uint8_t *rows,
+                 size_t row_bytes, int T, int H, int I, int E, int k,
+                 const double *shared_os, const double *shared_sigma,
+                 uint16_t *y, float *logits_out, int32_t *ids_out, double *w_out,
+                 uint16_t *h_out, double *o_out)
+{
+    return layer_impl(x, wr, bias, rows, row_bytes, T, H, I, E, k, shared_os, shared_sigma, y, logits_out, ids_out,
+                      w_out, h_out, o_out, 0);
+}
+
+/* The same layer in the offload-qpacked profile: expert weights rounded to
+ * FP16 (oracle_dequant_expert_fp16), everything else unchanged. */
+int oracle_layer_fp16_slots(const uint16_t *x, const uint16_t *wr, const float *bias, const uint8_t *rows,
+                            size_t row_bytes, int T, int H, int I, int E, int k,
+                            const double *shared_os, const double *shared_sigma,
+                            uint16_t *y, float *logits_out, int32_t *ids_out, double *w_out,
+                            uint16_t *h_out, double *o_out)
+{
+    return layer_impl(x, wr, bias, rows, row_bytes, T, H, I, E, k, shared_os, shared_sigma, y, logits_out, ids_out,
+                      w_out, h_out, o_out, 1);
 }
 
 /* ------------------------------------------------------- array helpers */

@@ -16,10 +16,12 @@ def rows_of(name):
     return _ROWS[name]
 
 
-def gpu_layer(cfg, rows_np, wr, x, bias=None, slot_map=None, rows_dev=None, mode=None, shared=None):
+def gpu_layer(cfg, rows_np, wr, x, bias=None, slot_map=None, rows_dev=None, mode=None, shared=None, fused=False,
+              fp16_slots=False):
     """One layer call through the C ABI; mode: None (automatic) or a B.MOE_FFN_PATH_* value;
     shared: None or the FP16 shared expert (Wsg, Wsu, Wsd, wgate) as numpy arrays, run on a
-    second stream beside the routed experts."""
+    second stream beside the routed experts; fused: the one-call layer (moe_layer_forward)
+    instead of the separate calls."""
     import torch
     from w4a16_routed_expert_amd import binding as B
     from w4a16_routed_expert_amd.layer import RoutedExpertLayer, SharedExpert
@@ -31,11 +33,22 @@ def gpu_layer(cfg, rows_np, wr, x, bias=None, slot_map=None, rows_dev=None, mode
                           device=dev)
     if rows_dev is None:
         rows_dev = torch.from_numpy(rows_np).to(dev)
+    if fp16_slots:
+        # every expert's row dequantized on the GPU into an FP16 execution slot
+        fstride = (B.moe_expert_row_bytes_fp16(cfg.H, cfg.I) + 255) // 256 * 256
+        slots = torch.empty((rows_dev.shape[0], fstride), dtype=torch.uint8, device=dev)
+        B.moe_dequant_expert_rows(rows_dev, rows_dev.stride(0), slots, fstride, rows_dev.shape[0], cfg.H, cfg.I)
+        rows_dev = slots
     lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, rows_dev, torch.from_numpy(wr).to(dev),
                             None if bias is None else torch.from_numpy(bias).to(dev),
                             None if slot_map is None else torch.from_numpy(slot_map).to(dev),
                             max_T=max(T, 1), device=dev)
-    y = lay.forward(torch.from_numpy(x).to(dev), mode=B.MOE_FFN_PATH_AUTO if mode is None else mode, shared=sh)
+    xd = torch.from_numpy(x).to(dev)
+    if fp16_slots:
+        y = lay.forward(xd, shared=sh, fp16_slots=True)
+    else:
+        fwd = lay.forward_fused if fused else lay.forward
+        y = fwd(xd, mode=B.MOE_FFN_PATH_AUTO if mode is None else mode, shared=sh)
     torch.cuda.synchronize()
     n = T * cfg.k
     na = int(lay.n_active.cpu()[0]) if T else 0

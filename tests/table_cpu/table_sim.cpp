@@ -453,6 +453,52 @@ void scenario_default_stream_consumer()
     delete t;
 }
 
+void scenario_prefetch()
+{
+    // Before each step, a speculative load of a guess of its active set (some
+    // right, some wrong); the step's consumer still reads intact rows under
+    // either schedule, and every prefetched row is counted once as a hit, as
+    // unused (evicted first), or is still waiting.
+    const Source src({16, 256, 512}, 11);
+    SimTransport tr;
+    moe_table_desc d = desc_of(src, 5, 7, 2, 2, 3);
+    tcore::Table *t = nullptr;
+    CHECK(tcore::Table::create(&tr, &d, &t) == MOE_OK, "create");
+    if (!t) return;
+    Stepper st{tr, *t, src, tr.new_stream()};
+    std::mt19937 rng(5);
+    for (int s = 0; s < 200; ++s) {
+        auto act = random_active(rng, 16, 1 + (int)(rng() % 6u), 1);
+        std::vector<int32_t> guess;
+        for (int32_t e : act)
+            if (rng() % 4u) guess.push_back(e);                  // most of the real set
+        if (rng() & 1) guess.push_back((int32_t)(rng() % 16u));    // and a wrong one
+        std::vector<int32_t> uniq;
+        for (int32_t e : guess) {
+            bool dup = false;
+            for (int32_t u : uniq) dup |= u == e;
+            if (!dup) uniq.push_back(e);
+        }
+        const int rc0 = t->prefetch(uniq.data(), (int)uniq.size());
+        CHECK(rc0 == MOE_OK, "prefetch %d rc %d", s, rc0);
+        const bool consumer_first = rng() & 1;
+        if (!consumer_first && (rng() & 1)) tr.stream_sync(tr.streams[0].get());
+        const int rc = st.step(act, consumer_first);
+        CHECK(rc == MOE_OK, "step %d rc %d", s, rc);
+        if (rc0 || rc) break;
+        if (!consumer_first) tr.stream_sync(tr.streams[0].get());
+    }
+    tr.run_all();
+    CHECK(st.bad_reads == 0, "%d bad reads of %d", st.bad_reads, st.reads);
+    moe_table_counters c;
+    t->stats(&c);
+    CHECK(c.prefetched > 0 && c.prefetch_hits > 0, "prefetched %llu, hits %llu", (unsigned long long)c.prefetched,
+          (unsigned long long)c.prefetch_hits);
+    CHECK(c.prefetch_hits + c.prefetch_unused <= c.prefetched, "prefetch accounting");
+    CHECK(c.h2d_bytes == (c.misses + c.prefetched) * src.row_bytes, "h2d bytes");
+    delete t;
+}
+
 void scenario_staging_reuse()
 {
     // One staging buffer, three misses: each refill waits for the previous
@@ -663,7 +709,7 @@ void scenario_threads()
     for (auto &t : th) t.join();
     for (int w = 0; w < 4; ++w) CHECK(bad[w] == 0 && errs[w] == 0, "thread %d: %d bad reads, %d errors", w, bad[w],
                                       errs[w]);
-    CHECK(tcore::CopyPool::get().workers() == 3, "copy pool workers");
+    CHECK(tcore::CopyPool::get().workers() == tcore::CopyPool::configured_workers(), "copy pool workers");
 }
 
 }  // namespace
@@ -674,6 +720,7 @@ int main(int argc, char **argv)
     const std::pair<const char *, void (*)()> all[] = {
         {"steps", scenario_steps},
         {"default_stream", scenario_default_stream_consumer},
+        {"prefetch", scenario_prefetch},
         {"staging", scenario_staging_reuse},
         {"lease", scenario_open_lease_holds_rows},
         {"fail_before", scenario_failure_before_publication},

@@ -266,3 +266,89 @@ def test_qwen_partial_residency_with_shared_expert_T64():
         assert_close_rows(part[s], ref["y"], f"qwen partial T=64 step {s} vs oracle")
     assert tab.stats()["misses"] > 0
     tab.close()
+
+
+def test_residual_add_is_the_correctly_rounded_sum():
+    # out = RN16(a + b): random values over the FP16 range, plus pairs whose sum
+    # needs more bits than FP32 holds (a large value and a tiny one) and sums on
+    # FP16 rounding midpoints
+    from w4a16_routed_expert_amd import binding as B
+    g = np.random.default_rng(3)
+    a = (g.standard_normal(50_000) * np.exp2(g.integers(-14, 14, 50_000))).astype(np.float16)
+    b = (g.standard_normal(50_000) * np.exp2(g.integers(-24, 14, 50_000))).astype(np.float16)
+    a[:4] = np.array([2048.0, 1.0, 65504.0, -0.5], np.float16)
+    b[:4] = np.array([1.0, 2.0 ** -11, 8.0, 2.0 ** -24], np.float16)      # ties and far-apart magnitudes
+    want = oracle.double_to_half(oracle.half_to_double(a.view(np.uint16)) + oracle.half_to_double(b.view(np.uint16)))
+    dev = torch.device("cuda:0")
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    out = torch.empty_like(ta)
+    B.moe_residual_add(ta, tb, out, a.size)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want), f"{int((got != want).sum())} sums differ"
+
+
+def make_stack(cfg, L, T, prefetch, layer0=0):
+    from w4a16_routed_expert_amd.layer import DecodeStack, RoutedExpertLayer
+    dev = torch.device("cuda:0")
+    layers, tables, host = [], [], []
+    for l in range(layer0, layer0 + L):
+        rows = synth.make_expert_rows(cfg, layer=l)
+        host.append((rows, synth.make_router(cfg, layer=l), synth.make_zipf_bias(cfg, layer=l)))
+        tab = make_table(cfg, rows, cfg.resident, min(cfg.E - cfg.resident, T * cfg.k), max_tokens=T)
+        _, stride, _ = tab.device()
+        layers.append(RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.empty((1, stride), dtype=torch.uint8,
+                                                                               device=dev),
+                                        torch.from_numpy(host[-1][1]).to(dev), torch.from_numpy(host[-1][2]).to(dev),
+                                        max_T=T, device=dev))
+        tables.append(tab)
+    return DecodeStack(layers, tables, prefetch=prefetch), host
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_stack_prefetch_is_transparent_and_layers_match_the_oracle(T):
+    # Four chained layers of the OLMoE-shaped stack (Zipf-biased routers, 40 of
+    # 64 experts resident), three steps, with and without next-layer prefetch:
+    # every layer's y and the stack's output are bit-identical either way;
+    # prefetch turns demand misses into prefetch hits; each layer's y matches
+    # the oracle on that layer's input, and the residual chain matches its
+    # definition.
+    from layer_util import oracle_tokens
+    cfg = synth.CONFIGS["olmoe_stack"]
+    L = 4
+    dev = torch.device("cuda:0")
+    runs = {}
+    for prefetch in (False, True):
+        stack, host = make_stack(cfg, L, T, prefetch)
+        outs = []
+        for s in range(3):
+            x0 = torch.from_numpy(synth.make_x(cfg, T, step=30 + s)).to(dev)
+            ys = []
+            xL = stack.step(x0, ys=ys)
+            torch.cuda.synchronize()
+            for lay in stack.layers:
+                lay.check_status()
+            outs.append(([y.cpu().numpy().view(np.uint16).copy() for y in ys], xL.cpu().numpy().view(np.uint16)))
+        st = [t.stats() for t in stack.tables]
+        for t in stack.tables:
+            t.close()
+        runs[prefetch] = (outs, st, host)
+    for s in range(3):
+        for l in range(L):
+            assert np.array_equal(runs[False][0][s][0][l], runs[True][0][s][0][l]), f"step {s} layer {l}: y differs"
+        assert np.array_equal(runs[False][0][s][1], runs[True][0][s][1]), f"step {s}: stack output differs"
+    plain, pre = runs[False][1], runs[True][1]
+    assert sum(t["prefetched"] for t in plain) == 0
+    assert sum(t["prefetch_hits"] for t in pre) > 0
+    assert sum(t["misses"] for t in pre) < sum(t["misses"] for t in plain), "prefetch did not remove demand misses"
+    # per-layer oracle on the first step, with the chain rebuilt from the GPU's own y
+    ys, xL = runs[True][0][0]
+    host = runs[True][2]
+    x = synth.make_x(cfg, T, step=30)
+    for l in range(L):
+        rows, wr, bias = host[l]
+        ref = oracle_tokens(x, wr, rows, cfg, bias=bias)
+        assert_close_rows(ys[l], ref["y"], f"stack layer {l} T={T} vs oracle")
+        x = oracle.double_to_half(oracle.half_to_double(x.view(np.uint16)) + oracle.half_to_double(ys[l]))
+        x = x.view(np.float16)
+    assert np.array_equal(x.view(np.uint16), xL), "residual chain differs from RN16(x + y)"

@@ -402,3 +402,60 @@ def test_combine_closed_form():
     os_ = np.array([[8.0, 8.0, 8.0]]); sig = np.array([0.5])
     y = oracle.combine(o, w, os_, sig)
     assert np.array_equal(y.view(np.float16).astype(np.float64), [[6.5, 5.0, 5.375]])
+
+
+# ----------------------------------------------- offload-qpacked profile (FP16 execution slots)
+def test_fp16_slot_weights_are_the_nearest_fp16_values():
+    # Every weight of the FP16-slot profile is (code - 8) * scale rounded to the
+    # nearest FP16 value, ties to even (numpy's float16 conversion, an
+    # independent implementation of that rounding); scales that leave values
+    # between FP16 neighbours, and large and subnormal results, included.
+    H, I = 256, 256
+    g = np.random.default_rng(21)
+    mats = []
+    for R, K in ((I, H), (I, H), (H, I)):
+        codes = g.integers(0, 16, size=(R, K)).astype(np.uint8)
+        scales = (g.random((R, (K + 255) // 256)) * 0.05).astype(np.float16)
+        scales[0, 0] = np.float16(65504.0)           # 7 * 65504 overflows FP16 -> inf
+        scales[1, 0] = np.float16(2.0 ** -24)        # results deep in the subnormal range
+        scales[2, 0] = np.float16(0.0123)
+        mats.append((codes, scales))
+    row = synth.pack_expert_row(H, I, *mats)
+    exact = oracle.dequant_expert(row, H, I)
+    slots = oracle.dequant_expert(row, H, I, fp16=True)
+    for e, s in zip(exact, slots):
+        with np.errstate(over="ignore"):
+            want = e.astype(np.float16).astype(np.float64)
+        assert np.array_equal(np.isinf(want), np.isinf(s))
+        fin = np.isfinite(want)
+        assert np.array_equal(s[fin], want[fin])
+    # the rounding changes something, so the profile is not silently the exact one
+    assert any(not np.array_equal(e, s) for e, s in zip(exact, slots))
+
+
+def test_fp16_slot_layer_equals_the_exact_layer_when_weights_are_fp16_values():
+    # With power-of-two scales every (code - 8) * scale is an FP16 value, so
+    # the offload-qpacked layer and the exact layer agree bit for bit; with
+    # ordinary scales they differ.
+    E, k, H, I, T = 4, 2, 256, 256, 5
+    g = np.random.default_rng(22)
+    rows = []
+    for e in range(E):
+        mats = []
+        for R, K in ((I, H), (I, H), (H, I)):
+            codes = g.integers(1, 16, size=(R, K)).astype(np.uint8)
+            scales = np.exp2(g.integers(-9, -4, size=(R, (K + 255) // 256))).astype(np.float16)
+            mats.append((codes, scales))
+        rows.append(synth.pack_expert_row(H, I, *mats))
+    rows = np.stack(rows)
+    x = g.standard_normal((T, H)).astype(np.float16)
+    wr = (g.standard_normal((H, E)) * 0.05).astype(np.float16)
+    a = oracle.layer(x, wr, rows, H, I, E, k, want_h=True)
+    b = oracle.layer(x, wr, rows, H, I, E, k, want_h=True, fp16_slots=True)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["h"], b["h"]) and np.array_equal(a["o"], b["o"])
+    x2, wr2, rows2 = _tiny_layer(E, k, H, I, T, seed=23)
+    packed = np.stack([r for r, _ in rows2])
+    c = oracle.layer(x2, wr2, packed, H, I, E, k)
+    d = oracle.layer(x2, wr2, packed, H, I, E, k, fp16_slots=True)
+    assert np.array_equal(c["ids"], d["ids"])                  # routing does not use expert weights
+    assert not np.array_equal(c["o"], d["o"])

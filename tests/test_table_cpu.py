@@ -6,7 +6,8 @@ consumer reading overwritten bytes) and whose calls can be made to fail.  It is
 built with g++ twice: with the address and undefined-behaviour sanitizers
 (every scenario) and with the thread sanitizer (several tables on several
 threads sharing the copy pool).  Scenarios: random decode steps against
-consumer reads, staging reuse after its copy retired, open leases holding rows
+consumer reads (consumer first or copies first), a consumer on the default
+stream, speculative prefetch before each step, staging reuse after its copy retired, open leases holding rows
 and maps, failures before publication (old generation intact and current),
 a failure after publication (table faulted), create-time rejections (spare
 rows, staging, digests, non-finite scales) and the source re-check.
@@ -42,7 +43,8 @@ def run(exe, scenario, env_extra):
 def test_table_state_machine_asan_ubsan(tmp_path):
     exe = build(tmp_path, "table_sim_asan", ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"])
     out = run(exe, "all", {"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0", "UBSAN_OPTIONS": "print_stacktrace=1"})
-    for name in ("steps", "staging", "lease", "fail_before", "fail_after", "create", "threads"):
+    for name in ("steps", "default_stream", "prefetch", "staging", "lease", "fail_before", "fail_after", "create",
+                 "threads"):
         assert f"{name}: ok" in out
 
 

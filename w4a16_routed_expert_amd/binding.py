@@ -25,6 +25,9 @@ MOE_ERR_FAULTED = 6
 MOE_ERR_ABSENT_EXPERT = 7
 MOE_ERR_SOURCE = 8
 
+MOE_SLOT_QPACKED = 0
+MOE_SLOT_FP16 = 1
+
 MOE_FFN_PATH_AUTO = 0
 MOE_FFN_PATH_STREAM = 1
 MOE_FFN_PATH_GEMM = 2
@@ -35,8 +38,10 @@ EXPORTS = (
     "moe_route_workspace_size", "moe_route", "moe_route_exact", "moe_route_static_max_bytes", "moe_route_static",
     "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
     "moe_combine", "moe_shared_ffn_workspace_size", "moe_shared_ffn",
+    "moe_layer_workspace_size", "moe_layer_forward", "moe_residual_add",
+    "moe_expert_row_bytes_fp16", "moe_dequant_expert_rows", "moe_fp16_expert_ffn",
     "moe_row_digest", "moe_table_create", "moe_table_destroy", "moe_table_device", "moe_table_misses",
-    "moe_upload_expert_rows", "moe_table_acquire", "moe_table_release", "moe_table_verify_source",
+    "moe_upload_expert_rows", "moe_table_prefetch", "moe_table_acquire", "moe_table_release", "moe_table_verify_source",
     "moe_table_stats", "moe_table_published",
 )
 
@@ -46,13 +51,22 @@ class TableDesc(ctypes.Structure):
                 ("spare_rows", ctypes.c_int), ("staging_rows", ctypes.c_int), ("top_k", ctypes.c_int),
                 ("max_tokens", ctypes.c_int), ("host_source", ctypes.c_void_p),
                 ("host_row_stride", ctypes.c_size_t), ("initial_resident", ctypes.c_void_p),
-                ("row_digests", ctypes.c_void_p)]
+                ("row_digests", ctypes.c_void_p), ("slot_format", ctypes.c_int)]
+
+
+class LayerBuffers(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p), ("sorted_pairs", ctypes.c_void_p), ("pair_pos", ctypes.c_void_p),
+                ("active_list", ctypes.c_void_p), ("n_active", ctypes.c_void_p), ("h", ctypes.c_void_p),
+                ("pair_out", ctypes.c_void_p), ("status", ctypes.c_void_p), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
 
 
 class TableCounters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("steps", "hits", "misses", "evictions", "h2d_bytes", "staging_waits",
                                                "expert_d2h_bytes", "host_writes", "generation", "open_leases",
-                                               "failed_uploads")]
+                                               "failed_uploads", "prefetched", "prefetch_hits",
+                                               "prefetch_unused")]
 
 
 class TableLease(ctypes.Structure):
@@ -112,6 +126,20 @@ def load(path: str = LIB_PATH):
     L.moe_shared_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]
     L.moe_row_digest.restype = ctypes.c_uint64
     L.moe_row_digest.argtypes = [_vp, _sz]
+    L.moe_layer_workspace_size.restype = _sz
+    L.moe_layer_workspace_size.argtypes = [_i, _i, _i]
+    L.moe_layer_forward.restype = _i
+    L.moe_layer_forward.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp,
+                                    ctypes.POINTER(LayerBuffers), _i, _vp]
+    L.moe_expert_row_bytes_fp16.restype = _sz
+    L.moe_expert_row_bytes_fp16.argtypes = [_i, _i]
+    L.moe_dequant_expert_rows.restype = _i
+    L.moe_dequant_expert_rows.argtypes = [_vp, _sz, _vp, _sz, _i, _i, _i, _vp]
+    L.moe_fp16_expert_ffn.restype = _i
+    L.moe_fp16_expert_ffn.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp]
+    L.moe_residual_add.restype = _i
+    L.moe_residual_add.argtypes = [_vp, _vp, _vp, ctypes.c_longlong, _vp]
     L.moe_table_create.restype = _i
     L.moe_table_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(TableDesc), _vp]
     L.moe_table_destroy.restype = None
@@ -122,6 +150,8 @@ def load(path: str = LIB_PATH):
     L.moe_table_misses.argtypes = [_vp, _vp, _i, _vp, ctypes.POINTER(_i)]
     L.moe_upload_expert_rows.restype = _i
     L.moe_upload_expert_rows.argtypes = [_vp, _vp, _i, _vp]
+    L.moe_table_prefetch.restype = _i
+    L.moe_table_prefetch.argtypes = [_vp, _vp, _i]
     L.moe_table_acquire.restype = _i
     L.moe_table_acquire.argtypes = [_vp, _vp, ctypes.POINTER(TableLease)]
     L.moe_table_release.restype = _i
@@ -240,6 +270,46 @@ def moe_shared_ffn(x, w_gate, w_up, w_down, w_sgate, T, H, Is, shared_out, share
                                  _p(shared_gate), _p(ws), ws_bytes, _s(stream)))
 
 
+def moe_layer_workspace_size(T, H, E) -> int:
+    return int(load().moe_layer_workspace_size(T, H, E))
+
+
+def layer_buffers(logits, topk_ids, topk_w, expert_offsets, sorted_pairs, pair_pos, active_list, n_active, h,
+                  pair_out, status, ws, ws_bytes) -> LayerBuffers:
+    return LayerBuffers(_p(logits), _p(topk_ids), _p(topk_w), _p(expert_offsets), _p(sorted_pairs), _p(pair_pos),
+                        _p(active_list), _p(n_active), _p(h), _p(pair_out), _p(status), _p(ws), ws_bytes)
+
+
+def moe_layer_forward(x, w_router, bias, T, H, I, E, k, rows, row_stride, slot_map, shared_out, shared_gate,
+                      shared_ready_event, y, buffers: LayerBuffers, mode=MOE_FFN_PATH_AUTO, stream=None):
+    """shared_ready_event: a torch.cuda.Event, a raw hipEvent_t address, or None."""
+    ev = shared_ready_event
+    if ev is not None and not isinstance(ev, int):
+        ev = ev.cuda_event
+    _check(load().moe_layer_forward(_p(x), _p(w_router), _p(bias), T, H, I, E, k, _p(rows), row_stride,
+                                    _p(slot_map), _p(shared_out), _p(shared_gate), ev, _p(y),
+                                    ctypes.byref(buffers), mode, _s(stream)))
+
+
+def moe_expert_row_bytes_fp16(H: int, I: int) -> int:
+    return int(load().moe_expert_row_bytes_fp16(H, I))
+
+
+def moe_dequant_expert_rows(q_rows, q_stride, f_rows, f_stride, n, H, I, stream=None):
+    _check(load().moe_dequant_expert_rows(_p(q_rows), q_stride, _p(f_rows), f_stride, n, H, I, _s(stream)))
+
+
+def moe_fp16_expert_ffn(x, T, H, I, E, k, rows, row_stride, slot_map, expert_offsets, sorted_pairs, active_list,
+                        n_active, h, pair_out, status=None, stream=None):
+    _check(load().moe_fp16_expert_ffn(_p(x), T, H, I, E, k, _p(rows), row_stride, _p(slot_map),
+                                      _p(expert_offsets), _p(sorted_pairs), _p(active_list), _p(n_active), _p(h),
+                                      _p(pair_out), _p(status), _s(stream)))
+
+
+def moe_residual_add(a, b, out, n, stream=None):
+    _check(load().moe_residual_add(_p(a), _p(b), _p(out), n, _s(stream)))
+
+
 # ------------------------------------------------------------------ resident expert table
 def moe_row_digest(a) -> int:
     """Digest of a host buffer (numpy array), the identity moe_table_create checks."""
@@ -249,14 +319,15 @@ def moe_row_digest(a) -> int:
 
 
 def moe_table_create(E, H, I, capacity, spare_rows, staging_rows, top_k, max_tokens, host_source, host_row_stride,
-                     initial_resident=None, row_digests=None, stream=None):
+                     initial_resident=None, row_digests=None, stream=None, slot_format=MOE_SLOT_QPACKED):
     """host_source: a C-contiguous uint8 numpy array [E, host_row_stride] that must outlive the table.
     Returns the table handle (an int)."""
     import numpy as np
     init = None if initial_resident is None else np.ascontiguousarray(initial_resident, dtype=np.int32)
     dig = None if row_digests is None else np.ascontiguousarray(row_digests, dtype=np.uint64)
     d = TableDesc(E, H, I, capacity, spare_rows, staging_rows, top_k, max_tokens, host_source.ctypes.data,
-                  host_row_stride, None if init is None else init.ctypes.data, None if dig is None else dig.ctypes.data)
+                  host_row_stride, None if init is None else init.ctypes.data, None if dig is None else dig.ctypes.data,
+                  slot_format)
     out = _vp()
     _check(load().moe_table_create(ctypes.byref(out), ctypes.byref(d), _s(stream)))
     return out.value
@@ -288,6 +359,12 @@ def moe_upload_expert_rows(table, expert_ids, stream=None):
     import numpy as np
     ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
     _check(load().moe_upload_expert_rows(table, ids.ctypes.data if len(ids) else None, len(ids), _s(stream)))
+
+
+def moe_table_prefetch(table, expert_ids):
+    import numpy as np
+    ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    _check(load().moe_table_prefetch(table, ids.ctypes.data if len(ids) else None, len(ids)))
 
 
 def moe_table_acquire(table, stream=None) -> TableLease:

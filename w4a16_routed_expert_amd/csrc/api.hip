@@ -62,9 +62,24 @@ size_t row_bytes(int H, int I, size_t *off6)
     return o;
 }
 
+size_t row_bytes_fp16(int H, int I, size_t *off6)
+{
+    if (H <= 0 || I <= 0 || H % 128 || I % 128) return 0;
+    const size_t m = (size_t)I * H * 2;        // one FP16 matrix, a multiple of 4096 bytes
+    if (off6) {
+        off6[0] = 0;
+        off6[1] = m;
+        off6[2] = 2 * m;
+        off6[3] = off6[4] = off6[5] = 3 * m;   // no scale planes
+    }
+    return 3 * m;
+}
+
 }  // namespace moe
 
 extern "C" {
+
+size_t moe_expert_row_bytes_fp16(int H, int I) { return moe::row_bytes_fp16(H, I, nullptr); }
 
 int moe_version(void) { return 100; }
 

@@ -21,45 +21,33 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *pair_out
     const int t = blockIdx.x / per_token;
     const int c4 = (blockIdx.x % per_token) * kThreads + threadIdx.x;
     if (c4 * 4 >= H) return;
-    // all k positions and weights first, then all k row loads, so the loads overlap
-    int pos[MOE_MAX_TOPK];
-    float w[MOE_MAX_TOPK];
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-        pos[j] = -1;
-        w[j] = 0.0f;
-        if (j < k) {
-            pos[j] = pair_pos[(size_t)t * k + j];
-            w[j] = topk_w[(size_t)t * k + j];
-        }
-    }
-    float4 v[MOE_MAX_TOPK];
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (pos[j] >= 0 && pos[j] < T * k)       // a corrupted grouping is skipped, never read out of bounds
-            v[j] = *reinterpret_cast<const float4 *>(pair_out + (size_t)pos[j] * H + c4 * 4);
-    }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-        if (j < k) {
-            acc.x += w[j] * v[j].x; acc.y += w[j] * v[j].y; acc.z += w[j] * v[j].z; acc.w += w[j] * v[j].w;
-        }
-    }
-    if (shared_out) {
-        const float g = shared_gate[t];
-        const float4 sv = *reinterpret_cast<const float4 *>(shared_out + (size_t)t * H + c4 * 4);
-        acc.x += g * sv.x; acc.y += g * sv.y; acc.z += g * sv.z; acc.w += g * sv.w;
-    }
-    const _Float16 hx = (_Float16)acc.x, hy = (_Float16)acc.y, hz = (_Float16)acc.z, hw = (_Float16)acc.w;
-    uint2 packed;
-    packed.x = (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
-    packed.y = (uint32_t)__builtin_bit_cast(uint16_t, hz) | ((uint32_t)__builtin_bit_cast(uint16_t, hw) << 16);
-    *reinterpret_cast<uint2 *>(y + (size_t)t * H + c4 * 4) = packed;
+    moe::combine_cols4(pair_out, pair_pos, topk_w, shared_out, shared_gate, T, H, k, t, c4, y);
+}
+
+// out = RN16(a + b) elementwise for FP16 a, b: the sum of two FP16 values is
+// exact in fp64, so one rounding to FP16 gives the correctly rounded result.
+__global__ __launch_bounds__(256) void residual_add_kernel(const uint16_t *a, const uint16_t *b, uint16_t *out,
+                                                           long long n)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const double s = (double)(float)__builtin_bit_cast(_Float16, a[i]) +
+                     (double)(float)__builtin_bit_cast(_Float16, b[i]);
+    out[i] = __builtin_bit_cast(uint16_t, (_Float16)s);
 }
 
 }  // namespace
+
+extern "C" int moe_residual_add(const void *a_dev, const void *b_dev, void *out_dev, long long n, void *stream)
+{
+    moe::clear_error();
+    if (n < 0) return moe::fail(MOE_ERR_INVALID_ARG, "moe_residual_add: n=%lld", n);
+    if (n == 0) return MOE_OK;
+    if (!a_dev || !b_dev || !out_dev) return moe::fail(MOE_ERR_INVALID_ARG, "moe_residual_add: null pointer argument");
+    hipLaunchKernelGGL(residual_add_kernel, dim3((unsigned int)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       (const uint16_t *)a_dev, (const uint16_t *)b_dev, (uint16_t *)out_dev, n);
+    return moe::check_launch("moe_residual_add");
+}
 
 extern "C" int moe_combine(const float *pair_out_dev, const int32_t *pair_pos_dev, const float *topk_w_dev,
                            const float *shared_out_dev, const float *shared_gate_dev,

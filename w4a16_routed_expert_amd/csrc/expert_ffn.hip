@@ -92,7 +92,13 @@ struct Unit {
     bool absent;          // the expert has no device row
 };
 
-template <bool GATEUP, int NT, int S>
+// F16W: the weights are FP16 values in the expanded slot layout (the
+// offload-qpacked profile) instead of qpacked INT4: a 4096-byte tile covers
+// the same 16 rows x 128 columns and is read as four coalesced 1024-byte
+// pieces, piece q giving each lane one MFMA operand (row n16, columns
+// 32*g4 + 8q .. +7 of the tile, natural order); no conversion, no zero
+// point, no scale.
+template <bool GATEUP, int NT, int S, bool F16W = false>
 struct Ffn {
     // Weight streams per wavefront: gate/up the gate and up rows of one row
     // group; down two adjacent row groups (each activation fragment then
@@ -104,7 +110,9 @@ struct Ffn {
     static constexpr int NTW = NT / S;          // tiles of one wavefront
     static constexpr int RGB = kWaves / S;      // wavefront row slots per item
     static constexpr int NB = (NT + 1) / 2;     // scale blocks of the reduction axis
-    static constexpr int D = ring_depth(NTW, NMAT);
+    static constexpr int QW = F16W ? 4 : 1;    // 16-byte loads per lane per tile
+    static constexpr int D = ring_depth(NTW, NMAT * QW);
+    static constexpr float kOut = F16W ? 1.0f : kUnit;
     static_assert(NT >= 1 && NT <= kMaxNT, "reduction axis of 128 .. 2048 columns");
     static_assert(NT % S == 0 && (S == 1 || NTW % 2 == 0), "split slices cover whole scale blocks");
     static_assert(NTW % D == 0, "ring depth divides the unit");
@@ -180,6 +188,21 @@ struct Ffn {
         return __builtin_amdgcn_raw_buffer_load_b128(rsrc(row, nrec), lane * 16, qm + ((r * NT) + t0 + j) * 1024, 0);
     }
 
+    // All QW loads of tile j into w (the qpacked tile, or the four FP16 pieces).
+    __device__ void load_tile(u32x4 (&w)[QW], const uint8_t *row, int nrec, int rg, int mat, int j) const
+    {
+        if constexpr (F16W) {
+            const int qm = GATEUP ? a.off_q[mat] : a.off_q[2];
+            const int r = GATEUP ? rg : rg + mat;
+            const int base = qm + ((r * NT) + t0 + j) * 4096;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                w[q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(row, nrec), lane * 16, base + q * 1024, 0);
+        } else {
+            w[0] = load_q(row, nrec, rg, mat, j);
+        }
+    }
+
     // FP16 scale of the block of tile j, row n16 of the row group.
     __device__ _Float16 load_s(const uint8_t *row, int nrec, int rg, int mat, int j) const
     {
@@ -219,6 +242,13 @@ struct Ffn {
             u32x4 *dst = &L.xl[(t * 4) * 64 + g * 16 + m];
             // kind q holds columns 8q + (1, 5, 0, 4, 3, 7, 2, 6) of the group,
             // the order in which the weight conversion yields them
+            if constexpr (F16W) {
+                dst[0] = d0;
+                dst[64] = d1;
+                dst[128] = d2;
+                dst[192] = d3;
+                continue;
+            }
             dst[0] = permute_activations(d0);
             dst[64] = permute_activations(d1);
             dst[128] = permute_activations(d2);
@@ -234,6 +264,7 @@ struct Ffn {
             L.sxp[t][g][m] = s;
         }
         lds_barrier();
+        if constexpr (F16W) return;
         for (int i = threadIdx.x; i < NB * 16; i += kThreads) {
             const int b = i >> 4, m = i & 15;
             float s = 0.f;
@@ -249,7 +280,7 @@ struct Ffn {
     // with the tile D steps ahead (from unit `nxt` past the end), then write
     // the unit's outputs.  Rounds of D tiles run as a loop, so the ring slot
     // of every tile is fixed and the loop carries the ring in place.
-    __device__ void run(const Unit &cur, const Unit &nxt, u32x4 (&wq)[D][NMAT], _Float16 (&ws)[D][NMAT]) const
+    __device__ void run(const Unit &cur, const Unit &nxt, u32x4 (&wq)[D][NMAT][QW], _Float16 (&ws)[D][NMAT]) const
     {
         constexpr int NR = NTW / D;
         const u32x4 *xl = &L.xl[t0 * 4 * 64 + lane];
@@ -269,7 +300,7 @@ struct Ffn {
 #pragma unroll
             for (int jd = 0; jd < D; ++jd) {
                 const int j = jo * D + jd;
-                if (j % 2 == 0) {
+                if (!F16W && j % 2 == 0) {
                     const f32x4 z = sx[(j / 2) * 4];      // zero-point term of this scale block
 #pragma unroll
                     for (int mat = 0; mat < NMAT; ++mat) p[mat] = z;
@@ -281,20 +312,31 @@ struct Ffn {
                 float sc[NMAT];
 #pragma unroll
                 for (int mat = 0; mat < NMAT; ++mat) {
-                    const u32x4 w = wq[jd][mat];
+                    if constexpr (F16W) {
+                        half8 b[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) b[q] = __builtin_bit_cast(half8, wq[jd][mat][q]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_tile(wq[jd][mat], rrow, rnrec, rrg, mat, rj0 + jd);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[mat] = mfma(xa[q], b[q], acc[mat]);
+                        continue;
+                    }
+                    const u32x4 w = wq[jd][mat][0];
                     half8 b[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) b[q] = codes_to_operand(w[q]);
                     sc[mat] = scale_f32(ws[jd][mat]);
                     // every read of this slot happens above: reload it in place
                     __builtin_amdgcn_sched_barrier(0);
-                    wq[jd][mat] = load_q(rrow, rnrec, rrg, mat, rj0 + jd);
+                    wq[jd][mat][0] = load_q(rrow, rnrec, rrg, mat, rj0 + jd);
                     ws[jd][mat] = load_s(rrow, rnrec, rrg, mat, rj0 + jd);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) p[mat] = mfma(xa[q], b[q], p[mat]);
                 }
-                if (merge) {
+                if (!F16W && merge) {
 #pragma unroll
                     for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
@@ -333,25 +375,25 @@ struct Ffn {
             if (m < cur.nval) {
                 const size_t pr = (size_t)(cur.p0 + m);
                 if constexpr (GATEUP) {
-                    const float g = acc[0][r] * kUnit, u = acc[NMAT - 1][r] * kUnit;
+                    const float g = acc[0][r] * kOut, u = acc[NMAT - 1][r] * kOut;
                     a.h[pr * a.I + col] = cur.absent ? (uint16_t)0 : float_to_half_bits(g / (1.0f + expf(-g)) * u);
                 } else {
 #pragma unroll
                     for (int mat = 0; mat < NMAT; ++mat)
-                        a.out[pr * a.H + col + 16 * mat] = cur.absent ? 0.0f : acc[mat][r] * kUnit;
+                        a.out[pr * a.H + col + 16 * mat] = cur.absent ? 0.0f : acc[mat][r] * kOut;
                 }
             }
         }
     }
 };
 
-template <bool GATEUP, int NT, int S>
+template <bool GATEUP, int NT, int S, bool F16W = false>
 __global__ __launch_bounds__(kThreads) void w4a16_ffn_kernel(FfnArgs a, const int32_t *__restrict__ active,
                                                              const int32_t *__restrict__ offsets,
                                                              const int32_t *__restrict__ slot_map,
                                                              const int32_t *__restrict__ n_active)
 {
-    using F = Ffn<GATEUP, NT, S>;
+    using F = Ffn<GATEUP, NT, S, F16W>;
     __shared__ typename F::Lds L;
     // the slot table's inputs first: their loads do not wait for n_active
     TableIn tin{};
@@ -366,15 +408,15 @@ __global__ __launch_bounds__(kThreads) void w4a16_ffn_kernel(FfnArgs a, const in
     const int it0 = (int)(N * blockIdx.x / gridDim.x), it1 = (int)(N * (blockIdx.x + 1) / gridDim.x);
     if (it0 >= it1) return;
 
-    u32x4 wq[F::D][F::NMAT];
+    u32x4 wq[F::D][F::NMAT][F::QW];
     _Float16 ws[F::D][F::NMAT];
     Unit cur = f.unit(it0, 0);
 #pragma unroll
     for (int j = 0; j < F::D; ++j)
 #pragma unroll
         for (int mat = 0; mat < F::NMAT; ++mat) {
-            wq[j][mat] = f.load_q(cur.row, cur.nrec, cur.rg, mat, j);
-            ws[j][mat] = f.load_s(cur.row, cur.nrec, cur.rg, mat, j);
+            f.load_tile(wq[j][mat], cur.row, cur.nrec, cur.rg, mat, j);
+            if constexpr (!F16W) ws[j][mat] = f.load_s(cur.row, cur.nrec, cur.rg, mat, j);
         }
     f.stage(cur);
     // The body is the same for every item, so the ring registers need no
@@ -407,10 +449,10 @@ int ffn::cu_count()
 
 namespace {
 
-template <bool GATEUP, int NT, int S>
+template <bool GATEUP, int NT, int S, bool F16W>
 int launch_one(const FfnArgs &a, hipStream_t s, long long max_items, const char *who)
 {
-    auto kern = w4a16_ffn_kernel<GATEUP, NT, S>;
+    auto kern = w4a16_ffn_kernel<GATEUP, NT, S, F16W>;
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess || occ <= 0) occ = 1;
     long long g = (long long)cu_count() * occ;
@@ -443,19 +485,19 @@ int choose_split(int NT, int RG, int T, int k, int E)
     return S;
 }
 
-template <bool GATEUP, int NT>
+template <bool GATEUP, int NT, bool F16W>
 int launch_nt(const FfnArgs &a, hipStream_t s, int S, long long max_items, const char *who)
 {
     if constexpr (NT % 4 == 0) {
-        if (S == 2) return launch_one<GATEUP, NT, 2>(a, s, max_items * 2, who);
+        if (S == 2) return launch_one<GATEUP, NT, 2, F16W>(a, s, max_items * 2, who);
     }
     if constexpr (NT % 8 == 0) {
-        if (S == 4) return launch_one<GATEUP, NT, 4>(a, s, max_items * 4, who);
+        if (S == 4) return launch_one<GATEUP, NT, 4, F16W>(a, s, max_items * 4, who);
     }
     if constexpr (NT % 16 == 0) {
-        if (S == 8) return launch_one<GATEUP, NT, 8>(a, s, max_items * 8, who);
+        if (S == 8) return launch_one<GATEUP, NT, 8, F16W>(a, s, max_items * 8, who);
     }
-    return launch_one<GATEUP, NT, 1>(a, s, max_items, who);
+    return launch_one<GATEUP, NT, 1, F16W>(a, s, max_items, who);
 }
 
 // The grouped GEMM once experts average 64 routed pairs or more: then the
@@ -469,10 +511,10 @@ bool use_gemm(const FfnArgs &a, int mode)
     return (long long)a.T * a.k >= 64LL * a.E;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool F16W = false>
 int launch_ffn(const FfnArgs &a, int mode, hipStream_t s, const char *who)
 {
-    if (use_gemm(a, mode)) return GATEUP ? launch_gemm_gateup(a, s) : launch_gemm_down(a, s);
+    if (!F16W && use_gemm(a, mode)) return GATEUP ? launch_gemm_gateup(a, s) : launch_gemm_down(a, s);
     const int K = GATEUP ? a.H : a.I;
     const int R = GATEUP ? a.I : a.H;
     // row slots of wavefronts: gate/up one row group each, down two when the
@@ -484,22 +526,22 @@ int launch_ffn(const FfnArgs &a, int mode, hipStream_t s, const char *who)
     const long long max_items = (max_slots + pairs / 16) * ((RG + kWaves - 1) / kWaves);
     const int S = choose_split(NT, RG, a.T, a.k, a.E);
     switch (NT) {
-    case 1: return launch_nt<GATEUP, 1>(a, s, S, max_items, who);
-    case 2: return launch_nt<GATEUP, 2>(a, s, S, max_items, who);
-    case 3: return launch_nt<GATEUP, 3>(a, s, S, max_items, who);
-    case 4: return launch_nt<GATEUP, 4>(a, s, S, max_items, who);
-    case 5: return launch_nt<GATEUP, 5>(a, s, S, max_items, who);
-    case 6: return launch_nt<GATEUP, 6>(a, s, S, max_items, who);
-    case 7: return launch_nt<GATEUP, 7>(a, s, S, max_items, who);
-    case 8: return launch_nt<GATEUP, 8>(a, s, S, max_items, who);
-    case 9: return launch_nt<GATEUP, 9>(a, s, S, max_items, who);
-    case 10: return launch_nt<GATEUP, 10>(a, s, S, max_items, who);
-    case 11: return launch_nt<GATEUP, 11>(a, s, S, max_items, who);
-    case 12: return launch_nt<GATEUP, 12>(a, s, S, max_items, who);
-    case 13: return launch_nt<GATEUP, 13>(a, s, S, max_items, who);
-    case 14: return launch_nt<GATEUP, 14>(a, s, S, max_items, who);
-    case 15: return launch_nt<GATEUP, 15>(a, s, S, max_items, who);
-    case 16: return launch_nt<GATEUP, 16>(a, s, S, max_items, who);
+    case 1: return launch_nt<GATEUP, 1, F16W>(a, s, S, max_items, who);
+    case 2: return launch_nt<GATEUP, 2, F16W>(a, s, S, max_items, who);
+    case 3: return launch_nt<GATEUP, 3, F16W>(a, s, S, max_items, who);
+    case 4: return launch_nt<GATEUP, 4, F16W>(a, s, S, max_items, who);
+    case 5: return launch_nt<GATEUP, 5, F16W>(a, s, S, max_items, who);
+    case 6: return launch_nt<GATEUP, 6, F16W>(a, s, S, max_items, who);
+    case 7: return launch_nt<GATEUP, 7, F16W>(a, s, S, max_items, who);
+    case 8: return launch_nt<GATEUP, 8, F16W>(a, s, S, max_items, who);
+    case 9: return launch_nt<GATEUP, 9, F16W>(a, s, S, max_items, who);
+    case 10: return launch_nt<GATEUP, 10, F16W>(a, s, S, max_items, who);
+    case 11: return launch_nt<GATEUP, 11, F16W>(a, s, S, max_items, who);
+    case 12: return launch_nt<GATEUP, 12, F16W>(a, s, S, max_items, who);
+    case 13: return launch_nt<GATEUP, 13, F16W>(a, s, S, max_items, who);
+    case 14: return launch_nt<GATEUP, 14, F16W>(a, s, S, max_items, who);
+    case 15: return launch_nt<GATEUP, 15, F16W>(a, s, S, max_items, who);
+    case 16: return launch_nt<GATEUP, 16, F16W>(a, s, S, max_items, who);
     default: return moe::fail(MOE_ERR_UNSUPPORTED, "%s: reduction length %d > %d", who, K, kMaxNT * 128);
     }
 }
@@ -507,7 +549,7 @@ int launch_ffn(const FfnArgs &a, int mode, hipStream_t s, const char *who)
 int make_args(FfnArgs &a, const void *x_dev, int T, int H, int I, int E, int k, const void *rows_dev,
               size_t row_stride, const int32_t *slot_map_dev, const int32_t *expert_offsets_dev,
               const int32_t *sorted_pairs_dev, const int32_t *active_list_dev, const int32_t *n_active_dev,
-              void *h_dev, float *pair_out_dev, int32_t *status_dev, int mode, const char *who)
+              void *h_dev, float *pair_out_dev, int32_t *status_dev, int mode, const char *who, bool f16 = false)
 {
     int rc = moe::check_shape(T, H, I, E, k, true);
     if (rc) return rc;
@@ -517,7 +559,7 @@ int make_args(FfnArgs &a, const void *x_dev, int T, int H, int I, int E, int k, 
     if (H > kMaxNT * 128 || I > kMaxNT * 128)
         return moe::fail(MOE_ERR_UNSUPPORTED, "%s: H and I must be <= %d", who, kMaxNT * 128);
     size_t off[6];
-    const size_t rb = moe::row_bytes(H, I, off);
+    const size_t rb = f16 ? moe::row_bytes_fp16(H, I, off) : moe::row_bytes(H, I, off);
     if (!rows_dev || !expert_offsets_dev || !active_list_dev || !n_active_dev || !h_dev)
         return moe::fail(MOE_ERR_INVALID_ARG, "%s: null pointer argument", who);
     if (!moe::aligned(rows_dev, 256) || row_stride < rb || row_stride % 256)
@@ -603,6 +645,32 @@ int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
     rc = launch_gateup(a, mode, (hipStream_t)stream);
     if (rc) return rc;
     return launch_down(a, mode, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------ FP16 execution slots
+// The offload-qpacked profile ("Horizon RunMap - architecture", section
+// "Historical contracts remain distinct"; "Horizon technical notes —
+// publication edition v1", section "Precision is profile-specific"): the
+// low-bit source is dequantized into FP16 execution slots, which the FFN then
+// reads instead of the compact rows.
+
+int moe_fp16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
+                        const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                        const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
+                        const int32_t *active_list_dev, const int32_t *n_active_dev,
+                        void *h_dev, float *pair_out_dev, int32_t *status_dev, void *stream)
+{
+    moe::clear_error();
+    const char *who = "moe_fp16_expert_ffn";
+    FfnArgs a;
+    int rc = make_args(a, x_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev, expert_offsets_dev,
+                       sorted_pairs_dev, active_list_dev, n_active_dev, h_dev, pair_out_dev, status_dev,
+                       MOE_FFN_PATH_STREAM, who, true);
+    if (rc) return rc < 0 ? MOE_OK : rc;
+    if (!x_dev || !sorted_pairs_dev || !pair_out_dev) return moe::fail(MOE_ERR_INVALID_ARG, "%s: null pointer argument", who);
+    rc = launch_ffn<true, true>(a, MOE_FFN_PATH_STREAM, (hipStream_t)stream, who);
+    if (rc) return rc;
+    return launch_ffn<false, true>(a, MOE_FFN_PATH_STREAM, (hipStream_t)stream, who);
 }
 
 }  // extern "C"

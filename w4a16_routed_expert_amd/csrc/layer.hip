@@ -1,0 +1,83 @@
+// The whole routed-expert layer in one call: route -> W4A16 gate/up + SiLU*up
+// -> W4A16 down -> weighted combine (+ the gated shared-expert term).
+//
+// Decode batches (the streaming kernels, T <= 256) take four launches with no
+// host round trip and no wait of one block for another: routing in one
+// launch (the last block to finish its logits runs the top-k and the
+// grouping, 4 KB of logits handed over at device scope), gate/up, down and
+// the combine.  A combine folded into the down projection's epilogue (the
+// last unit of a token combining it) was measured slower: the outputs of one
+// launch would cross the XCDs' L2 caches either by write-back of whole
+// caches per unit or by uncombined device-scope stores, costing more than the
+// launch saved.  Larger batches (and the grouped GEMM) run the separate
+// calls in order.  The pages' executors for the same layer (a scalar path,
+// "Grouped T3", "top4-fused-v1": "Horizon RunMap - architecture", section
+// "Regimes and executor boundaries") are prior art; their kernels are not
+// published.
+#include "moe_internal.h"
+
+namespace {
+
+constexpr size_t kCtrl = 256;                       // done counter (and padding)
+
+size_t layer_ws_bytes(int T, int E) { return kCtrl + moe::route_logits_bytes(T, E); }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_layer_workspace_size(int T, int H, int E)
+{
+    (void)H;
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    return layer_ws_bytes(T, E);
+}
+
+int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int I,
+                      int E, int k, const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                      const float *shared_out_dev, const float *shared_gate_dev, void *shared_ready_event,
+                      void *y_dev, const moe_layer_buffers *b, int mode, void *stream)
+{
+    moe::clear_error();
+    const char *who = "moe_layer_forward";
+    int rc = moe::check_shape(T, H, I, E, k, true);
+    if (rc) return rc;
+    if (mode != MOE_FFN_PATH_AUTO && mode != MOE_FFN_PATH_STREAM && mode != MOE_FFN_PATH_GEMM)
+        return moe::fail(MOE_ERR_INVALID_ARG, "%s: unknown mode %d", who, mode);
+    if (T == 0) return MOE_OK;
+    if (!b || !x_dev || !w_router_dev || !rows_dev || !y_dev || !b->topk_ids || !b->topk_w || !b->expert_offsets ||
+        !b->sorted_pairs || !b->pair_pos || !b->active_list || !b->n_active || !b->h || !b->pair_out)
+        return moe::fail(MOE_ERR_INVALID_ARG, "%s: null pointer argument", who);
+    if ((shared_out_dev == nullptr) != (shared_gate_dev == nullptr))
+        return moe::fail(MOE_ERR_INVALID_ARG, "%s: shared_out and shared_gate must both be given or both NULL", who);
+    const size_t need = layer_ws_bytes(T, E);
+    if (!b->ws || b->ws_bytes < need || !moe::aligned(b->ws, 256))
+        return moe::fail(MOE_ERR_WORKSPACE, "%s: the workspace needs %zu bytes, 256-byte aligned", who, need);
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = (uint8_t *)b->ws;
+    unsigned int *done = (unsigned int *)ws;
+    void *route_ws = ws + kCtrl;
+    const size_t route_ws_bytes = moe::route_logits_bytes(T, E);
+    const bool stream_kernels = mode == MOE_FFN_PATH_STREAM || (mode == MOE_FFN_PATH_AUTO && (long long)T * k < 64LL * E);
+    if (stream_kernels && T <= moe::kFusedMaxT)
+        rc = moe::route_fused(x_dev, w_router_dev, bias_dev, T, H, E, k, b->logits, b->topk_ids, b->topk_w,
+                              b->expert_offsets, b->sorted_pairs, b->pair_pos, b->active_list, b->n_active,
+                              (float *)route_ws, done, s);
+    else
+        rc = moe_route(x_dev, w_router_dev, bias_dev, T, H, E, k, b->logits, b->topk_ids, b->topk_w,
+                       b->expert_offsets, b->sorted_pairs, b->pair_pos, b->active_list, b->n_active, route_ws,
+                       route_ws_bytes, stream);
+    if (rc) return rc;
+    rc = moe_w4a16_expert_ffn(x_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev, b->expert_offsets,
+                              b->sorted_pairs, b->active_list, b->n_active, b->h, b->pair_out, b->status, mode,
+                              stream);
+    if (rc) return rc;
+    if (shared_ready_event) {
+        const hipError_t e = hipStreamWaitEvent(s, (hipEvent_t)shared_ready_event, 0);
+        if (e != hipSuccess) return moe::fail(MOE_ERR_HIP, "%s: waiting for the shared expert: %s", who,
+                                              hipGetErrorString(e));
+    }
+    return moe_combine(b->pair_out, b->pair_pos, b->topk_w, shared_out_dev, shared_gate_dev, T, H, k, y_dev, stream);
+}
+
+}  // extern "C"

@@ -87,6 +87,62 @@ __device__ inline V sum_phases(V v)
     return v;
 }
 
+// Data handed between blocks of one launch.  Stores and loads at device
+// scope (relaxed atomics: the sc1 bit, coherent across the XCDs' L2 caches)
+// reach every block without write-back or invalidation of whole L2 caches
+// (a device-scope fence does both, which costs microseconds per wave); a
+// wave orders its device-scope stores before a counter update by waiting
+// for them to complete (s_waitcnt vmcnt(0)).  Worth it for small data only:
+// scattered device-scope stores bypass the L2's write combining.
+__device__ inline void store_dev(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float load_dev(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// y[t][c4*4 .. c4*4+3] = RN16( sum_{j<k} topk_w[t][j] * pair_out[pair_pos[t*k+j]][..]
+// (+ shared_gate[t] * shared_out[t][..]) ), FP32 in slot order: the combine of
+// one token's 4 columns.
+__device__ inline void combine_cols4(const float *pair_out, const int32_t *pair_pos, const float *topk_w,
+                                     const float *shared_out, const float *shared_gate, int T, int H, int k, int t,
+                                     int c4, uint16_t *y)
+{
+    // all k positions and weights first, then all k row loads, so the loads overlap
+    int pos[MOE_MAX_TOPK];
+    float w[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        pos[j] = -1;
+        w[j] = 0.0f;
+        if (j < k) {
+            pos[j] = pair_pos[(size_t)t * k + j];
+            w[j] = topk_w[(size_t)t * k + j];
+        }
+    }
+    float4 v[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (pos[j] >= 0 && pos[j] < T * k)       // a corrupted grouping is skipped, never read out of bounds
+            v[j] = *reinterpret_cast<const float4 *>(pair_out + (size_t)pos[j] * H + c4 * 4);
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (j < k) {
+            acc.x += w[j] * v[j].x; acc.y += w[j] * v[j].y; acc.z += w[j] * v[j].z; acc.w += w[j] * v[j].w;
+        }
+    }
+    if (shared_out) {
+        const float g = shared_gate[t];
+        const float4 sv = *reinterpret_cast<const float4 *>(shared_out + (size_t)t * H + c4 * 4);
+        acc.x += g * sv.x; acc.y += g * sv.y; acc.z += g * sv.z; acc.w += g * sv.w;
+    }
+    const _Float16 hx = (_Float16)acc.x, hy = (_Float16)acc.y, hz = (_Float16)acc.z, hw = (_Float16)acc.w;
+    uint2 packed;
+    packed.x = (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+    packed.y = (uint32_t)__builtin_bit_cast(uint16_t, hz) | ((uint32_t)__builtin_bit_cast(uint16_t, hw) << 16);
+    *reinterpret_cast<uint2 *>(y + (size_t)t * H + c4 * 4) = packed;
+}
+
 // Thread-local message behind moe_last_error().
 void set_error(const char *fmt, ...);
 void vset_error(const char *fmt, va_list ap);
@@ -104,5 +160,22 @@ inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_
 int check_shape(int T, int H, int I, int E, int k, bool need_I);
 
 size_t row_bytes(int H, int I, size_t *off6);
+// FP16 execution-slot row (gate, up, down in 4096-byte tiles; no scale planes).
+size_t row_bytes_fp16(int H, int I, size_t *off6);
+// Dequantizes n qpacked rows into FP16 slot rows (dequant.hip).
+int dequant_rows(const void *q_rows, size_t q_stride, void *f_rows, size_t f_stride, int n, int H, int I,
+                 hipStream_t s);
+
+// Pieces of the fused layer (moe_layer_forward).
+constexpr int kFusedMaxT = 256;        // largest batch routed in one launch
+
+// route.hip: logits, top-k and grouping of 1 <= T <= kFusedMaxT tokens in one
+// launch.  lbuf: FP32 [T][E] (route_logits_bytes); done: a counter that is 0
+// before the call and 0 after it.
+int route_fused(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int E, int k,
+                float *logits_dev, int32_t *topk_ids_dev, float *topk_w_dev, int32_t *expert_offsets_dev,
+                int32_t *sorted_pairs_dev, int32_t *pair_pos_dev, int32_t *active_list_dev, int32_t *n_active_dev,
+                float *lbuf, unsigned int *done, hipStream_t s);
+size_t route_logits_bytes(int T, int E);
 
 }  // namespace moe

@@ -486,7 +486,7 @@ struct GroupLds {
 // a prefix over experts and waves gives each wave its starting position per
 // expert, then each wave walks its range 64 pairs at a time; a pair's rank
 // among equal experts of its chunk comes from a ballot.
-template <int NW, bool TOPK>
+template <int NW, bool TOPK, bool DEV = false>
 __device__ void group_phase(const RouteArgs &a, GroupLds<NW, TOPK> &S)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -500,7 +500,8 @@ __device__ void group_phase(const RouteArgs &a, GroupLds<NW, TOPK> &S)
             for (int i = 0; i < kTopkBatch; ++i) {
                 tok[i] = t0 + i * NW;
                 // clamped (always valid) addresses: the loads issue back to back
-                lv[i] = a.lbuf[(size_t)min(tok[i], a.T - 1) * E + min(lane, E - 1)];
+                const float *src = a.lbuf + (size_t)min(tok[i], a.T - 1) * E + min(lane, E - 1);
+                lv[i] = DEV ? moe::load_dev(src) : *src;
             }
             if (a.logits && a.logits != a.lbuf && lane < E) {
 #pragma unroll
@@ -566,8 +567,19 @@ __device__ void group_phase(const RouteArgs &a, GroupLds<NW, TOPK> &S)
 // row, loads VEC experts of a row; rows h = RPW*(kSelWaves*i + wave) + hp,
 // RPW = 64/EQ rows per wave step.  The first batch of router rows is loaded
 // before the activation row is staged, so the two memory latencies overlap.
-template <int VEC>
-__global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
+struct LogitsLds {
+    double x[kMaxH];
+    double acc[kSelWaves][kGroupE];
+    float bnd[kSelWaves][kGroupE];
+    long long red[kSelWaves][2];
+    float logit[kGroupE];
+    unsigned long long redo;
+};
+
+// DEV: the logits go to a.lbuf at device scope (read by another block of the
+// same launch).
+template <int VEC, bool DEV = false>
+__device__ void logits_block(const RouteArgs &a, LogitsLds &S, int t, int g)
 {
     constexpr int EQ = kGroupE / VEC;
     constexpr int RPW = 64 / EQ;
@@ -576,16 +588,14 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
     constexpr int kPath = kMaxH / (RPW * kSelWaves) + ilog2_ceil(RPW) + kSelWaves;
     constexpr int kErrExp = ilog2_ceil(kPath) + 1 - 53;
     static_assert(kErrExp <= -44, "summation paths of at most 256 additions");
-    const int G = (a.E + kGroupE - 1) / kGroupE;
-    const int t = blockIdx.x / G, g = blockIdx.x % G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.E, H = a.H;
-    __shared__ double s_x[kMaxH];
-    __shared__ double s_acc[kSelWaves][kGroupE];
-    __shared__ float s_bnd[kSelWaves][kGroupE];
-    __shared__ long long s_red[kSelWaves][2];
-    __shared__ float s_logit[kGroupE];
-    __shared__ unsigned long long s_redo;
+    double *s_x = S.x;
+    auto &s_acc = S.acc;
+    auto &s_bnd = S.bnd;
+    auto &s_red = S.red;
+    float *s_logit = S.logit;
+    unsigned long long &s_redo = S.redo;
 
     const int eq = lane % EQ, hp = lane / EQ;
     const int e0 = g * kGroupE + VEC * eq;          // first expert of this lane
@@ -692,9 +702,18 @@ __global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
         if (e < E) {
             float lv = s_logit[tid];
             if (a.bias) lv = lv + a.bias[e];
-            a.lbuf[(size_t)t * E + e] = lv;
+            if (DEV) moe::store_dev(&a.lbuf[(size_t)t * E + e], lv);
+            else a.lbuf[(size_t)t * E + e] = lv;
         }
     }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kSelThreads) void route_logits_kernel(RouteArgs a)
+{
+    __shared__ LogitsLds S;
+    const int G = (a.E + kGroupE - 1) / kGroupE;
+    logits_block<VEC>(a, S, blockIdx.x / G, blockIdx.x % G);
 }
 
 // One block: top-k + softmax of every token from a.lbuf (TOPK), then the
@@ -704,6 +723,36 @@ __global__ __launch_bounds__(kGrpThreads) void route_group_kernel(RouteArgs a)
 {
     __shared__ GroupLds<kGrpWaves, TOPK> s_grp;
     group_phase<kGrpWaves, TOPK>(a, s_grp);
+}
+
+// Small batches in one launch (the fused layer, moe_layer_forward): every
+// block computes its (token, expert group) logits as route_logits_kernel
+// does, stored at device scope; once they are complete the block counts
+// itself in the workspace, and the block that counts last (no block ever
+// waits for another) runs the top-k and the grouping over all logits, read
+// at device scope, and resets the counter for the next call.
+union FusedRouteLds {
+    LogitsLds lg;
+    GroupLds<kSelWaves, true> gr;
+};
+
+template <int VEC>
+__global__ __launch_bounds__(kSelThreads) void route_fused_kernel(RouteArgs a, unsigned int *done)
+{
+    __shared__ FusedRouteLds S;
+    __shared__ int s_last;
+    const int G = (a.E + kGroupE - 1) / kGroupE;
+    logits_block<VEC, true>(a, S.lg, blockIdx.x / G, blockIdx.x % G);
+    moe::wait_stores();                                     // this wave's logits are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned int before = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = before == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    group_phase<kSelWaves, true, true>(a, S.gr);
+    if (threadIdx.x == 0) *done = 0u;
 }
 
 // Large batches: the stable counting sort runs on many blocks (one single
@@ -870,6 +919,40 @@ int route_launch(const void *x_dev, const void *w_router_dev, const float *bias_
 }
 
 }  // namespace
+
+int moe::route_fused(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int E, int k,
+                     float *logits_dev, int32_t *topk_ids_dev, float *topk_w_dev, int32_t *expert_offsets_dev,
+                     int32_t *sorted_pairs_dev, int32_t *pair_pos_dev, int32_t *active_list_dev,
+                     int32_t *n_active_dev, float *lbuf, unsigned int *done, hipStream_t s)
+{
+    if (T < 1 || T > kSmallBatch) return moe::fail(MOE_ERR_UNSUPPORTED, "fused routing: T=%d outside [1, %d]", T,
+                                                   kSmallBatch);
+    if (H > kMaxH) return moe::fail(MOE_ERR_UNSUPPORTED, "fused routing: H=%d > %d", H, kMaxH);
+    if (!moe::aligned(x_dev, 8) || !moe::aligned(w_router_dev, 2))
+        return moe::fail(MOE_ERR_INVALID_ARG, "fused routing: x must be 8-byte and w_router 2-byte aligned");
+    RouteArgs a;
+    a.x = (const uint16_t *)x_dev;
+    a.wr = (const uint16_t *)w_router_dev;
+    a.bias = bias_dev;
+    a.T = T; a.H = H; a.E = E; a.k = k;
+    a.logits = logits_dev;
+    a.ids = topk_ids_dev;
+    a.w = topk_w_dev;
+    a.offsets = expert_offsets_dev;
+    a.sorted_pairs = sorted_pairs_dev;
+    a.pair_pos = pair_pos_dev;
+    a.active = active_list_dev;
+    a.n_active = n_active_dev;
+    a.force_exact = 0;
+    a.lbuf = lbuf;
+    const unsigned int blocks = (unsigned int)T * (unsigned int)((E + kGroupE - 1) / kGroupE);
+    if (E % 2 == 0 && moe::aligned(w_router_dev, 4))
+        hipLaunchKernelGGL(route_fused_kernel<2>, dim3(blocks), dim3(kSelThreads), 0, s, a, done);
+    else hipLaunchKernelGGL(route_fused_kernel<1>, dim3(blocks), dim3(kSelThreads), 0, s, a, done);
+    return moe::check_launch("moe_layer_forward (routing)");
+}
+
+size_t moe::route_logits_bytes(int T, int E) { return route_ws_bytes(T, E); }
 
 extern "C" {
 

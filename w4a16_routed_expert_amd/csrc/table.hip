@@ -75,6 +75,31 @@ public:
         return note(hipGetLastError());
     }
     const char *message() override { return msg_; }
+    // FP16 execution slots: the qpacked row goes to a device staging row, then
+    // is dequantized into the slot (same stream, so the staging row is free
+    // again for the next row)
+    int row_upload(void *dst, const void *src, size_t n, void *s) override
+    {
+        if (!dev_stage_) return h2d_async(dst, src, n, s);
+        if (h2d_async(dev_stage_, src, n, s)) return 1;
+        if (moe::dequant_rows(dev_stage_, stage_stride_, dst, slot_stride_, 1, H_, I_, (hipStream_t)s) != MOE_OK) {
+            msg_ = moe_last_error();
+            return 1;
+        }
+        return 0;
+    }
+    int init_fp16_slots(int H, int I)
+    {
+        H_ = H;
+        I_ = I;
+        stage_stride_ = (moe::row_bytes(H, I, nullptr) + 255) / 256 * 256;
+        slot_stride_ = (moe::row_bytes_fp16(H, I, nullptr) + 255) / 256 * 256;
+        return alloc_device(&dev_stage_, stage_stride_);
+    }
+    ~HipTransport() override
+    {
+        if (dev_stage_) (void)hipFree(dev_stage_);
+    }
 
 private:
     int note(hipError_t e)
@@ -84,6 +109,9 @@ private:
         return 1;
     }
     const char *msg_ = "";
+    void *dev_stage_ = nullptr;
+    int H_ = 0, I_ = 0;
+    size_t stage_stride_ = 0, slot_stride_ = 0;
 };
 
 }  // namespace
@@ -114,6 +142,12 @@ int moe_table_create(moe_table **out, const moe_table_desc *d, void *stream)
     *out = nullptr;
     moe_table *t = new (std::nothrow) moe_table;
     if (!t) return moe::fail(MOE_ERR_CAPACITY, "moe_table_create: out of host memory");
+    if (d->slot_format == MOE_SLOT_FP16 && moe::row_bytes(d->H, d->I, nullptr) != 0 &&
+        t->tr.init_fp16_slots(d->H, d->I) != 0) {
+        const int rc = moe::fail(MOE_ERR_CAPACITY, "moe_table_create: device staging row: %s", t->tr.message());
+        delete t;
+        return rc;
+    }
     const int rc = tcore::Table::create(&t->tr, d, &t->core);
     if (rc) {
         delete t;
@@ -151,6 +185,13 @@ int moe_upload_expert_rows(moe_table *t, const int32_t *expert_ids, int n, void 
     moe::clear_error();
     if (!t || (n > 0 && !expert_ids)) return moe::fail(MOE_ERR_INVALID_ARG, "moe_upload_expert_rows: null pointer");
     return t->core->upload(expert_ids, n, stream);
+}
+
+int moe_table_prefetch(moe_table *t, const int32_t *expert_ids, int n)
+{
+    moe::clear_error();
+    if (!t || (n > 0 && !expert_ids)) return moe::fail(MOE_ERR_INVALID_ARG, "moe_table_prefetch: null pointer");
+    return t->core->prefetch(expert_ids, n);
 }
 
 int moe_table_acquire(moe_table *t, void *stream, moe_table_lease *lease)

@@ -33,6 +33,7 @@
 
 #include <condition_variable>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -72,6 +73,10 @@ struct Transport {
     virtual int stream_sync(void *s) = 0;
     // writes map_dev[e] = slots[e] for e < E, asynchronously on stream s
     virtual int publish(int32_t *map_dev, const int32_t *slots, int E, void *s) = 0;
+    // one expert row (n host bytes in pinned staging) into device row dst,
+    // asynchronously on s: a copy, or for FP16 execution slots a copy and a
+    // dequantization into the slot
+    virtual int row_upload(void *dst, const void *src, size_t n, void *s) { return h2d_async(dst, src, n, s); }
     virtual const char *message() = 0;
 };
 
@@ -101,10 +106,23 @@ inline uint64_t digest(const void *p, size_t n)
 // run on the calling thread.
 class CopyPool {
 public:
+    // Worker threads besides the caller: MOE_COPY_THREADS - 1 if set (1..32
+    // threads in all), else 3 (four threads copy a row; on the host of an
+    // MI355X a decode stack's upload rate was the same with 4, 8 and 12).
     static CopyPool &get()
     {
-        static CopyPool pool(3);
+        static CopyPool pool(configured_workers());
         return pool;
+    }
+
+    static int configured_workers()
+    {
+        const char *v = std::getenv("MOE_COPY_THREADS");
+        if (v) {
+            const int n = std::atoi(v);
+            if (n >= 1 && n <= 32) return n - 1;
+        }
+        return 3;
     }
 
     void copy(uint8_t *dst, const uint8_t *src, size_t n)
@@ -283,6 +301,10 @@ public:
             last_use_[e] = step_;
             if (slot_of_[e] >= 0) {
                 ctr_.hits++;
+                if (prefetched_[e]) {
+                    prefetched_[e] = 0;
+                    ctr_.prefetch_hits++;
+                }
             } else {
                 ctr_.misses++;
                 miss_out[m++] = e;
@@ -296,7 +318,41 @@ public:
     // One miss transaction: copies the n experts' rows into free spare rows
     // and publishes the next generation; `consumer` is ordered after the
     // publication (a null handle is the default stream, as in HIP).
-    int upload(const int32_t *ids, int n, void *consumer)
+    int upload(const int32_t *ids, int n, void *consumer) { return transact(ids, n, consumer, true); }
+
+    // Speculative load of experts a later step is expected to route: starts a
+    // step with these ids as its active set (so the transaction's eviction
+    // keeps them), and uploads those without a published row as one
+    // transaction that no stream waits for (a later acquire orders its
+    // consumer after the publication).  Counted as prefetches, not misses;
+    // a prefetched expert that a later step routes counts a prefetch hit.
+    int prefetch(const int32_t *ids, int n)
+    {
+        if (faulted_) return fail(MOE_ERR_FAULTED, "moe_table_prefetch: the table faulted earlier");
+        if (n < 0 || n > E_) return fail(MOE_ERR_INVALID_ARG, "moe_table_prefetch: n=%d outside [0, E]", n);
+        for (int i = 0; i < n; ++i)
+            if (ids[i] < 0 || ids[i] >= E_)
+                return fail(MOE_ERR_INVALID_ARG, "moe_table_prefetch: expert id %d outside [0, E)", ids[i]);
+        step_++;
+        std::fill(active_now_.begin(), active_now_.end(), 0);
+        std::vector<int32_t> load;
+        for (int i = 0; i < n; ++i) {
+            const int e = ids[i];
+            if (active_now_[e]) continue;
+            active_now_[e] = 1;
+            last_use_[e] = step_;
+            if (slot_of_[e] < 0) load.push_back(e);
+        }
+        const int rc = transact(load.data(), (int)load.size(), nullptr, false);
+        if (rc == MOE_OK) {
+            for (int e : load) prefetched_[e] = 1;
+            ctr_.prefetched += load.size();
+        }
+        return rc;
+    }
+
+private:
+    int transact(const int32_t *ids, int n, void *consumer, bool order_consumer)
     {
         if (faulted_) return fail(MOE_ERR_FAULTED, "moe_upload_expert_rows: the table faulted earlier");
         if (n < 0 || n > E_) return fail(MOE_ERR_INVALID_ARG, "moe_upload_expert_rows: n=%d", n);
@@ -372,11 +428,15 @@ public:
             expert_in_[sl] = -1;
             last_visible_[sl] = g_new - 1;
             ctr_.evictions++;
+            if (prefetched_[e]) {
+                prefetched_[e] = 0;
+                ctr_.prefetch_unused++;
+            }
         }
         for (int i = 0; i < n; ++i) expert_in_[target[i]] = ids[i];
         slot_of_.swap(next);
         ctr_.generation = gen_;
-        if (tr_->stream_wait(consumer, published_[gen_ % kMaps]) != 0) {
+        if (order_consumer && tr_->stream_wait(consumer, published_[gen_ % kMaps]) != 0) {
             faulted_ = true;
             return fail(MOE_ERR_FAULTED, "moe_upload_expert_rows: ordering the consumer stream after publication "
                         "failed (%s); the table is faulted", tr_->message());
@@ -384,6 +444,7 @@ public:
         return MOE_OK;
     }
 
+public:
     // Captures the current generation for a consumer on `stream` (ordered
     // after its publication; a null handle is the default stream).
     int acquire(void *stream, moe_table_lease *out)
@@ -482,6 +543,8 @@ private:
             return fail(MOE_ERR_CAPACITY, "moe_table_create: %d spare rows; steps of %d tokens x top-%d need %d "
                         "(at most %d rows in all)", d->spare_rows, d->max_tokens, d->top_k, need,
                         4 * MOE_MAX_EXPERTS);
+        if (d->slot_format != MOE_SLOT_QPACKED && d->slot_format != MOE_SLOT_FP16)
+            return fail(MOE_ERR_INVALID_ARG, "moe_table_create: slot_format %d", d->slot_format);
         if (d->staging_rows < 1 || d->staging_rows > 16)
             return fail(MOE_ERR_CAPACITY, "moe_table_create: staging_rows %d outside [1, 16]", d->staging_rows);
         const size_t rb = row_layout(d->H, d->I, off);
@@ -504,7 +567,10 @@ private:
         nslots_ = d->capacity + d->spare_rows;
         size_t off[6];
         row_bytes_ = row_layout(d->H, d->I, off);
-        row_stride_ = (row_bytes_ + 255) / 256 * 256;
+        // device rows: the qpacked row, or an FP16 execution slot (three FP16
+        // matrices of I*H values each)
+        const size_t dev_bytes = d->slot_format == MOE_SLOT_FP16 ? (size_t)3 * d->I * d->H * 2 : row_bytes_;
+        row_stride_ = (dev_bytes + 255) / 256 * 256;
         host_stride_ = d->host_row_stride;
         host_ = static_cast<const uint8_t *>(d->host_source);
         // identity and layout of the host source
@@ -529,6 +595,7 @@ private:
         last_visible_.assign(nslots_, 0);
         last_use_.assign(E_, 0);
         active_now_.assign(E_, 0);
+        prefetched_.assign(E_, 0);
         if (tr_->create_stream(&copy_) != 0) return hip_fail("copy stream");
         if (tr_->alloc_device(&rows_, (size_t)nslots_ * row_stride_) != 0) return hip_fail("device rows");
         if (tr_->alloc_device(reinterpret_cast<void **>(&maps_), sizeof(int32_t) * (size_t)E_ * kMaps) != 0)
@@ -670,8 +737,8 @@ private:
                 return fail(MOE_ERR_HIP, "moe_upload_expert_rows (staging): %s", tr_->message());
         }
         CopyPool::get().copy(staging_[i], host_ + (size_t)e * host_stride_, row_bytes_);
-        if (tr_->h2d_async(static_cast<uint8_t *>(rows_) + (size_t)slot * row_stride_, staging_[i], row_bytes_,
-                           copy_) != 0)
+        if (tr_->row_upload(static_cast<uint8_t *>(rows_) + (size_t)slot * row_stride_, staging_[i], row_bytes_,
+                            copy_) != 0)
             return fail(MOE_ERR_HIP, "moe_upload_expert_rows (copy): %s", tr_->message());
         staging_used_[i] = 1;
         if (tr_->record(staging_done_[i], copy_) != 0) {
@@ -701,6 +768,7 @@ private:
     std::vector<uint64_t> last_visible_;     // slot -> last generation that named it before it was freed
     std::vector<uint64_t> last_use_;         // expert -> step of last use
     std::vector<uint8_t> active_now_;        // expert -> active in the current step
+    std::vector<uint8_t> prefetched_;        // expert -> uploaded by a prefetch, not yet routed
     uint64_t step_ = 0, gen_ = 0;
     std::vector<uint8_t *> staging_;
     std::vector<void *> staging_done_;

@@ -51,6 +51,17 @@ class RoutedExpertLayer:
         self.h = torch.empty((n, I), dtype=torch.float16, device=d)
         self.pair_out = torch.empty((n, H), dtype=torch.float32, device=d)
         self.status = torch.zeros(1, dtype=torch.int32, device=d)
+        # workspace of the one-call layer: zero-filled once, left zero by every call
+        self.layer_ws = torch.zeros(max(B.moe_layer_workspace_size(T, H, E), 256), dtype=torch.uint8, device=d)
+        self._bufs = B.layer_buffers(self.logits, self.topk_ids, self.topk_w, self.expert_offsets, self.sorted_pairs,
+                                     self.pair_pos, self.active_list, self.n_active, self.h, self.pair_out,
+                                     self.status, self.layer_ws, self.layer_ws.numel())
+
+    def _rows(self, rows):
+        """Rows, stride and slot map: the layer's own, or an explicit rows tensor with its stride."""
+        if rows is None:
+            return self.rows, self.row_stride, self.slot_map
+        return rows, rows.stride(0), self.slot_map
 
     def route(self, x: torch.Tensor, stream=None, exact: bool = False):
         T = x.shape[0]
@@ -65,14 +76,21 @@ class RoutedExpertLayer:
                         self.topk_w, self.expert_offsets, self.sorted_pairs, self.pair_pos, self.active_list,
                         self.n_active, self.ws, self.ws_bytes, stream)
 
-    def ffn(self, x: torch.Tensor, stream=None, rows=None, lease=None, mode: int = B.MOE_FFN_PATH_AUTO):
+    def ffn(self, x: torch.Tensor, stream=None, rows=None, lease=None, mode: int = B.MOE_FFN_PATH_AUTO,
+            fp16_slots: bool = False):
         """Expert FFN over the rows tensor (or `rows`), or over the rows and map of a table lease
-        (ResidentExpertTable.acquire).  mode: kernel family (B.MOE_FFN_PATH_AUTO / _STREAM / _GEMM)."""
+        (ResidentExpertTable.acquire).  mode: kernel family (B.MOE_FFN_PATH_AUTO / _STREAM / _GEMM).
+        fp16_slots: the rows are FP16 execution slots (moe_fp16_expert_ffn) instead of qpacked rows."""
         T = x.shape[0]
         if lease is not None:
             rows_dev, stride, smap = lease.rows_dev, lease.row_stride, lease.slot_map_dev
         else:
-            rows_dev, stride, smap = (self.rows if rows is None else rows), self.row_stride, self.slot_map
+            rows_dev, stride, smap = self._rows(rows)
+        if fp16_slots:
+            B.moe_fp16_expert_ffn(x, T, self.H, self.I, self.E, self.k, rows_dev, stride, smap, self.expert_offsets,
+                                  self.sorted_pairs, self.active_list, self.n_active, self.h, self.pair_out,
+                                  status=self.status, stream=stream)
+            return
         B.moe_w4a16_expert_ffn(x, T, self.H, self.I, self.E, self.k, rows_dev, stride, smap, self.expert_offsets,
                                self.sorted_pairs, self.active_list, self.n_active, self.h, self.pair_out,
                                status=self.status, mode=mode, stream=stream)
@@ -83,7 +101,7 @@ class RoutedExpertLayer:
 
     def forward(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None, rows=None,
                 shared_out=None, shared_gate=None, table=None, shared: "SharedExpert | None" = None,
-                mode: int = B.MOE_FFN_PATH_AUTO) -> torch.Tensor:
+                mode: int = B.MOE_FFN_PATH_AUTO, fp16_slots: bool = False) -> torch.Tensor:
         """y = layer(x); x float16 [T, H] on the device.  With a ResidentExpertTable the
         routed experts' misses are uploaded (host round trip of the active list; the copies
         run on the table's copy stream) and the expert FFN reads the rows and map of a lease
@@ -104,12 +122,41 @@ class RoutedExpertLayer:
         if table is not None:
             table.prepare(self.active_experts(main), main)
             lease = table.acquire(main)
-        self.ffn(x, main, rows, lease, mode)
+        self.ffn(x, main, rows, lease, mode, fp16_slots=fp16_slots or (table is not None and table.fp16_slots))
         if lease is not None:
             table.release(lease, main)
         if shared is not None:
             main.wait_stream(side)
         self.combine(T, y, shared_out, shared_gate, main)
+        return y
+
+    def forward_fused(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None, rows=None, lease=None,
+                      shared: "SharedExpert | None" = None, mode: int = B.MOE_FFN_PATH_AUTO) -> torch.Tensor:
+        """y = layer(x) through the one-call layer (moe_layer_forward: four launches for decode
+        batches, no host round trip).  rows/lease as for ffn().  With a SharedExpert its FFN runs
+        on a second stream beside the routed work and the combine waits for its event."""
+        T = x.shape[0]
+        if T > self.max_T:
+            self._alloc(T)
+        if y is None:
+            y = torch.empty((T, self.H), dtype=torch.float16, device=self.device)
+        main = _torch_stream(stream)
+        if lease is not None:
+            rows_dev, stride, smap = lease.rows_dev, lease.row_stride, lease.slot_map_dev
+        else:
+            rows_dev, stride, smap = self._rows(rows)
+        sh_out = sh_gate = ready = None
+        if shared is not None:
+            side = shared.side_stream()
+            side.wait_stream(main)
+            shared.run(x, side)
+            ready = shared.ready_event()
+            ready.record(side)
+            sh_out, sh_gate = shared.out, shared.gate
+        B.moe_layer_forward(x, self.router, self.bias, T, self.H, self.I, self.E, self.k, rows_dev, stride, smap,
+                            sh_out, sh_gate, ready, y, self._bufs, mode, main)
+        if shared is not None:
+            main.wait_stream(shared.side_stream())   # the side stream's work is joined before reuse
         return y
 
     def active_experts(self, stream=None):
@@ -162,6 +209,12 @@ class SharedExpert:
         self.out = torch.empty((max(T, 1), self.H), dtype=torch.float32, device=self.device)
         self.gate = torch.empty((max(T, 1),), dtype=torch.float32, device=self.device)
 
+    def ready_event(self) -> torch.cuda.Event:
+        """Event recorded after this expert's kernels (the one-call layer waits for it)."""
+        if getattr(self, "_ready", None) is None:
+            self._ready = torch.cuda.Event()
+        return self._ready
+
     def side_stream(self) -> torch.cuda.Stream:
         """The second stream the layer forks this expert onto (default priority)."""
         if self._side is None:
@@ -189,12 +242,15 @@ class ResidentExpertTable:
     """
 
     def __init__(self, host_rows, H: int, I: int, capacity: int, spare_rows: int, staging_rows: int = 2,
-                 initial_resident=None, top_k: int = 1, max_tokens: int = 1, row_digests=None):
+                 initial_resident=None, top_k: int = 1, max_tokens: int = 1, row_digests=None,
+                 fp16_slots: bool = False):
         import numpy as np
         self.host_rows = np.ascontiguousarray(host_rows)
         self.E = self.host_rows.shape[0]
+        self.fp16_slots = fp16_slots
         self.handle = B.moe_table_create(self.E, H, I, capacity, spare_rows, staging_rows, top_k, max_tokens,
-                                         self.host_rows, self.host_rows.strides[0], initial_resident, row_digests)
+                                         self.host_rows, self.host_rows.strides[0], initial_resident, row_digests,
+                                         slot_format=B.MOE_SLOT_FP16 if fp16_slots else B.MOE_SLOT_QPACKED)
 
     def device(self):
         """(rows, stride, map) of the current generation, without a lease."""
@@ -213,6 +269,10 @@ class ResidentExpertTable:
         misses = self.misses(active)
         self.upload(misses, stream)
         return misses
+
+    def prefetch(self, expert_ids):
+        """Speculative load of experts a later step is expected to route (no stream waits for it)."""
+        B.moe_table_prefetch(self.handle, expert_ids)
 
     def acquire(self, stream=None):
         """Lease on the current generation (stream ordered after its publication)."""
@@ -240,3 +300,71 @@ class ResidentExpertTable:
             self.close()
         except Exception:
             pass
+
+
+class DecodeStack:
+    """Decode through a stack of routed-expert layers with partial residency, chained by the
+    residual stream: x_{l+1} = RN16(x_l + y_l) (moe_residual_add).
+
+    Each layer: route, bring the active experts to the host, one miss transaction on the layer's
+    ResidentExpertTable (copies on its copy stream), a lease on the new generation, the expert FFN
+    on the lease's rows, release, combine (and the FP16 shared expert where given).  With
+    prefetch, layer l+1's router is also applied to x_l before the host round trip of layer l (one
+    wait serves both), and the experts it selects are loaded into layer l+1's table right after
+    layer l's kernels are enqueued, so those copies overlap layer l's compute; layer l+1 then
+    routes its real input and loads only what the prediction missed.  Speculative next-layer
+    loading is named among related systems' staging semantics ("Horizon RunMap - Architecture,
+    Experimental Evidence and Scope", "Architecture comparison matrix", row "Publication/staging
+    semantics"); predicting from the residual stream is this implementation's reading.
+    Results do not depend on prefetching: the same kernels read the same bytes.
+    """
+
+    def __init__(self, layers, tables, shared=None, prefetch: bool = False):
+        self.layers, self.tables = list(layers), list(tables)
+        self.shared = shared
+        self.prefetch = prefetch
+        self.L = len(self.layers)
+        lay = self.layers[0]
+        # predictors: the next layer's router (and bias) on buffers of their own
+        self.preds = [None] + [RoutedExpertLayer(l.H, l.I, l.E, l.k, l.rows, l.router, l.bias, max_T=l.max_T,
+                                                 device=l.device) for l in self.layers[1:]] if prefetch else None
+        self.device = lay.device
+
+    def step(self, x0: torch.Tensor, ys=None, timer=None) -> torch.Tensor:
+        """Runs every layer on x0 (float16 [T, H]); returns x_L.  ys: optional list receiving each
+        layer's y (copies).  timer: optional callable(layer, phase) for event timing."""
+        T, H = x0.shape
+        x = x0
+        main = torch.cuda.current_stream()
+        for l in range(self.L):
+            lay, tab = self.layers[l], self.tables[l]
+            lay.route(x, main)
+            nxt = self.preds[l + 1] if self.prefetch and l + 1 < self.L else None
+            if nxt is not None:
+                nxt.route(x, main)
+            sh = self.shared[l] if self.shared is not None else None
+            if sh is not None:
+                sh.run(x, main)
+            active = lay.active_experts(main)
+            predicted = nxt.active_experts(main) if nxt is not None else None
+            tab.prepare(active, main)
+            lease = tab.acquire(main)
+            if timer:
+                timer(l, "ffn_begin")
+            lay.ffn(x, main, lease=lease, fp16_slots=tab.fp16_slots)
+            if timer:
+                timer(l, "ffn_end")
+            tab.release(lease, main)
+            y = torch.empty((T, H), dtype=torch.float16, device=self.device)
+            if sh is not None:
+                lay.combine(T, y, sh.out, sh.gate, main)
+            else:
+                lay.combine(T, y, stream=main)
+            if predicted is not None:
+                self.tables[l + 1].prefetch(predicted)
+            if ys is not None:
+                ys.append(y)
+            x_next = torch.empty_like(x)
+            B.moe_residual_add(x, y, x_next, T * H, main)
+            x = x_next
+        return x
