@@ -207,7 +207,9 @@ def main():
     replicas = [rows0] + [rows0.clone() for _ in range(R - 1)]
     shared_reps = None
     if Is:
-        sh0 = [torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in shared_np]
+        # gate/up/down in the tile8 layout the shared-expert kernels read (packed on the device)
+        sh0 = [B.pack_tile8(torch.from_numpy(np.ascontiguousarray(m)).to(dev)) for m in shared_np[:3]]
+        sh0.append(torch.from_numpy(np.ascontiguousarray(shared_np[3])).to(dev))
         shared_reps = [sh0] + [[m.clone() for m in sh0] for _ in range(R - 1)]
     router = torch.from_numpy(wr_np).to(dev)
     xs = [torch.from_numpy(x).to(dev) for x in xs_np]

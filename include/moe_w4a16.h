@@ -260,10 +260,10 @@ int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *
  *   hs = RN16(silu(g) * u),  shared_out[t] = Wsd hs (FP32),
  *   shared_gate[t] = 1 / (1 + exp(-(w_sgate . x_t)))  (FP32).
  * The layer output then adds shared_gate[t] * shared_out[t] (moe_combine).
- * Inputs:  x_dev FP16 [T][H]; w_gate_dev, w_up_dev FP16 [Is][H]; w_down_dev
- *          FP16 [H][Is]; w_sgate_dev FP16 [H]; all row-major, 16-byte
- *          aligned.  H and Is positive multiples of 128, each matrix under
- *          2 GiB, 0 <= T <= 65536.
+ * Inputs:  x_dev FP16 [T][H] row-major; w_gate_dev, w_up_dev FP16 [Is][H] and
+ *          w_down_dev FP16 [H][Is] in the tile8 layout (moe_pack_fp16_tile8);
+ *          w_sgate_dev FP16 [H]; all 16-byte aligned.  H and Is positive
+ *          multiples of 128, each matrix under 2 GiB, 0 <= T <= 65536.
  * Outputs: shared_out_dev FP32 [T][H] (16-byte aligned), shared_gate_dev FP32 [T].
  * ws_dev / ws_bytes: workspace of moe_shared_ffn_workspace_size(T, H, Is)
  *   bytes (256-byte aligned) holding hs and, for shapes whose reduction axis
@@ -272,6 +272,16 @@ int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *
  * Two to four kernel launches on `stream` (chunk sums are added in a fixed
  * order: results do not depend on scheduling); T = 0 enqueues nothing. */
 size_t moe_shared_ffn_workspace_size(int T, int H, int Is);
+/* tile8 layout of an FP16 matrix W [R][K] (R a multiple of 8, K of 128): tile
+ * (r8, kt) = rows 8 r8 .. 8 r8 + 7 x columns 128 kt .. 128 kt + 127 is 1024
+ * values at element (r8 * K/128 + kt) * 1024; its piece s (0..3, 256 values
+ * at element s * 256) holds, at element (8 g + r) * 8 + c (g 0..3, r 0..7,
+ * c 0..7), W[8 r8 + r][128 kt + 32 s + 8 g + c].  Each 512-byte piece is the
+ * weight operand of one matrix instruction over 8 rows, read as one
+ * contiguous run.
+ * moe_pack_fp16_tile8: dst_dev (R*K FP16) = tile8 of the row-major src_dev;
+ * both device, 16-byte aligned, not overlapping; one kernel on `stream`. */
+int moe_pack_fp16_tile8(const void *src_dev, void *dst_dev, int R, int K, void *stream);
 int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_dev, const void *w_down_dev,
                    const void *w_sgate_dev, int T, int H, int Is, float *shared_out_dev, float *shared_gate_dev,
                    void *ws_dev, size_t ws_bytes, void *stream);

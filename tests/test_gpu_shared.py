@@ -27,9 +27,13 @@ def small_shared(H, Is, seed):
 def run_shared(x, shared):
     from w4a16_routed_expert_amd import binding as B
     dev = torch.device("cuda:0")
-    Wsg, Wsu, Wsd, wg = (torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in shared)
+    from w4a16_routed_expert_amd import synth
+    # the kernels read the tile8 layout; packed here by the numpy packer (the
+    # library's own packer is checked against it below)
+    Wsg, Wsu, Wsd = (torch.from_numpy(synth.pack_fp16_tile8(m)).to(dev) for m in shared[:3])
+    wg = torch.from_numpy(np.ascontiguousarray(shared[3])).to(dev)
     T, H = x.shape
-    Is = Wsg.shape[0]
+    Is = shared[0].shape[0]
     xd = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     out = torch.full((max(T, 1), H), float("nan"), dtype=torch.float32, device=dev)
     sig = torch.full((max(T, 1),), float("nan"), dtype=torch.float32, device=dev)
@@ -49,6 +53,17 @@ def check_shared(x, shared, what):
     check_shared_stages(dict(x=x, shared_hs=hs, shared_os=os_gpu.astype(np.float64),
                              shared_sigma=sig_gpu.astype(np.float64)),
                         dict(shared_os=os_ref, shared_sigma=sig_ref), shared, what)
+
+
+@pytest.mark.parametrize("R,K", [(8, 128), (16, 256), (40, 384), (2048, 5632)])
+def test_tile8_packer_matches_numpy(R, K):
+    from w4a16_routed_expert_amd import binding as B, synth
+    dev = torch.device("cuda:0")
+    w = (np.random.default_rng(R + K).standard_normal((R, K)) * 4).astype(np.float16)
+    got = B.pack_tile8(torch.from_numpy(w).to(dev))
+    torch.cuda.synchronize()
+    want = synth.pack_fp16_tile8(w)
+    assert np.array_equal(got.cpu().numpy().view(np.uint16), want.view(np.uint16)), f"tile8 {R}x{K}"
 
 
 @pytest.mark.parametrize("T", [1, 5, 16, 20, 33, 70])

@@ -378,6 +378,34 @@ def test_batch_invariance():
 
 
 # ------------------------------------------------------------ shared expert
+def test_tile8_packer_places_values_at_the_documented_positions():
+    # The shared expert's kernels read its matrices in the tile8 layout; the
+    # oracle reads them row-major, so the packer is the only link between the
+    # two.  A hand-computed position: R = 16, K = 256 (two 128-column tiles
+    # per row group), W[9][161]: 8-row tile r8 = 1, row r = 1; column 161 =
+    # 128 + 32*1 + 8*0 + 1, so kt = 1, piece s = 1, g = 0, c = 1; flat index
+    # ((r8 * 2 + kt) * 4 + s) * 256 + (8 g + r) * 8 + c = 13 * 256 + 9.
+    w = np.zeros((16, 256), np.float16)
+    w[9, 161] = 1.0
+    p = synth.pack_fp16_tile8(w)
+    assert np.flatnonzero(p).tolist() == [13 * 256 + 9]
+    # every position, by the documented index formula written as loops
+    R, K = 24, 384
+    w = (np.arange(R * K) % 2039).astype(np.float16).reshape(R, K)          # integers, exact in FP16
+    p = synth.pack_fp16_tile8(w)
+    NT = K // 128
+    for r8 in range(R // 8):
+        for kt in range(NT):
+            for s_ in range(4):
+                for g in range(4):
+                    for r in range(8):
+                        for c in range(8):
+                            idx = ((r8 * NT + kt) * 4 + s_) * 256 + (8 * g + r) * 8 + c
+                            assert p[idx] == w[8 * r8 + r, 128 * kt + 32 * s_ + 8 * g + c]
+    # a permutation: nothing lost or duplicated
+    assert np.array_equal(np.sort(p), np.sort(w.reshape(-1)))
+
+
 def test_shared_expert_matches_numpy():
     g = np.random.default_rng(31)
     T, H, Is = 3, 128, 96

@@ -37,7 +37,7 @@ EXPORTS = (
     "moe_version", "moe_last_error", "moe_expert_row_bytes",
     "moe_route_workspace_size", "moe_route", "moe_route_exact", "moe_route_static_max_bytes", "moe_route_static",
     "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
-    "moe_combine", "moe_shared_ffn_workspace_size", "moe_shared_ffn",
+    "moe_combine", "moe_shared_ffn_workspace_size", "moe_shared_ffn", "moe_pack_fp16_tile8",
     "moe_layer_workspace_size", "moe_layer_forward", "moe_residual_add",
     "moe_expert_row_bytes_fp16", "moe_dequant_expert_rows", "moe_fp16_expert_ffn",
     "moe_row_digest", "moe_table_create", "moe_table_destroy", "moe_table_device", "moe_table_misses",
@@ -122,6 +122,8 @@ def load(path: str = LIB_PATH):
     L.moe_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]
     L.moe_shared_ffn_workspace_size.restype = _sz
     L.moe_shared_ffn_workspace_size.argtypes = [_i, _i, _i]
+    L.moe_pack_fp16_tile8.restype = _i
+    L.moe_pack_fp16_tile8.argtypes = [_vp, _vp, _i, _i, _vp]
     L.moe_shared_ffn.restype = _i
     L.moe_shared_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]
     L.moe_row_digest.restype = ctypes.c_uint64
@@ -268,6 +270,20 @@ def moe_shared_ffn_workspace_size(T, H, Is) -> int:
 def moe_shared_ffn(x, w_gate, w_up, w_down, w_sgate, T, H, Is, shared_out, shared_gate, ws, ws_bytes, stream=None):
     _check(load().moe_shared_ffn(_p(x), _p(w_gate), _p(w_up), _p(w_down), _p(w_sgate), T, H, Is, _p(shared_out),
                                  _p(shared_gate), _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_pack_fp16_tile8(src, dst, R, K, stream=None):
+    _check(load().moe_pack_fp16_tile8(_p(src), _p(dst), R, K, _s(stream)))
+
+
+def pack_tile8(w):
+    """A new device tensor holding the tile8 layout of the row-major float16 device matrix w [R, K]
+    (moe_pack_fp16_tile8 on the current stream)."""
+    import torch
+    R, K = w.shape
+    out = torch.empty(R * K, dtype=torch.float16, device=w.device)
+    moe_pack_fp16_tile8(w.contiguous(), out, R, K, torch.cuda.current_stream())
+    return out
 
 
 def moe_layer_workspace_size(T, H, E) -> int:

@@ -7,21 +7,31 @@
 // weighted sum.  Rounding points are those of a routed expert: FP32 sums, the
 // SwiGLU activation rounded to FP16 before the down projection, FP32 outputs.
 //
+// Weight layout ("tile8", written by moe_pack_fp16_tile8 from row-major
+// [R][K]): tile (r8, kt) = rows 8 r8 .. 8 r8 + 7 x columns 128 kt .. 128 kt +
+// 127, 2048 bytes at element (r8 * K/128 + kt) * 1024; its piece s (512 bytes
+// at element s * 256) holds, at element (8 g + r) * 8, row 8 r8 + r, columns
+// 128 kt + 32 s + 8 g .. +7.  One MFMA B operand of 8 rows (32 columns) is
+// then one contiguous 512-byte run: row-major weights would give each
+// instruction sixteen 64-byte runs, which stream from HBM about a fifth
+// slower (measured on the MI355X with a read-pattern probe).
+//
 // Kernel design (gfx950, wave64).  Decode batches make this a skinny GEMM,
 // bound by HBM (69 MB of FP16 weights for the Qwen shape), and a CU only
 // streams at its share of HBM bandwidth when it holds an equal share of the
 // bytes, so the work is cut into many equal units:
-//   * The weights are plain row-major [R][K] FP16.  A unit is 16 output rows
+//   * The weights are in the tile8 layout above.  A unit is 16 output rows
 //     (gate/up: the same 16 rows of both matrices) x one chunk of the
 //     reduction axis x one pass of up to 16 MT tokens.  The chunk count NKC
 //     is planned on the host so that the units spread evenly over 256 blocks
 //     and the 8 wavefronts of a block share a chunk's 128-column tiles
 //     (wave w takes tiles w, w + 8 of the chunk, NTW <= 2 per wave).
-//   * Per tile a lane loads four 16-byte pieces of its row (columns 32s +
-//     8g .. +7): each is one MFMA B operand as stored, and the A operand is
-//     the same columns of a token's activation row, read straight from
-//     memory (L2-resident).  Every wave keeps its NTW tiles of the next unit
-//     in flight while it computes the current one.
+//   * Per 128-column tile a lane loads four 16-byte pieces of its row
+//     (columns 32s + 8g .. +7, one from each 512-byte piece of its 8-row
+//     tile): each is one MFMA B operand as stored, and the A operand is the
+//     same columns of a token's activation row, read straight from memory
+//     (L2-resident).  Every wave keeps its NTW tiles of the next unit in
+//     flight while it computes the current one.
 //   * The 8 partial sums of a unit meet in LDS and are added in wave order;
 //     the unit's FP32 result goes to partial sums [NKC][T][NMAT R], which a
 //     second kernel adds in chunk order (gate/up: then the SwiGLU into hs,
@@ -52,9 +62,9 @@ constexpr int kPlanBlocks = 256;          // blocks the chunking is planned for 
 
 struct SArgs {
     const uint16_t *x;      // [T][H]
-    const uint16_t *wg;     // [Is][H]
-    const uint16_t *wu;     // [Is][H]
-    const uint16_t *wd;     // [H][Is]
+    const uint16_t *wg;     // [Is][H], tile8 layout
+    const uint16_t *wu;     // [Is][H], tile8 layout
+    const uint16_t *wd;     // [H][Is], tile8 layout
     const uint16_t *wgate;  // [H]
     int T, H, Is;
     uint16_t *hs;           // [T][Is] FP16 activations between the projections
@@ -170,7 +180,10 @@ __global__ __launch_bounds__(kThreads) void fp16_stream_kernel(SArgs a, int nkc,
         const int rg = rest % RG, p = rest / RG;
         q.kt0 = kc * NT / nkc;
         q.kt1 = any ? (kc + 1) * NT / nkc : q.kt0;
-        q.wvoff = n16 < RU ? ((rg * RU + n16) * K + 8 * g4) * 2 : kOob;
+        // row rg RU + n16: 8-row tile r8, row r within it; pieces start at
+        // the tile's byte (r8 NT) 2048 plus kt 2048 + s 512 (soffset)
+        const int row = rg * RU + n16;
+        q.wvoff = n16 < RU ? (((row >> 3) * NT) * 1024 + (8 * g4 + (row & 7)) * 8) * 2 : kOob;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int tok = (p * MT + m) * 16 + n16;
@@ -183,24 +196,24 @@ __global__ __launch_bounds__(kThreads) void fp16_stream_kernel(SArgs a, int nkc,
     // and activation fragments are the same in each: loaded once and kept.
     const bool act_fixed = passes == 1 && n_main % nkc == 0;
     u32x4 wb[NTW][NMAT][4], ab[NTW][MT][4];
-    auto issue_act = [&](const Src &q, int j, bool ok, int soff) {
+    auto issue_act = [&](const Src &q, int j, bool ok, int kt) {
         const __amdgpu_buffer_rsrc_t arr = rsrc(am, ok ? abytes : 0);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ab[j][m][s] = bload(arr, q.avoff[m], soff + 64 * s);
+            for (int s = 0; s < 4; ++s) ab[j][m][s] = bload(arr, q.avoff[m], kt * 256 + 64 * s);
     };
     auto issue = [&](const Src &q, int j, bool with_act) {
-        const int kt = q.kt0 + wave + 8 * j;
-        const bool ok = kt < q.kt1;
-        const int soff = (ok ? kt : 0) * 256;
+        const int kt0 = q.kt0 + wave + 8 * j;
+        const bool ok = kt0 < q.kt1;
+        const int kt = ok ? kt0 : 0;
 #pragma unroll
         for (int mat = 0; mat < NMAT; ++mat) {
             const __amdgpu_buffer_rsrc_t wr = rsrc(wm[mat], ok ? wbytes : 0);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) wb[j][mat][s] = bload(wr, q.wvoff, soff + 64 * s);
+            for (int s = 0; s < 4; ++s) wb[j][mat][s] = bload(wr, q.wvoff, kt * 2048 + 512 * s);
         }
-        if (with_act) issue_act(q, j, ok, soff);
+        if (with_act) issue_act(q, j, ok, kt);
     };
 
     int u = blockIdx.x;
@@ -305,6 +318,24 @@ __global__ __launch_bounds__(kThreads) void shared_down_finish(SArgs a, int nkc)
         f32x4 v = *reinterpret_cast<const f32x4 *>(pp);
         for (int kc = 1; kc < nkc; ++kc) v += *reinterpret_cast<const f32x4 *>(pp + kc * stride);
         *reinterpret_cast<f32x4 *>(a.out + (size_t)t * a.H + c) = v;
+    }
+}
+
+// tile8 packing: one thread per 16-byte chunk of the packed matrix (8
+// consecutive FP16 values of one row), read from the row-major source.
+__global__ __launch_bounds__(256) void pack_tile8_kernel(const uint16_t *src, uint16_t *dst, int R, int K)
+{
+    const int NT = K / 128;
+    const long long chunks = (long long)R * K / 8;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (long long)gridDim.x * 256) {
+        const long long tile = i >> 7;                    // 128 chunks per 2048-byte tile
+        const int j = (int)(i & 127);
+        const int s = j >> 5, g = (j >> 3) & 3, r = j & 7;
+        const long long r8 = tile / NT;
+        const int kt = (int)(tile - r8 * NT);
+        const long long row = 8 * r8 + r;
+        const long long col = 128LL * kt + 32 * s + 8 * g;
+        *reinterpret_cast<u32x4 *>(dst + 8 * i) = *reinterpret_cast<const u32x4 *>(src + row * K + col);
     }
 }
 
@@ -464,6 +495,27 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
     if (rc || pd.nkc == 1) return rc;
     hipLaunchKernelGGL(shared_down_finish, dim3(grid_of((long long)T * (H / 4))), dim3(kThreads), 0, s, a, pd.nkc);
     return moe::check_launch("moe_shared_ffn (down sums)");
+}
+
+int moe_pack_fp16_tile8(const void *src_dev, void *dst_dev, int R, int K, void *stream)
+{
+    moe::clear_error();
+    if (R <= 0 || K <= 0 || R % 8 || K % 128)
+        return moe::fail(MOE_ERR_UNSUPPORTED, "moe_pack_fp16_tile8: R=%d must be a positive multiple of 8 and "
+                         "K=%d of 128", R, K);
+    if ((long long)R * K * 2 >= (1ll << 31)) return moe::fail(MOE_ERR_UNSUPPORTED, "moe_pack_fp16_tile8: over 2 GiB");
+    if (!src_dev || !dst_dev) return moe::fail(MOE_ERR_INVALID_ARG, "moe_pack_fp16_tile8: null pointer argument");
+    if (!moe::aligned(src_dev, 16) || !moe::aligned(dst_dev, 16))
+        return moe::fail(MOE_ERR_INVALID_ARG, "moe_pack_fp16_tile8: src and dst must be 16-byte aligned");
+    const uintptr_t a0 = (uintptr_t)src_dev, b0 = (uintptr_t)dst_dev, n = (uintptr_t)R * K * 2;
+    if (a0 < b0 + n && b0 < a0 + n)
+        return moe::fail(MOE_ERR_INVALID_ARG, "moe_pack_fp16_tile8: src and dst overlap");
+    const long long chunks = (long long)R * K / 8;
+    long long g = (chunks + 255) / 256;
+    if (g > 8LL * ffn::cu_count()) g = 8LL * ffn::cu_count();
+    hipLaunchKernelGGL(pack_tile8_kernel, dim3((unsigned int)g), dim3(256), 0, (hipStream_t)stream,
+                       (const uint16_t *)src_dev, (uint16_t *)dst_dev, R, K);
+    return moe::check_launch("moe_pack_fp16_tile8");
 }
 
 }  // extern "C"

@@ -51,6 +51,10 @@ class RoutedExpertLayer:
         self.h = torch.empty((n, I), dtype=torch.float16, device=d)
         self.pair_out = torch.empty((n, H), dtype=torch.float32, device=d)
         self.status = torch.zeros(1, dtype=torch.int32, device=d)
+        # host copy of [n_active, active_list] (pinned, so the copies are asynchronous), and the
+        # event the host waits on for it
+        self._act_host = torch.empty(E + 1, dtype=torch.int32, pin_memory=True)
+        self._act_evt = torch.cuda.Event()
         # workspace of the one-call layer: zero-filled once, left zero by every call
         self.layer_ws = torch.zeros(max(B.moe_layer_workspace_size(T, H, E), 256), dtype=torch.uint8, device=d)
         self._bufs = B.layer_buffers(self.logits, self.topk_ids, self.topk_w, self.expert_offsets, self.sorted_pairs,
@@ -163,9 +167,25 @@ class RoutedExpertLayer:
         """Active expert ids of the last route, on the host.  The copies are ordered after
         the work already enqueued on `stream` (the stream the route ran on; None = the
         current stream), and the call waits for them."""
-        with torch.cuda.stream(_torch_stream(stream)):
-            n = int(self.n_active.cpu()[0])
-            return self.active_list[:n].cpu().numpy()
+        self.enqueue_active_copy(stream).synchronize()
+        return self.host_active()
+
+    def enqueue_active_copy(self, stream=None) -> torch.cuda.Event:
+        """Enqueues the copy of n_active and the active list to pinned host memory on `stream`
+        (None = the current stream) and returns the event recorded after it; read them with
+        host_active() once that event has completed.  Lets several layers' lists come back with
+        one wait."""
+        s = _torch_stream(stream)
+        with torch.cuda.stream(s):
+            self._act_host[:1].copy_(self.n_active, non_blocking=True)
+            self._act_host[1:].copy_(self.active_list, non_blocking=True)
+        self._act_evt.record(s)
+        return self._act_evt
+
+    def host_active(self):
+        """The active expert ids copied by the last enqueue_active_copy (after its stream's wait)."""
+        n = int(self._act_host[0])
+        return self._act_host[1:1 + n].numpy().copy()
 
     def check_status(self, stream=None):
         """Raises MoeError if an expert FFN call since this layer's buffers were made
@@ -190,14 +210,17 @@ def _torch_stream(stream):
 class SharedExpert:
     """FP16 shared expert (moe_shared_ffn) with its output buffers and workspace.
 
-    wg, wu: float16 CUDA tensors [Is, H]; wd: [H, Is]; wgate: [H] (16-byte aligned).
+    wg, wu: row-major float16 CUDA tensors [Is, H]; wd: [H, Is]; wgate: [H] (16-byte aligned).
+    The matrices are packed into the tile8 layout the kernels read (moe_pack_fp16_tile8) once,
+    here; the row-major inputs are not kept.
     out (FP32 [T, H]) and gate (FP32 [T]) hold the last run's shared_out and shared_gate.
     """
 
     def __init__(self, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor, wgate: torch.Tensor,
                  max_T: int = 64, device: str | torch.device = "cuda:0"):
-        self.wg, self.wu, self.wd, self.wgate = wg, wu, wd, wgate
         self.Is, self.H = wg.shape
+        self.wg, self.wu, self.wd = B.pack_tile8(wg), B.pack_tile8(wu), B.pack_tile8(wd)
+        self.wgate = wgate
         self.device = torch.device(device)
         self._side = None
         self.max_T = 0
@@ -345,8 +368,13 @@ class DecodeStack:
             sh = self.shared[l] if self.shared is not None else None
             if sh is not None:
                 sh.run(x, main)
-            active = lay.active_experts(main)
-            predicted = nxt.active_experts(main) if nxt is not None else None
+            # one wait brings back this layer's active list and the predicted next-layer list
+            ev = lay.enqueue_active_copy(main)
+            if nxt is not None:
+                ev = nxt.enqueue_active_copy(main)
+            ev.synchronize()
+            active = lay.host_active()
+            predicted = nxt.host_active() if nxt is not None else None
             tab.prepare(active, main)
             lease = tab.acquire(main)
             if timer:

@@ -230,6 +230,18 @@ def make_shared(cfg: LayerConfig, layer: int = 0):
     return tuple(out)
 
 
+def pack_fp16_tile8(w: np.ndarray) -> np.ndarray:
+    """The tile8 layout of an FP16 matrix [R][K] (R % 8 == 0, K % 128 == 0), as a flat float16
+    array: tile (r8, kt) of 8 rows x 128 columns at element (r8 * K/128 + kt) * 1024, its piece s
+    (256 values) at s * 256, and inside the piece element (8 g + r) * 8 + c = w[8 r8 + r][128 kt +
+    32 s + 8 g + c].  A permutation of the values (no arithmetic)."""
+    R, K = w.shape
+    if R % 8 or K % 128:
+        raise ValueError(f"tile8 needs R % 8 == 0 and K % 128 == 0, got {R}x{K}")
+    a = np.ascontiguousarray(w, dtype=np.float16).reshape(R // 8, 8, K // 128, 4, 4, 8)   # r8 r kt s g c
+    return np.ascontiguousarray(a.transpose(0, 2, 3, 4, 1, 5)).reshape(-1)             # r8 kt s g r c
+
+
 def expected_active(E: int, k: int, T: int) -> float:
     """E * (1 - (1 - k/E)^T): expected number of distinct experts hit by T tokens (planning only)."""
     return E * (1.0 - math.pow(1.0 - k / E, T))
