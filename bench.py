@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--fused", action="store_true",
                     help="run each step through the one-call layer (moe_layer_forward) instead of the separate calls")
+    ap.add_argument("--ffn-mode", choices=["auto", "stream", "ksplit"], default="auto",
+                    help="--fused: the expert-FFN family of the one call (auto: the K-split launch for the "
+                         "smallest batches, else the streaming kernels)")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="olmoe: skip the prefill measurement (T=4096, grouped GEMM) that the line carries")
@@ -279,6 +282,9 @@ def main():
 
     shared_done = torch.cuda.Event() if Is else None
 
+    fused_mode = {"auto": B.MOE_FFN_PATH_AUTO, "stream": B.MOE_FFN_PATH_STREAM,
+                  "ksplit": B.MOE_FFN_PATH_KSPLIT}[args.ffn_mode]
+
     def run_step_fused(s, ev=None):
         """One step through the one-call layer (moe_layer_forward); the shared expert, where
         the layer has one, runs on the second stream and the call's combine waits for it."""
@@ -293,7 +299,7 @@ def main():
             B.moe_shared_ffn(x, Wsg, Wsu, Wsd, wg, T, H, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes, side)
             shared_done.record(side)
         B.moe_layer_forward(x, router, None, T, H, I, E, k, rows, lay.row_stride, None, sh_out if Is else None,
-                            sh_gate if Is else None, shared_done, y, lay._bufs, B.MOE_FFN_PATH_AUTO, main)
+                            sh_gate if Is else None, shared_done, y, lay._bufs, fused_mode, main)
         if Is:
             main.wait_stream(side)
         if ev is not None:
@@ -474,7 +480,7 @@ def main():
             "experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
             "shared_expert_intermediate": Is,
             "shared_expert_stream": "second stream, concurrent with routing and the routed experts" if Is else None,
-            "layer_call": "moe_layer_forward (one call)" if args.fused else "separate calls",
+            "layer_call": f"moe_layer_forward (one call, expert FFN {args.ffn_mode})" if args.fused else "separate calls",
             "weights": "int4 qpacked, 256-value blocks, fp16 scales; fp16 activations, fp32 accumulation",
             "replicas": R, "input_batches": S, "graph_replay": not args.no_graph,
             "steps_per_graph": None if args.no_graph else G,

@@ -189,7 +189,8 @@ int moe_route_static(const void *x_dev, const void *w_router_dev, const float *b
  *     (built for prefill batches, bound by the matrix cores);
  *   MOE_FFN_PATH_AUTO: the GEMM when T*k >= 64*E, else the streaming kernels.
  * Any other value returns MOE_ERR_INVALID_ARG. */
-enum moe_ffn_path { MOE_FFN_PATH_AUTO = 0, MOE_FFN_PATH_STREAM = 1, MOE_FFN_PATH_GEMM = 2 };
+enum moe_ffn_path { MOE_FFN_PATH_AUTO = 0, MOE_FFN_PATH_STREAM = 1, MOE_FFN_PATH_GEMM = 2, MOE_FFN_PATH_KSPLIT = 3 };
+/* MOE_FFN_PATH_KSPLIT: moe_layer_forward only (the FFN calls reject it); see there. */
 
 int moe_w4a16_gateup(const void *x_dev, int T, int H, int I, int E, int k,
                      const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
@@ -209,22 +210,32 @@ int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
 
 /* ------------------------------------------------------------ whole layer
  * moe_layer_forward: route -> gate/up + SiLU*up -> down -> combine in one call,
- * with the results of moe_route, the FFN calls and moe_combine (the same
- * kernels after the routing; y is bit-identical to the separate calls).
- * Decode batches (the streaming kernels: mode STREAM, or AUTO with
+ * with the results of moe_route, the FFN calls and moe_combine (the pages'
+ * "top4-fused-v1" executor is prior art for fusing the layer: "Horizon
+ * RunMap - architecture", section "Regimes and executor boundaries").
+ * Decode batches (the streaming kernels: mode STREAM or KSPLIT, or AUTO with
  * T*k < 64*E, and T <= 256) route in one launch instead of two: the block
  * that finishes its logits last runs the top-k and the grouping (no block
- * waits for another), so the layer is four launches with no host round trip
- * (the pages' "top4-fused-v1" executor is prior art for fusing the layer:
- * "Horizon RunMap - architecture", section "Regimes and executor
- * boundaries").  Other batches run moe_route, moe_w4a16_expert_ffn and
- * moe_combine in order.
+ * waits for another).  Then
+ *   - mode KSPLIT (T <= 16, H <= 2048 with H/128 even, I <= 2048; AUTO
+ *     does not choose it: measured slower than the streaming kernels at
+ *     every batch so far): ONE expert-FFN launch for gate/up and down.  Its work items are (active expert, slice of W columns of I);
+ *     the block of an item keeps that slice of h in LDS and multiplies it
+ *     with the same columns of the down matrix, writing partial pair outputs
+ *     to I/W planes in the workspace; the combine adds each pair's planes in
+ *     plane order (and writes that sum to pair_out).  Same operation and
+ *     rounding points; only the FP32 summation order of the down projection
+ *     differs from the streaming kernels.  Three launches in all.
+ *   - otherwise the streaming gate/up and down launches and the combine (y
+ *     then bit-identical to the separate calls).
+ * Other batches run moe_route, moe_w4a16_expert_ffn and moe_combine in order.
  * Buffers (device, caller-owned, sized for T): the routing outputs and the
- * FFN intermediates of moe_route / moe_w4a16_expert_ffn, plus
- *   ws / ws_bytes: moe_layer_workspace_size(T, H, E) bytes, 256-byte aligned,
- *     ZERO-FILLED BEFORE ITS FIRST USE; every call leaves its counter zero
- *     again (a workspace sized for T serves any T' <= T); not shared by calls
- *     that can overlap.
+ * FFN intermediates of moe_route / moe_w4a16_expert_ffn (h and pair_out are
+ * written on every path), plus
+ *   ws / ws_bytes: moe_layer_workspace_size(T, H, I, E, k) bytes, 256-byte
+ *     aligned, ZERO-FILLED BEFORE ITS FIRST USE; every call leaves its counter
+ *     zero again (a workspace sized for T serves any T' <= T); not shared by
+ *     calls that can overlap.
  * shared_out / shared_gate: the shared-expert terms (moe_shared_ffn) or both
  * NULL; shared_ready_event: a hipEvent_t recorded after the shared expert (on
  * another stream), waited for before the combine, or NULL when the shared
@@ -245,7 +256,7 @@ typedef struct {
     size_t ws_bytes;
 } moe_layer_buffers;
 
-size_t moe_layer_workspace_size(int T, int H, int E);
+size_t moe_layer_workspace_size(int T, int H, int I, int E, int k);
 int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int I,
                       int E, int k, const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                       const float *shared_out_dev, const float *shared_gate_dev, void *shared_ready_event,

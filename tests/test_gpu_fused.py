@@ -1,14 +1,16 @@
 """GPU parity of the one-call layer (moe_layer_forward) against the CPU oracle,
 through the C ABI.
 
-For decode batches the call runs four launches: routing in one (the last
-block to finish its logits runs the top-k and the grouping), gate/up, down
-and the combine.  Every stage is compared with the oracle as in
+For decode batches the call routes in one launch (the last block to finish
+its logits runs the top-k and the grouping).  With the streaming kernels it
+then runs gate/up, down and the combine, and y must equal the separate calls'
+y bit for bit; with the K-split expert FFN (MOE_FFN_PATH_KSPLIT, opt-in)
+gate/up and down run in one launch that writes partial outputs per slice of
+the intermediate axis, and the combine adds them.  Every stage is compared with the oracle as in
 test_gpu_parity.py (routing and grouping bit for bit, h within one FP16 ulp,
-expert outputs and y within tolerance, plus the stage-wise check), and y must
-equal the separate calls' y bit for bit.  Shapes: the OLMoE-shaped layer at
-T = 1/8/32, the Qwen-shaped layer with its shared expert (on a second stream,
-joined by an event before the combine) at T = 1/16/64, the tiny layer, odd
+expert outputs and y within tolerance, plus the stage-wise check).  Shapes:
+the OLMoE-shaped layer, the Qwen-shaped layer with its shared expert (on a
+second stream, joined by an event before the combine), the tiny layer, odd
 shapes, an absent expert, batches that take the separate kernels, repeated
 calls and graph replay.
 """
@@ -23,9 +25,13 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def both(cfg, rows, wr, x, **kw):
-    fused = gpu_layer(cfg, rows, wr, x, fused=True, **kw)
-    sep = gpu_layer(cfg, rows, wr, x, **kw)
+STREAM, KSPLIT = 1, 3            # MOE_FFN_PATH_STREAM, MOE_FFN_PATH_KSPLIT
+
+
+def both(cfg, rows, wr, x, mode=STREAM, **kw):
+    """The one-call layer and the separate calls with the same kernel family: y bit-identical."""
+    fused = gpu_layer(cfg, rows, wr, x, fused=True, mode=mode, **kw)
+    sep = gpu_layer(cfg, rows, wr, x, mode=mode, **kw)
     assert np.array_equal(fused["y"].view(np.uint16), sep["y"].view(np.uint16)), \
         "one-call layer and separate calls differ"
     return fused
@@ -77,6 +83,53 @@ def test_odd_shapes_one_call(H, I):
     check_full(cfg, both(cfg, rows, wr, x, mode=1), ref, f"one-call H={H} I={I}", rows=rows)
 
 
+@pytest.mark.parametrize("name,T", [("olmoe", 1), ("olmoe", 2), ("olmoe", 3), ("olmoe", 8), ("olmoe", 16),
+                                    ("qwen", 1), ("qwen", 5), ("qwen", 16), ("tiny", 1), ("tiny", 16)])
+def test_ksplit_expert_ffn_one_call(name, T):
+    # gate/up and down of a slice of the intermediate axis in one block,
+    # partial outputs per slice added by the combine: slice widths 32 (T = 1
+    # to 3 on the OLMoE shape, 44 planes on the Qwen shape), 64 and 128, and
+    # the tiny layer's H = 256 (two tiles, one wave per row group)
+    cfg = synth.CONFIGS[name]
+    rows, wr, x = rows_of(name), synth.make_router(cfg), synth.make_x(cfg, T, step=30 + T)
+    shared = synth.make_shared(cfg) if cfg.shared_I else None
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, shared=shared, want_h=True)
+    got = gpu_layer(cfg, rows, wr, x, fused=True, mode=KSPLIT, shared=shared)
+    assert got["status"] == 0
+    check_full(cfg, got, ref, f"k-split {name} T={T}", rows=rows)
+    assert workspace_is_zero(got["layer"], T)
+
+
+@pytest.mark.parametrize("T,path", [(1, STREAM), (8, STREAM), (32, STREAM)])
+def test_auto_keeps_the_streaming_ffn_in_one_call(T, path):
+    # AUTO runs the same kernels as the forced mode, so the bits agree (the
+    # K-split launch is opt-in: measured slower)
+    cfg = synth.CONFIGS["olmoe"]
+    rows, wr, x = rows_of("olmoe"), synth.make_router(cfg), synth.make_x(cfg, T, step=40)
+    auto = gpu_layer(cfg, rows, wr, x, fused=True)
+    forced = gpu_layer(cfg, rows, wr, x, fused=True, mode=path)
+    assert np.array_equal(auto["y"].view(np.uint16), forced["y"].view(np.uint16))
+
+
+def test_ksplit_absent_expert():
+    # an expert without a device row: status word set, its pairs' outputs
+    # zero, the other pairs as with the streaming kernels (within tolerance:
+    # the down projection's FP32 summation order differs)
+    cfg = synth.CONFIGS["tiny"]
+    T = 6
+    rows, wr, x = rows_of("tiny"), synth.make_router(cfg), synth.make_x(cfg, T, step=41)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k)
+    missing = int(ref["active"][0])
+    slot_map = np.arange(cfg.E, dtype=np.int32)
+    slot_map[missing] = -1
+    got = gpu_layer(cfg, rows, wr, x, slot_map=slot_map, fused=True, mode=KSPLIT)
+    st = gpu_layer(cfg, rows, wr, x, slot_map=slot_map, fused=True, mode=STREAM)
+    assert got["status"] == 7 and st["status"] == 7
+    lo, hi = ref["offsets"][missing], ref["offsets"][missing + 1]
+    assert np.all(got["pair_out"][lo:hi] == 0) and np.all(got["h"][lo:hi] == 0)
+    np.testing.assert_allclose(got["pair_out"], st["pair_out"], rtol=2e-3, atol=2e-3 * np.abs(st["pair_out"]).max())
+
+
 def test_batches_that_take_the_separate_kernels():
     # T > 256 and the grouped GEMM: the call runs the separate kernels
     from w4a16_routed_expert_amd import binding as B
@@ -96,8 +149,8 @@ def test_absent_expert_one_call():
     missing = int(ref["active"][0])
     slot_map = np.arange(cfg.E, dtype=np.int32)
     slot_map[missing] = -1
-    got = gpu_layer(cfg, rows, wr, x, slot_map=slot_map, fused=True)
-    sep = gpu_layer(cfg, rows, wr, x, slot_map=slot_map)
+    got = gpu_layer(cfg, rows, wr, x, slot_map=slot_map, fused=True, mode=STREAM)
+    sep = gpu_layer(cfg, rows, wr, x, slot_map=slot_map, mode=STREAM)
     assert got["status"] == 7
     lo, hi = ref["offsets"][missing], ref["offsets"][missing + 1]
     assert np.all(got["pair_out"][lo:hi] == 0)
@@ -115,7 +168,10 @@ def test_repeated_calls_and_graph_replay():
     lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev), torch.from_numpy(wr).to(dev),
                             max_T=32, device=dev)
     xs = {T: torch.from_numpy(synth.make_x(cfg, T, step=16 + T)).to(dev) for T in (32, 1, 8)}
-    want = {T: lay.forward(x).clone() for T, x in xs.items()}
+    # references: T = 32 the separate calls (same kernels), the small batches
+    # a first one-call run (the K-split expert FFN, which the separate calls
+    # do not have)
+    want = {T: (lay.forward(x) if T == 32 else lay.forward_fused(x)).clone() for T, x in xs.items()}
     torch.cuda.synchronize()
     for _ in range(2):
         for T, x in xs.items():

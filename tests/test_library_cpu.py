@@ -94,6 +94,30 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert "shared" in B.moe_last_error()
 
 
+def test_layer_ksplit_mode_checks_and_workspace(lib):
+    F = 0x1000
+    buf = B.LayerBuffers(F, F, F, F, F, F, F, F, F, F, F, F, 1 << 30)
+    # the K-split expert FFN needs T <= 16, H/128 even and H, I <= 2048: rejected on the host
+    for T, H, I in ((17, 256, 512), (4, 384, 512), (4, 256, 4096)):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_layer_forward(F, F, None, T, H, I, 8, 2, F, 1 << 20, None, None, None, None, F, buf,
+                                mode=B.MOE_FFN_PATH_KSPLIT, stream=0)
+        assert ei.value.code == B.MOE_ERR_UNSUPPORTED and "K-split" in B.moe_last_error()
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_layer_forward(F, F, None, 4, 256, 512, 8, 2, F, 1 << 20, None, None, None, None, F, buf, mode=4,
+                            stream=0)
+    assert ei.value.code == B.MOE_ERR_INVALID_ARG
+    # a workspace sized for T serves every smaller batch (the planes of the
+    # K-split path depend on the batch through the slice width)
+    for (H, I, E, k) in ((2048, 1024, 64, 8), (2048, 1408, 60, 4), (256, 512, 8, 2)):
+        sizes = [B.moe_layer_workspace_size(T, H, I, E, k) for T in range(0, 40)]
+        assert all(b >= a for a, b in zip(sizes, sizes[1:])), (H, I, E, k)
+        # T = 1 on the OLMoE shape: 8 pairs x 32 planes of 2048 FP32 values at least
+        if (H, I, E, k) == (2048, 1024, 64, 8):
+            assert sizes[1] >= 8 * 32 * 2048 * 4
+    assert B.moe_layer_workspace_size(4, 2048, 1024, 64, 9) == 0
+
+
 def test_table_create_rejects_before_touching_the_gpu(lib):
     # moe_table_create validates the descriptor and the host source's identity
     # and layout before any device call, so these run without a GPU.

@@ -31,6 +31,7 @@ MOE_SLOT_FP16 = 1
 MOE_FFN_PATH_AUTO = 0
 MOE_FFN_PATH_STREAM = 1
 MOE_FFN_PATH_GEMM = 2
+MOE_FFN_PATH_KSPLIT = 3
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -129,7 +130,7 @@ def load(path: str = LIB_PATH):
     L.moe_row_digest.restype = ctypes.c_uint64
     L.moe_row_digest.argtypes = [_vp, _sz]
     L.moe_layer_workspace_size.restype = _sz
-    L.moe_layer_workspace_size.argtypes = [_i, _i, _i]
+    L.moe_layer_workspace_size.argtypes = [_i, _i, _i, _i, _i]
     L.moe_layer_forward.restype = _i
     L.moe_layer_forward.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp,
                                     ctypes.POINTER(LayerBuffers), _i, _vp]
@@ -286,8 +287,8 @@ def pack_tile8(w):
     return out
 
 
-def moe_layer_workspace_size(T, H, E) -> int:
-    return int(load().moe_layer_workspace_size(T, H, E))
+def moe_layer_workspace_size(T, H, I, E, k) -> int:
+    return int(load().moe_layer_workspace_size(T, H, I, E, k))
 
 
 def layer_buffers(logits, topk_ids, topk_w, expert_offsets, sorted_pairs, pair_pos, active_list, n_active, h,

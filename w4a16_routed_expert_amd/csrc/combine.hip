@@ -24,6 +24,85 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *pair_out
     moe::combine_cols4(pair_out, pair_pos, topk_w, shared_out, shared_gate, T, H, k, t, c4, y);
 }
 
+// The combine over `planes` planes of partial pair outputs (the K-split
+// expert FFN of the one-call layer).  Block = (token t, 64 columns); its 256
+// threads are 16 plane groups x 16 column quads: thread (g, q) sums planes
+// g, g + 16, ... (ascending) of the token's k pairs at columns 4q .. 4q+3 of
+// the block; the 16 group sums of a pair meet in LDS in group order (the
+// pair's output, also written to sum_out); then the threads of group 0 weight
+// the k pairs in slot order, add the shared term and round, with the same
+// arithmetic as the plain combine.  Every order is fixed: the result is the
+// same on every run.
+constexpr int kPG = 16, kPQ = 16, kPThreads = kPG * kPQ;
+
+__global__ __launch_bounds__(kPThreads) void combine_planes_kernel(const float *planes_, size_t plane_stride,
+                                                                   int planes, float *sum_out, const int32_t *pair_pos,
+                                                                   const float *topk_w, const float *shared_out,
+                                                                   const float *shared_gate, int T, int H, int k,
+                                                                   uint16_t *y)
+{
+    __shared__ float4 red[kPG][MOE_MAX_TOPK][kPQ];
+    __shared__ float4 tot[MOE_MAX_TOPK][kPQ];
+    const int nb = H / 64;
+    const int t = blockIdx.x / nb;
+    const int col = (blockIdx.x % nb) * 64 + 4 * (threadIdx.x % kPQ);
+    const int g = threadIdx.x / kPQ, q = threadIdx.x % kPQ;
+    int pos[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        pos[j] = j < k ? pair_pos[(size_t)t * k + j] : -1;
+        if (pos[j] >= T * k) pos[j] = -1;        // a corrupted grouping is skipped, never read out of bounds
+    }
+    float4 v[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = g; s < planes; s += kPG) {
+        float4 u[MOE_MAX_TOPK];
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_TOPK; ++j)
+            if (pos[j] >= 0)
+                u[j] = *reinterpret_cast<const float4 *>(planes_ + s * plane_stride + (size_t)pos[j] * H + col);
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_TOPK; ++j)
+            if (pos[j] >= 0) {
+                v[j].x += u[j].x; v[j].y += u[j].y; v[j].z += u[j].z; v[j].w += u[j].w;
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) red[g][j][q] = v[j];
+    __syncthreads();
+    if (g < k) {
+        float4 o = red[0][g][q];
+        for (int gg = 1; gg < kPG; ++gg) {
+            const float4 r = red[gg][g][q];
+            o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+        }
+        tot[g][q] = o;
+        if (sum_out && pos[g] >= 0) *reinterpret_cast<float4 *>(sum_out + (size_t)pos[g] * H + col) = o;
+    }
+    __syncthreads();
+    if (g != 0) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (j < k) {
+            const float w = topk_w[(size_t)t * k + j];
+            const float4 vj = tot[j][q];
+            acc.x += w * vj.x; acc.y += w * vj.y; acc.z += w * vj.z; acc.w += w * vj.w;
+        }
+    }
+    if (shared_out) {
+        const float gs = shared_gate[t];
+        const float4 sv = *reinterpret_cast<const float4 *>(shared_out + (size_t)t * H + col);
+        acc.x += gs * sv.x; acc.y += gs * sv.y; acc.z += gs * sv.z; acc.w += gs * sv.w;
+    }
+    const _Float16 hx = (_Float16)acc.x, hy = (_Float16)acc.y, hz = (_Float16)acc.z, hw = (_Float16)acc.w;
+    uint2 packed;
+    packed.x = (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+    packed.y = (uint32_t)__builtin_bit_cast(uint16_t, hz) | ((uint32_t)__builtin_bit_cast(uint16_t, hw) << 16);
+    *reinterpret_cast<uint2 *>(y + (size_t)t * H + col) = packed;
+}
+
 // out = RN16(a + b) elementwise for FP16 a, b: the sum of two FP16 values is
 // exact in fp64, so one rounding to FP16 gives the correctly rounded result.
 __global__ __launch_bounds__(256) void residual_add_kernel(const uint16_t *a, const uint16_t *b, uint16_t *out,
@@ -47,6 +126,17 @@ extern "C" int moe_residual_add(const void *a_dev, const void *b_dev, void *out_
     hipLaunchKernelGGL(residual_add_kernel, dim3((unsigned int)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
                        (const uint16_t *)a_dev, (const uint16_t *)b_dev, (uint16_t *)out_dev, n);
     return moe::check_launch("moe_residual_add");
+}
+
+int moe::combine_planes(const float *planes, size_t plane_stride, int n_planes, float *sum_out,
+                        const int32_t *pair_pos_dev, const float *topk_w_dev, const float *shared_out_dev,
+                        const float *shared_gate_dev, int T, int H, int k, void *y_dev, hipStream_t s)
+{
+    if (T == 0) return MOE_OK;
+    hipLaunchKernelGGL(combine_planes_kernel, dim3((unsigned int)(T * (H / 64))), dim3(kPThreads), 0, s, planes,
+                       plane_stride, n_planes, sum_out, pair_pos_dev, topk_w_dev, shared_out_dev, shared_gate_dev, T,
+                       H, k, (uint16_t *)y_dev);
+    return moe::check_launch("moe_layer_forward (combine)");
 }
 
 extern "C" int moe_combine(const float *pair_out_dev, const int32_t *pair_pos_dev, const float *topk_w_dev,

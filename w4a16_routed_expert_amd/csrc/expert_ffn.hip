@@ -594,6 +594,25 @@ int launch_down(const FfnArgs &a, int mode, hipStream_t s) { return launch_ffn<f
 
 }  // namespace
 
+int moe::ffn_ksplit_width(int T, int H, int I, int E, int k) { return ffn::ksplit_width(T, H, I, E, k); }
+
+int moe::ffn_ksplit(const void *x_dev, int T, int H, int I, int E, int k, const void *rows_dev, size_t row_stride,
+                    const int32_t *slot_map_dev, const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
+                    const int32_t *active_list_dev, const int32_t *n_active_dev, void *h_dev, int32_t *status_dev,
+                    float *planes, int width, hipStream_t s)
+{
+    const char *who = "moe_layer_forward (expert FFN)";
+    if (width <= 0 || width != ffn::ksplit_width(T, H, I, E, k) || !planes || !sorted_pairs_dev || !x_dev)
+        return moe::fail(MOE_ERR_INVALID_ARG, "%s: K-split launch arguments", who);
+    FfnArgs a;
+    const int rc = make_args(a, x_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev, expert_offsets_dev,
+                             sorted_pairs_dev, active_list_dev, n_active_dev, h_dev, planes, status_dev,
+                             MOE_FFN_PATH_STREAM, who);
+    if (rc == -1) return MOE_OK;
+    if (rc) return rc;
+    return ffn::launch_ksplit(a, planes, width, s, who);
+}
+
 extern "C" {
 
 int moe_w4a16_gateup(const void *x_dev, int T, int H, int I, int E, int k,

@@ -234,20 +234,6 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// One MFMA B operand from a word of 8 codes (column 2i in the low nibble of
-// byte i) with the columns in natural order: half j is code j moved to bits
-// 4-7, the FP16 subnormal code * 2^-20, plus the zero point zp (-8 * 2^-20,
-// which makes (code - 8) * 2^-20 exactly; 0 for a padding K-tile, whose
-// operand is then exactly zero).  Byte j of lo holds code 2j in its high
-// nibble, byte j of hi code 2j + 1; one byte permute per dword places them.
-__device__ inline half8 codes_to_signed_natural(uint32_t w, half8 zp)
-{
-    const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
-    const u32x4 d = {__builtin_amdgcn_perm(hi, lo, 0x0C040C00u), __builtin_amdgcn_perm(hi, lo, 0x0C050C01u),
-                     __builtin_amdgcn_perm(hi, lo, 0x0C060C02u), __builtin_amdgcn_perm(hi, lo, 0x0C070C03u)};
-    return __builtin_bit_cast(half8, d) + zp;
-}
-
 // End of a K-tile: this wavefront's direct-to-LDS loads older than its
 // newest N vector-memory operations are complete (N counted by the caller),
 // its LDS operations too, then the block barrier.  Written as one asm

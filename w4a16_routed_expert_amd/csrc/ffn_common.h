@@ -94,6 +94,20 @@ __device__ inline u32x4 permute_activations(u32x4 d)
     return u32x4{hi2(d[0], d[2]), lo2(d[0], d[2]), hi2(d[1], d[3]), lo2(d[1], d[3])};
 }
 
+// One MFMA operand from a word of 8 codes (column 2i in the low nibble of
+// byte i) with the columns in natural order: half j is code j moved to bits
+// 4-7, the FP16 subnormal code * 2^-20, plus the zero point zp (-8 * 2^-20,
+// which makes (code - 8) * 2^-20 exactly; 0 for a padding K-tile, whose
+// operand is then exactly zero).  Byte j of lo holds code 2j in its high
+// nibble, byte j of hi code 2j + 1; one byte permute per dword places them.
+__device__ inline half8 codes_to_signed_natural(uint32_t w, half8 zp)
+{
+    const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+    const u32x4 d = {__builtin_amdgcn_perm(hi, lo, 0x0C040C00u), __builtin_amdgcn_perm(hi, lo, 0x0C050C01u),
+                     __builtin_amdgcn_perm(hi, lo, 0x0C060C02u), __builtin_amdgcn_perm(hi, lo, 0x0C070C03u)};
+    return __builtin_bit_cast(half8, d) + zp;
+}
+
 // Per-block table of the active slots, built once in LDS: expert, first
 // grouped pair, pair count, device slot and the first work item of the slot.
 struct SlotTable {
@@ -168,5 +182,11 @@ int cu_count();
 // Grouped-GEMM launches for large batches (expert_gemm.hip).
 int launch_gemm_gateup(const FfnArgs &a, hipStream_t s);
 int launch_gemm_down(const FfnArgs &a, hipStream_t s);
+
+// The K-split FFN of batches of at most 16 tokens (ffn_ksplit.hip): slice
+// width W (0: not applicable to the shape), and the launch writing h and the
+// I/W planes of partial pair outputs [I/W][T*k][H] (FP32).
+int ksplit_width(int T, int H, int I, int E, int k);
+int launch_ksplit(const FfnArgs &a, float *planes, int W, hipStream_t s, const char *who);
 
 }  // namespace ffn

@@ -124,6 +124,7 @@ __device__ inline void combine_cols4(const float *pair_out, const int32_t *pair_
         if (pos[j] >= 0 && pos[j] < T * k)       // a corrupted grouping is skipped, never read out of bounds
             v[j] = *reinterpret_cast<const float4 *>(pair_out + (size_t)pos[j] * H + c4 * 4);
     }
+
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
@@ -177,5 +178,21 @@ int route_fused(const void *x_dev, const void *w_router_dev, const float *bias_d
                 int32_t *sorted_pairs_dev, int32_t *pair_pos_dev, int32_t *active_list_dev, int32_t *n_active_dev,
                 float *lbuf, unsigned int *done, hipStream_t s);
 size_t route_logits_bytes(int T, int E);
+
+// combine.hip: the combine over n_planes planes of partial pair outputs
+// (plane stride in floats), writing each pair's plane sum to sum_out.
+int combine_planes(const float *planes, size_t plane_stride, int n_planes, float *sum_out,
+                   const int32_t *pair_pos_dev, const float *topk_w_dev, const float *shared_out_dev,
+                   const float *shared_gate_dev, int T, int H, int k, void *y_dev, hipStream_t s);
+
+// expert_ffn.hip: the K-split expert FFN of the one-call layer (batches of at
+// most 16 tokens): its slice width for a shape (0 = not applicable), and the
+// launch, which writes h and the I / width planes of partial pair outputs
+// [I/width][T*k][H] (FP32).
+int ffn_ksplit_width(int T, int H, int I, int E, int k);
+int ffn_ksplit(const void *x_dev, int T, int H, int I, int E, int k, const void *rows_dev, size_t row_stride,
+               const int32_t *slot_map_dev, const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
+               const int32_t *active_list_dev, const int32_t *n_active_dev, void *h_dev, int32_t *status_dev,
+               float *planes, int width, hipStream_t s);
 
 }  // namespace moe

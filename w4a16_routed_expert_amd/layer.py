@@ -56,7 +56,7 @@ class RoutedExpertLayer:
         self._act_host = torch.empty(E + 1, dtype=torch.int32, pin_memory=True)
         self._act_evt = torch.cuda.Event()
         # workspace of the one-call layer: zero-filled once, left zero by every call
-        self.layer_ws = torch.zeros(max(B.moe_layer_workspace_size(T, H, E), 256), dtype=torch.uint8, device=d)
+        self.layer_ws = torch.zeros(max(B.moe_layer_workspace_size(T, H, I, E, k), 256), dtype=torch.uint8, device=d)
         self._bufs = B.layer_buffers(self.logits, self.topk_ids, self.topk_w, self.expert_offsets, self.sorted_pairs,
                                      self.pair_pos, self.active_list, self.n_active, self.h, self.pair_out,
                                      self.status, self.layer_ws, self.layer_ws.numel())
@@ -136,8 +136,9 @@ class RoutedExpertLayer:
 
     def forward_fused(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None, rows=None, lease=None,
                       shared: "SharedExpert | None" = None, mode: int = B.MOE_FFN_PATH_AUTO) -> torch.Tensor:
-        """y = layer(x) through the one-call layer (moe_layer_forward: four launches for decode
-        batches, no host round trip).  rows/lease as for ffn().  With a SharedExpert its FFN runs
+        """y = layer(x) through the one-call layer (moe_layer_forward: three or four launches for
+        decode batches, no host round trip; mode B.MOE_FFN_PATH_KSPLIT forces the one-launch expert
+        FFN of small batches).  rows/lease as for ffn().  With a SharedExpert its FFN runs
         on a second stream beside the routed work and the combine waits for its event."""
         T = x.shape[0]
         if T > self.max_T:
