@@ -221,6 +221,36 @@ def test_partial_residency_output_equals_full_residency(name, capacity, spare, T
     tab.close()
 
 
+def test_table_forward_on_a_stream_that_is_not_current():
+    # forward(table=..., stream=s) with s not torch's current stream: the
+    # active-expert list is read back after the routing on s (not on the
+    # current stream), the misses are uploaded before the FFN on s reads
+    # them, and the output equals full residency; the status word stays clear.
+    from w4a16_routed_expert_amd.layer import RoutedExpertLayer
+    cfg = synth.CONFIGS["olmoe_stack"]
+    T = 8
+    rows = synth.make_expert_rows(cfg, layer=3)
+    wr = synth.make_router(cfg, layer=3)
+    bias = synth.make_zipf_bias(cfg, layer=3)
+    xs = [synth.make_x(cfg, T, step=s, layer=3) for s in range(3)]
+    full = run_layer(cfg, rows, wr, xs, bias)
+    dev = torch.device("cuda:0")
+    tab = make_table(cfg, rows, cfg.resident, min(cfg.E - cfg.resident, T * cfg.k), max_tokens=T)
+    lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev),
+                            torch.from_numpy(wr).to(dev), torch.from_numpy(bias).to(dev), max_T=T, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    for s, x in enumerate(xs):
+        xd = torch.from_numpy(x).to(dev)
+        side.wait_stream(torch.cuda.current_stream())   # x was copied on the current stream
+        y = lay.forward(xd, stream=side, table=tab)
+        side.synchronize()
+        lay.check_status(side)
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), full[s]), f"step {s}"
+    st = tab.stats()
+    assert st["misses"] > 0 and st["open_leases"] == 0
+    tab.close()
+
+
 @pytest.mark.parametrize("T", [1, 32])
 def test_olmoe_stack_two_layers_partial_residency_vs_oracle(T):
     # Two consecutive layers of the OLMoE-shaped stack (own weights, router and
