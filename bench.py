@@ -86,6 +86,9 @@ def parse():
     ap.add_argument("--prefetch", action="store_true",
                     help="olmoe_stack: load each next layer's predicted experts while the current layer computes")
     ap.add_argument("--staging", type=int, default=2, help="pinned staging rows per table (stack and partial)")
+    ap.add_argument("--pinned-source", action="store_true",
+                    help="stack and partial: keep the host source page-locked (misses copied directly, no "
+                         "staging); the default is a pageable source")
     ap.add_argument("--fp16-slots", action="store_true",
                     help="offload-qpacked profile: experts in FP16 execution slots (dequantized on the GPU).  With "
                          "olmoe/qwen: the decode layer's expert FFN over qpacked rows and over FP16 slots, side by "
@@ -759,7 +762,7 @@ def run_stack(args, torch, dev):
             shared.append(SharedExpert(*(torch.from_numpy(np.ascontiguousarray(m)).to(dev)
                                          for m in synth.make_shared(cfg, layer=l)), max_T=T, device=dev))
         tab = ResidentExpertTable(host[l], H, I, cfg.resident, spare, staging_rows=args.staging, top_k=k,
-                                  max_tokens=T, fp16_slots=args.fp16_slots)
+                                  max_tokens=T, fp16_slots=args.fp16_slots, pinned_source=args.pinned_source)
         rows_dev, stride, _ = tab.device()
         lay = RoutedExpertLayer(H, I, E, k, torch.empty((1, stride), dtype=torch.uint8, device=dev), wr, bias,
                                 max_T=T, device=dev)
@@ -815,7 +818,9 @@ def run_stack(args, torch, dev):
         "config": {"workload": (f"olmoe_stack{L}" if args.config == "olmoe_stack" else f"{args.config}_decode_layer")
                                + f"_T{T}_resident{cfg.resident}of{E}" + ("_prefetch" if args.prefetch else ""),
                    "layers": L, "tokens": T, "experts": E, "top_k": k, "hidden": H, "intermediate": I,
-                   "resident": cfg.resident, "spare_rows": spare, "staging_rows": args.staging, "zipf_s": cfg.zipf_s,
+                   "resident": cfg.resident, "spare_rows": spare, "staging_rows": args.staging,
+                   "host_source": "page-locked (direct copies)" if args.pinned_source else "pageable (staged)",
+                   "zipf_s": cfg.zipf_s,
                    "shared_expert_intermediate": Is, "input_batches": S,
                    "chain": "residual stream x_{l+1} = RN16(x_l + y_l)" if L > 1 else None,
                    "prefetch": "next layer's router on x_l, loaded while layer l computes" if args.prefetch else None,
@@ -830,6 +835,7 @@ def run_stack(args, torch, dev):
             "prefetch_hits_per_step": delta["prefetch_hits"] / K,
             "prefetch_unused_per_step": delta["prefetch_unused"] / K,
             "staging_waits": delta["staging_waits"],
+            "direct_copies_per_step": delta["direct_copies"] / K,
             "expert_d2h_bytes": delta["expert_d2h_bytes"], "host_writes": delta["host_writes"],
             "pinned_h2d_ceiling_gbs": h2d_ceiling,
             "h2d_frac_of_pinned_ceiling": delta["h2d_bytes"] / elapsed / 1e9 / h2d_ceiling,

@@ -305,6 +305,10 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
  * 0009"):
  *   - the host source holds every expert's qpacked row; it belongs to the
  *     caller, must stay unchanged and outlive the table, and is only read.
+ *     When the whole source is page-locked host memory (hipHostMalloc, a
+ *     pinned torch tensor), misses are copied straight from it and the
+ *     staging buffers are not used (counter direct_copies); pageable sources
+ *     go through the staging buffers as below.
  *     Creation takes a 64-bit digest of every row (its identity; compared
  *     with desc->row_digests when given) and checks that every FP16 scale is
  *     finite (its layout); moe_table_verify_source re-checks the digests;
@@ -382,6 +386,7 @@ typedef struct {
     uint64_t prefetched;               /* rows uploaded by moe_table_prefetch */
     uint64_t prefetch_hits;            /* prefetched experts that a later step routed */
     uint64_t prefetch_unused;          /* prefetched experts evicted before any step routed them */
+    uint64_t direct_copies;            /* rows copied straight from a page-locked host source (no staging) */
 } moe_table_counters;
 
 typedef struct {

@@ -112,6 +112,7 @@ class SimTransport final : public tcore::Transport {
 public:
     // the n-th call (1-based) of a kind fails; 0 = never
     int fail_h2d_at = 0, fail_publish_at = 0, fail_wait_at = 0, fail_record_at = 0, fail_pinned_at = 0;
+    bool pinned_source = false;          // host_pinned() answer: the source is page-locked
     int n_h2d = 0, n_publish = 0, n_wait = 0, n_record = 0, n_pinned = 0;
     std::vector<std::unique_ptr<SimStream>> streams;
     std::vector<std::unique_ptr<SimEvent>> events;
@@ -129,6 +130,7 @@ public:
         return alloc(p, n);
     }
     void free_pinned(void *p) override { release(p); }
+    bool host_pinned(const void *, size_t) override { return pinned_source; }
     int create_event(void **ev) override
     {
         events.emplace_back(new SimEvent);
@@ -526,6 +528,41 @@ void scenario_staging_reuse()
     delete t;
 }
 
+void scenario_direct_from_pinned_source()
+{
+    // A page-locked source: no staging buffer is allocated, every miss is one
+    // copy straight from the source; random steps with lazy consumers still
+    // see intact rows of their generation.
+    const Source src({16, 256, 512}, 11);
+    SimTransport tr;
+    tr.pinned_source = true;
+    moe_table_desc d = desc_of(src, 5, tcore::spare_needed(16, 5, 2, 2), 2, 2, 2);
+    tcore::Table *t = nullptr;
+    CHECK(tcore::Table::create(&tr, &d, &t) == MOE_OK, "create");
+    if (!t) return;
+    CHECK(tr.n_pinned == 0, "staging allocated: %d pinned buffers", tr.n_pinned);
+    Stepper st{tr, *t, src, tr.new_stream()};
+    std::mt19937 rng(17);
+    const int h2d_before = tr.n_h2d;
+    for (int s = 0; s < 100; ++s) {
+        const int n = 1 + (int)(rng() % 4u);
+        const bool consumer_first = rng() & 1;
+        const int rc = st.step(random_active(rng, 16, n, s & 1), consumer_first);
+        CHECK(rc == MOE_OK, "step %d rc %d", s, rc);
+        if (rc) break;
+        if (!consumer_first) tr.stream_sync(tr.streams[0].get());
+    }
+    tr.run_all();
+    CHECK(st.bad_reads == 0, "%d bad reads of %d", st.bad_reads, st.reads);
+    moe_table_counters k;
+    t->stats(&k);
+    CHECK(k.direct_copies == k.misses && k.misses > 0, "direct copies %llu of %llu misses",
+          (unsigned long long)k.direct_copies, (unsigned long long)k.misses);
+    CHECK((uint64_t)(tr.n_h2d - h2d_before) == k.misses, "one copy per miss");
+    CHECK(k.staging_waits == 0, "staging waits");
+    delete t;
+}
+
 void scenario_open_lease_holds_rows()
 {
     // A lease that is never released keeps the rows its generation names
@@ -722,6 +759,7 @@ int main(int argc, char **argv)
         {"default_stream", scenario_default_stream_consumer},
         {"prefetch", scenario_prefetch},
         {"staging", scenario_staging_reuse},
+        {"direct", scenario_direct_from_pinned_source},
         {"lease", scenario_open_lease_holds_rows},
         {"fail_before", scenario_failure_before_publication},
         {"fail_after", scenario_failure_after_publication},

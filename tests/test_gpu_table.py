@@ -221,6 +221,27 @@ def test_partial_residency_output_equals_full_residency(name, capacity, spare, T
     tab.close()
 
 
+def test_page_locked_source_is_copied_directly():
+    # A pinned host source: misses go straight from it to the device (no
+    # staging); the output equals full residency and every miss is a direct copy.
+    cfg = synth.CONFIGS["olmoe_stack"]
+    T = 8
+    rows = synth.make_expert_rows(cfg, layer=4)
+    wr = synth.make_router(cfg, layer=4)
+    bias = synth.make_zipf_bias(cfg, layer=4)
+    xs = [synth.make_x(cfg, T, step=s, layer=4) for s in range(3)]
+    full = run_layer(cfg, rows, wr, xs, bias)
+    from w4a16_routed_expert_amd.layer import ResidentExpertTable
+    tab = ResidentExpertTable(rows, cfg.H, cfg.I, cfg.resident, min(cfg.E - cfg.resident, T * cfg.k),
+                              top_k=cfg.k, max_tokens=T, pinned_source=True)
+    part = run_layer(cfg, rows, wr, xs, bias, table=tab)
+    for s, (a, b) in enumerate(zip(full, part)):
+        assert np.array_equal(a, b), f"step {s}: pinned-source table differs from full residency"
+    st = tab.stats()
+    assert st["misses"] > 0 and st["direct_copies"] == st["misses"] and st["staging_waits"] == 0
+    tab.close()
+
+
 def test_table_forward_on_a_stream_that_is_not_current():
     # forward(table=..., stream=s) with s not torch's current stream: the
     # active-expert list is read back after the routing on s (not on the

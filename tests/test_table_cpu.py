@@ -43,8 +43,8 @@ def run(exe, scenario, env_extra):
 def test_table_state_machine_asan_ubsan(tmp_path):
     exe = build(tmp_path, "table_sim_asan", ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"])
     out = run(exe, "all", {"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0", "UBSAN_OPTIONS": "print_stacktrace=1"})
-    for name in ("steps", "default_stream", "prefetch", "staging", "lease", "fail_before", "fail_after", "create",
-                 "threads"):
+    for name in ("steps", "default_stream", "prefetch", "staging", "direct", "lease", "fail_before", "fail_after",
+                 "create", "threads"):
         assert f"{name}: ok" in out
 
 

@@ -67,7 +67,7 @@ class TableCounters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("steps", "hits", "misses", "evictions", "h2d_bytes", "staging_waits",
                                                "expert_d2h_bytes", "host_writes", "generation", "open_leases",
                                                "failed_uploads", "prefetched", "prefetch_hits",
-                                               "prefetch_unused")]
+                                               "prefetch_unused", "direct_copies")]
 
 
 class TableLease(ctypes.Structure):

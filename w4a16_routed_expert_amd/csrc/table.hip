@@ -75,6 +75,22 @@ public:
         return note(hipGetLastError());
     }
     const char *message() override { return msg_; }
+    // Page-locked host memory (hipHostMalloc, pinned torch tensors) reports
+    // hipMemoryTypeHost; pageable memory is unregistered (or an error, which
+    // is cleared so the next launch check does not see it).
+    bool host_pinned(const void *p, size_t n) override
+    {
+        if (!p || n == 0) return false;
+        auto pinned = [](const void *q) {
+            hipPointerAttribute_t a{};
+            if (hipPointerGetAttributes(&a, q) != hipSuccess) {
+                (void)hipGetLastError();
+                return false;
+            }
+            return a.type == hipMemoryTypeHost;
+        };
+        return pinned(p) && pinned(static_cast<const uint8_t *>(p) + n - 1);
+    }
     // FP16 execution slots: the qpacked row goes to a device staging row, then
     // is dequantized into the slot (same stream, so the staging row is free
     // again for the next row)

@@ -77,6 +77,8 @@ struct Transport {
     // asynchronously on s: a copy, or for FP16 execution slots a copy and a
     // dequantization into the slot
     virtual int row_upload(void *dst, const void *src, size_t n, void *s) { return h2d_async(dst, src, n, s); }
+    // True when [p, p + n) is page-locked host memory the copy engine can read directly.
+    virtual bool host_pinned(const void *p, size_t n) { (void)p; (void)n; return false; }
     virtual const char *message() = 0;
 };
 
@@ -600,7 +602,9 @@ private:
         if (tr_->alloc_device(&rows_, (size_t)nslots_ * row_stride_) != 0) return hip_fail("device rows");
         if (tr_->alloc_device(reinterpret_cast<void **>(&maps_), sizeof(int32_t) * (size_t)E_ * kMaps) != 0)
             return hip_fail("device maps");
-        for (int i = 0; i < d->staging_rows; ++i) {
+        // a page-locked source is read by the copy engine directly: no staging
+        direct_ = tr_->host_pinned(host_, (size_t)(E_ - 1) * host_stride_ + row_bytes_);
+        for (int i = 0; i < (direct_ ? 0 : d->staging_rows); ++i) {
             void *p = nullptr, *ev = nullptr;
             if (tr_->alloc_pinned(&p, row_bytes_) != 0) return hip_fail("pinned staging");
             staging_.push_back(static_cast<uint8_t *>(p));
@@ -727,6 +731,15 @@ private:
     // Host row of expert e -> staging -> device row `slot`, on the copy stream.
     int copy_row(int e, int slot)
     {
+        if (direct_) {
+            // straight from the page-locked source (unchanged for the table's lifetime)
+            if (tr_->row_upload(static_cast<uint8_t *>(rows_) + (size_t)slot * row_stride_, host_ + (size_t)e * host_stride_,
+                                row_bytes_, copy_) != 0)
+                return fail(MOE_ERR_HIP, "moe_upload_expert_rows (copy): %s", tr_->message());
+            ctr_.h2d_bytes += row_bytes_;
+            ctr_.direct_copies++;
+            return MOE_OK;
+        }
         const size_t i = next_staging_;
         next_staging_ = (i + 1) % staging_.size();
         if (staging_used_[i]) {
@@ -761,6 +774,7 @@ private:
     const uint8_t *host_ = nullptr;
     std::vector<uint64_t> digests_;
     void *copy_ = nullptr;
+    bool direct_ = false;                    // the host source is page-locked: no staging
     void *rows_ = nullptr;
     int32_t *maps_ = nullptr;                // [kMaps][E]
     std::vector<int32_t> slot_of_;           // published map of generation gen_ (host mirror)

@@ -262,13 +262,20 @@ class ResidentExpertTable:
     host_rows: uint8 numpy array [E, stride] holding every expert's row; kept referenced (and
     never written) for the table's lifetime.  capacity experts stay published between steps;
     spare_rows device rows receive misses (at least what steps of max_tokens tokens with top_k
-    experts need; moe_table_create checks it).
+    experts need; moe_table_create checks it).  pinned_source: keep the source in page-locked
+    host memory (a pinned copy made here), which the table copies misses from directly instead
+    of through its staging buffers.
     """
 
     def __init__(self, host_rows, H: int, I: int, capacity: int, spare_rows: int, staging_rows: int = 2,
                  initial_resident=None, top_k: int = 1, max_tokens: int = 1, row_digests=None,
-                 fp16_slots: bool = False):
+                 fp16_slots: bool = False, pinned_source: bool = False):
         import numpy as np
+        self._pinned = None
+        if pinned_source:
+            self._pinned = torch.empty(host_rows.shape, dtype=torch.uint8, pin_memory=True)
+            self._pinned.numpy()[...] = host_rows
+            host_rows = self._pinned.numpy()
         self.host_rows = np.ascontiguousarray(host_rows)
         self.E = self.host_rows.shape[0]
         self.fp16_slots = fp16_slots
