@@ -559,6 +559,10 @@ void scenario_direct_from_pinned_source()
     CHECK(k.direct_copies == k.misses && k.misses > 0, "direct copies %llu of %llu misses",
           (unsigned long long)k.direct_copies, (unsigned long long)k.misses);
     CHECK((uint64_t)(tr.n_h2d - h2d_before) == k.misses, "one copy per miss");
+    int copies[2] = {0, 0};
+    for (int i = 0; i < 2; ++i)
+        for (const Op &op : tr.streams[i]->ops) copies[i] += op.kind == Op::COPY;
+    CHECK(copies[0] > 0 && copies[1] > 0, "copies on the two copy streams: %d, %d", copies[0], copies[1]);
     CHECK(k.staging_waits == 0, "staging waits");
     delete t;
 }
@@ -602,10 +606,12 @@ void scenario_failure_before_publication()
 {
     // A copy fails in the middle of a transaction: the previous generation
     // stays current and intact, the table is not faulted, the next
-    // transaction succeeds.
+    // transaction succeeds.  Cases 3-6 copy from a page-locked source over
+    // two copy streams (no staging records; the first record joins them).
     const Source src({8, 256, 512}, 4);
-    for (int which = 0; which < 3; ++which) {
+    for (int which = 0; which < 7; ++which) {
         SimTransport tr;
+        tr.pinned_source = which >= 3;
         moe_table_desc d = desc_of(src, 3, 5, 2, 2, 2);
         tcore::Table *t = nullptr;
         CHECK(tcore::Table::create(&tr, &d, &t) == MOE_OK, "create");
@@ -618,12 +624,22 @@ void scenario_failure_before_publication()
         if (which == 0) tr.fail_h2d_at = tr.n_h2d + 2;          // second copy of the transaction
         if (which == 1) tr.fail_publish_at = tr.n_publish + 1;  // the map write
         if (which == 2) tr.fail_record_at = tr.n_record + 4;    // the publication event (after 3 staging records)
+        if (which == 3) tr.fail_h2d_at = tr.n_h2d + 3;          // third copy (the second is in flight on stream 2)
+        if (which == 4) tr.fail_record_at = tr.n_record + 1;    // joining the copy streams
+        if (which == 5) tr.fail_publish_at = tr.n_publish + 1;
+        if (which == 6) tr.fail_record_at = tr.n_record + 2;    // the publication event
         std::vector<int32_t> act = {4, 5, 6}, miss(3);
         int nm = 0;
         t->misses(act.data(), 3, miss.data(), &nm);
         const int rc = t->upload(miss.data(), nm, c);
         CHECK(rc == MOE_ERR_HIP, "case %d: rc %d", which, rc);
         CHECK(!t->faulted(), "case %d: faulted", which);
+        // two copy streams: the failed transaction's copies are drained before
+        // the call returns (the retry may write its rows on the other stream)
+        if (tr.pinned_source)
+            for (int i = 0; i < 2; ++i)
+                CHECK(tr.streams[i]->next == tr.streams[i]->ops.size(), "case %d: copy stream %d not drained", which,
+                      i);
         int32_t after[64];
         t->published(after);
         CHECK(std::memcmp(before, after, sizeof(int32_t) * 8) == 0, "case %d: map changed", which);
