@@ -20,12 +20,18 @@
 //     first MFMA operand, so a lane of the result holds one pair and 4
 //     consecutive output rows per register quad: gate and up of an output
 //     meet in the same lane, and the outputs leave as 8- and 16-byte stores.
-//   * Staging with direct global-to-LDS loads (no registers, no VALU): per
-//     K-tile (128 columns) the item's 128 activation rows (gathered through
-//     sorted_pairs for gate/up), each wavefront's two 1 KB weight tiles and
-//     its 32 row scales, in a ring of 3 K-tiles loaded two K-tiles ahead.
-//     One barrier per K-tile, preceded by a wait that counts the loads
-//     issued since (so the newer K-tile's loads stay in flight).
+//   * Activations staged with direct global-to-LDS loads (no registers, no
+//     VALU): the item's 128 activation rows (gathered through sorted_pairs
+//     for gate/up) per K-tile of 128 columns, two K-tiles (one scale block)
+//     at a time with each wavefront's 32 row scales of that block, in a ring
+//     of two such pairs: each K-tile of a pair stages its counterpart of the
+//     next pair (the second also the scales), and one barrier per pair,
+//     preceded by a wait that counts the loads issued since, publishes it
+//     (one barrier per K-tile, or the whole next pair staged by the first
+//     K-tile, measured slower).  Each wavefront's weights are its
+//     own: they go straight into registers (two 16-byte loads per lane per
+//     K-tile, issued one K-tile ahead) - staging them through LDS as well
+//     was measured 3% slower.
 //     Activation layout: 64-byte granules, granule (row / 4, piece ^ (row / 4
 //     % 4)) holds the 16-byte piece of 4 consecutive rows, so one direct load
 //     instruction fills a whole 1 KB granule run and the MFMA operand reads
@@ -59,7 +65,7 @@ constexpr int kGWaves = 8;
 constexpr int kGThreads = 64 * kGWaves;
 constexpr int kBM = 128;              // grouped pairs per item
 constexpr int kStageBytes = kBM * 256;  // one staged K-tile
-constexpr int kStages = 3;            // staged K-tiles
+constexpr int kStages = 4;            // staged K-tiles: two pairs
 constexpr int kMT = 4;                // m-tiles (32 pairs) per wavefront: all 128 pairs of the item
 constexpr int kPD = 4;                // operand reads in flight ahead of the MFMAs
 // Buffer offset of a row (or lane) that reads nothing: past every resource
@@ -68,9 +74,8 @@ constexpr int kPD = 4;                // operand reads in flight ahead of the MF
 constexpr uint32_t kNone = 0x40000000u;
 
 struct GLds {
-    uint8_t xa[kStages][kStageBytes];    // staged activations (layout: see stage_addr)
-    uint8_t wt[kStages][kGWaves][2048];  // each wavefront's two weight tiles of a K-tile
-    uint8_t sc[kStages][kGWaves][256];   // each wavefront's 32 row scales of the K-tile's scale block (64 bytes used)
+    uint8_t xa[kStages][kStageBytes];    // staged activations (layout: see stage_addr); pair slot q: stages 2q, 2q + 1
+    uint8_t sc[2][kGWaves][256];         // each wavefront's 32 row scales of a pair's scale block (64 bytes used)
     uint32_t src[2][kBM];                // byte offset of each pair's activation row (kNone: none), two items
     SlotTable tb;
 };
@@ -104,7 +109,6 @@ struct Gemm {
     int nact;
     int lane, wave, j32, h2;
     int K, NT, NTP, NBK, RG, NBLK;
-    int wrd;                             // this lane's chunk 0 in a wavefront's weight stage
     int aq[4];                           // stage_addr of this lane's operand pieces, m-tile 0, K-steps q (+ 4n)
 
     __device__ Gemm(const FfnArgs &args, GLds &lds, int nact_) : a(args), L(lds), nact(nact_)
@@ -120,10 +124,6 @@ struct Gemm {
         NBK = (NT + 1) / 2;
         RG = (GATEUP ? a.I : a.H) / 16;
         NBLK = (RG + RGB - 1) / RGB;
-        // selected from uniform values: indexing the argument arrays with the
-        // per-lane matrix would read them with vector loads
-        // tile j32 / 16, row j32 % 16, columns 32 h2 .. +31 (chunk 1: 64 further on)
-        wrd = 1024 * (j32 >> 4) + (16 * h2 + (j32 & 15)) * 16;
         for (int q = 0; q < 4; ++q) aq[q] = stage_addr(j32, 4 * h2 + q);
     }
 
@@ -198,7 +198,7 @@ struct Gemm {
         if (threadIdx.x < kBM) L.src[par][threadIdx.x] = o;
     }
 
-    // Byte offset in the weight stage of tile t (0, 1) of this wavefront for
+    // Byte offset in the expert row of tile t (0, 1) of this wavefront for
     // K-tile kt: the qpacked tile of row group rg0 + wave (gate/up: t = the
     // matrix) or rg0 + 2 wave + t (down); kNone for a K-tile or row group
     // that does not exist.
@@ -207,6 +207,16 @@ struct Gemm {
         const int rg = it.rg0 + (GATEUP ? wave : 2 * wave + t);
         const int sec = GATEUP ? (t ? a.off_q[1] : a.off_q[0]) : a.off_q[2];
         return (kt < NT && rg < RG) ? (uint32_t)(sec + (rg * NT + kt) * 1024) : kNone;
+    }
+
+    // Byte offset of this lane's first 16-byte piece of the wavefront's
+    // weights of K-tile kt (the second is 512 bytes on): tile j32 / 16 of its
+    // two, piece 16 h2 + j32 % 16 (row j32 % 16, columns 32 h2 .. +31 of the
+    // tile's first chunk; the second piece: of its second chunk); past the
+    // row (zeros) when nothing is read.
+    __device__ uint32_t wpiece_off(const GItem &it, int kt) const
+    {
+        return wtile_off(it, kt, j32 >> 4) + 16 * (16 * h2 + (j32 & 15));
     }
 
     // Byte offset, for lane l < 16, of 4 bytes of the wavefront's row scales
@@ -303,84 +313,105 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
         acc[mt] = f32x16{};
         P[mt] = acc[mt];
     }
-    // K-tile kt of item `it` (row offsets in L.src[par]) loaded straight
-    // into stage st: one instruction per row quad g = wave + 8 j fills the
-    // 1 KB granule run of rows 4g .. 4g+3, lane l taking row 4g + l % 4,
-    // piece (l / 4) ^ (g % 4), which lands at stage_addr of that row and
-    // piece.  A row that reads nothing has offset kNone, which stays out of
-    // range with the column added (the lane stores zeros or nothing; such
-    // rows only feed outputs that are never written).
-    // The wavefront's two weight tiles go to its own part of the weight
-    // stage, lane l taking bytes 16 l .. 16 l + 15 of each.
-    auto dma = [&](const GItem &it, int par, int kt, int st) {
-        const __amdgpu_buffer_rsrc_t r = f.src_rsrc(it, kt);
+    // K-tile 2 pr + H of item `it` (row offsets in L.src[par]) loaded
+    // straight into stage 2 q + H: one instruction per row quad g = wave +
+    // 8 j fills the 1 KB granule run of rows 4g .. 4g+3, lane l taking row
+    // 4g + l % 4, piece (l / 4) ^ (g % 4), which lands at stage_addr of that
+    // row and piece.  A row that reads nothing has offset kNone, which stays
+    // out of range with the column added (the lane stores zeros or nothing;
+    // such rows only feed outputs that are never written).  With H = 1 also
+    // the wavefront's row scales of scale block pr.  Four (H = 0) or five
+    // vector-memory operations per wavefront.
+    auto stage_half = [&](auto h_c, const GItem &it, int par, int pr, int q) {
+        constexpr int H = decltype(h_c)::value;
+        const int kt = 2 * pr + H;
         // the four row offsets first, so their LDS reads overlap
         uint32_t so[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) so[j] = L.src[par][4 * (f.wave + 8 * j) + (f.lane & 3)];
+        const __amdgpu_buffer_rsrc_t r = f.src_rsrc(it, kt);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int g = f.wave + 8 * j;
             const uint32_t off = so[j] + kt * 256 + 16 * ((f.lane >> 2) ^ (g & 3));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&L.xa[st][1024 * g], 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&L.xa[2 * q + H][1024 * g], 16,
                                                      off, 0, 0, 0);
         }
-        const __amdgpu_buffer_rsrc_t rw = rsrc(it.row, it.nrec);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint32_t woff = f.wtile_off(it, kt, t) + 16 * f.lane;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)&L.wt[st][f.wave][1024 * t],
-                                                     16, woff, 0, 0, 0);
+        if constexpr (H == 1) {
+            const __amdgpu_buffer_rsrc_t rw = rsrc(it.row, it.nrec);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)&L.sc[q][f.wave][0], 4,
+                                                     f.scale_off(it, pr), 0, 0, 0);
         }
-        // the row scales of the K-tile's scale block (both K-tiles of a
-        // block load them; the merge reads those of the second)
-        const uint32_t soff = f.scale_off(it, kt >> 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)&L.sc[st][f.wave][0], 4, soff,
-                                                 0, 0, 0);
+    };
+    // This lane's weights of K-tile kt of item `it`: two 16-byte loads into
+    // registers (zeros past the row).
+    struct WTile {
+        u32x4 v[2];
+    };
+    auto wload = [&](const GItem &it, int kt) {
+        const __amdgpu_buffer_rsrc_t rw = rsrc(it.row, it.nrec);
+        const uint32_t o = f.wpiece_off(it, kt);
+        WTile t;
+        t.v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, 0));
+        t.v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o + 512, 0, 0));
+        return t;
     };
 
+    WTile wA, wB;                          // weights of the pair's first and second K-tile
     __syncthreads();
-    dma(cur, 0, 0, 0);
-    dma(cur, 0, 1, 1);
+    wA = wload(cur, 0);
+    stage_half(std::integral_constant<int, 0>{}, cur, 0, 0, 0);
+    stage_half(std::integral_constant<int, 1>{}, cur, 0, 0, 0);
     stage_barrier<0>();
 
     const int total = nk * NTP;
-    int kt = 0;
+    const int NPR = NTP / 2;               // pairs (scale blocks) per item
+    int pr = 0;                            // pair of the current item
     for (int g = 0; g < total; g += 2) {
+        const int rq = (g >> 1) & 1;       // ring slot of this pair
         static_for<0, 2>([&](auto slot_c) {
             constexpr int SLOT = decltype(slot_c)::value;
-            const int gg = g + SLOT;
-            // K-tile two ahead: staged and its weights loaded during this one
-            const bool anx = kt + 2 >= NTP;
-            const int akt = anx ? kt + 2 - NTP : kt + 2;
-            const GItem &ait = anx ? nxt : cur;
+            const int kt = 2 * pr + SLOT;
             // 32 steps (K-step s of 16 columns, m-tile mt), one MFMA each;
             // the operand reads from LDS run kPD steps ahead of their use.
             // K-step s uses word s % 4 of chunk s / 4: lanes h2 = 0 take
             // piece 8 (s / 4) + s % 4, lanes h2 = 1 the piece 4 further on.
-            const uint8_t *xs = &L.xa[gg % kStages][0];
+            const uint8_t *xs = &L.xa[2 * rq + SLOT][0];
             // stage_addr(32 mt + j32, 8 (s / 4) + 4 h2 + s % 4) = aq[s % 4] + 8192 mt + 512 (s / 4)
             auto rd = [&](int st) {
                 const int s = st >> 2, mt = st & 3;
                 return *reinterpret_cast<const half8 *>(xs + f.aq[s & 3] + 8192 * mt + 512 * (s >> 2));
             };
-            const uint8_t *wsrc = &L.wt[gg % kStages][f.wave][f.wrd];
-            // The first operand reads go out before the staging loads of the
-            // K-tile two ahead (a different stage), so their latency overlaps
-            // the address arithmetic of those loads.
+            // The first operand reads go out before the loads below, so their
+            // latency overlaps the address arithmetic of those loads.
             half8 xr[kPD + 1];
 #pragma unroll
             for (int st = 0; st < kPD; ++st) xr[st] = rd(st);
-            u32x4 wq[2];
-            wq[0] = *reinterpret_cast<const u32x4 *>(wsrc);
-            __builtin_amdgcn_sched_barrier(0);
-            dma(ait, (ci + anx) & 1, akt, (gg + 2) % kStages);
-            // the direct-to-LDS loads are the K-tile's only vector-memory
-            // operations before its end (the count there relies on it)
-            __builtin_amdgcn_sched_barrier(0);
+            const WTile wq = SLOT == 0 ? wA : wB;
+            // The vector-memory operations of a pair, in this order (the wait
+            // before the pair's barrier counts on it): SLOT 0's two weight
+            // loads and four staging loads, SLOT 1's five staging loads and
+            // two weight loads.  Staged: this K-tile's counterpart in the
+            // next pair (after an item's last pair: the next item's first),
+            // into the other ring slot.  Weights: the next K-tile's (after an
+            // item's last K-tile: the next item's first).
             {
-                // Interleaved with the MFMAs: the reloads of the weight chunks
-                // as soon as they are converted.
+                const bool anx = pr + 1 >= NPR;
+                const GItem &ait = anx ? nxt : cur;
+                const int apar = (ci + anx) & 1, apr = anx ? 0 : pr + 1;
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (SLOT == 0) {
+                    wB = wload(cur, kt + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    stage_half(std::integral_constant<int, 0>{}, ait, apar, apr, rq ^ 1);
+                } else {
+                    stage_half(std::integral_constant<int, 1>{}, ait, apar, apr, rq ^ 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    wA = wload(anx ? nxt : cur, anx ? 0 : kt + 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            {
                 half8 bq;
                 // a padding K-tile's operand is exactly zero (its stage may hold stale codes)
                 const bool real = kt < f.NT;
@@ -392,8 +423,7 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
                     constexpr int s = st >> 2, mt = st & 3;
                     constexpr bool pre = st + kPD < 32;
                     if constexpr (pre) xr[(st + kPD) % (kPD + 1)] = rd(st + kPD);
-                    if constexpr (st == 8) wq[1] = *reinterpret_cast<const u32x4 *>(wsrc + 512);
-                    if constexpr (mt == 0) bq = codes_to_signed_natural(wq[s >> 2][s & 3] & wmask, zp);
+                    if constexpr (mt == 0) bq = codes_to_signed_natural(wq.v[s >> 2][s & 3] & wmask, zp);
                     const half8 xf = xr[st % (kPD + 1)];
                     // weights as the first operand: lane l of the result then
                     // holds pair l % 32 of the m-tile (see the epilogue)
@@ -416,7 +446,7 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
                 // wavefront's 32 (tile n / 16, row n % 16), pair l % 32 of the
                 // m-tile; the scales of rows 8 q + 4 h2 .. +3 are 8 bytes at
                 // 16 q + 8 h2 of the wavefront's scale stage.
-                const uint8_t *sp = &L.sc[gg % kStages][f.wave][8 * f.h2];
+                const uint8_t *sp = &L.sc[rq][f.wave][8 * f.h2];
                 _Float16 scl[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -481,27 +511,27 @@ __global__ __launch_bounds__(kGThreads) void w4a16_gemm_kernel(FfnArgs a, const 
                 cur = nxt;
                 nxt = f.item(item_no(ci + 1), c1, hint);
                 // The next item's row offsets: loaded now, written to LDS at
-                // the end of the following K-tile (the first direct loads that
-                // read them come two K-tiles before this item ends; with only
-                // two K-tiles per item, at once).
+                // the end of its first pair (the first direct loads that read
+                // them come with this item's last pair; with one pair per
+                // item, at once).
                 pend = f.pair_of(nxt);
-                pend_put = NTP == 2;
+                pend_put = NPR == 1;
                 if (pend_put) f.put_src((ci + 1) & 1, f.src_of(nxt, pend));
                 if (cur.absent && threadIdx.x == 0 && a.status) *a.status = MOE_ERR_ABSENT_EXPERT;
-                kt = 0;
-                // Issued after the stages read next (loaded at the start of
-                // the previous K-tile): this K-tile's 7 direct loads, the
-                // output stores (gate/up 8, down 16) and the offset load.
-                stage_barrier<GATEUP ? 7 + 8 + 1 : 7 + 16>();
-            } else {
+                pr = 0;
+                // Issued after the staging loads of the pair read next: SLOT
+                // 1's two weight loads, the output stores (gate/up 8, down 16)
+                // and the offset load.
+                stage_barrier<GATEUP ? 2 + 8 + 1 : 2 + 16>();
+            } else if (SLOT == 1) {
                 if (!pend_put) {
                     f.put_src((ci + 1) & 1, f.src_of(nxt, pend));
                     pend_put = true;
                 }
-                ++kt;
-                // Issued after the stages read next (loaded at the start of
-                // the previous K-tile): this K-tile's 7 direct loads.
-                stage_barrier<7>();
+                ++pr;
+                // Issued after the staging loads of the pair read next: SLOT
+                // 1's two weight loads.
+                stage_barrier<2>();
             }
         });
     }
