@@ -75,6 +75,9 @@ def parse():
                          "replicas and input batches; each graph launch costs about 4.5 us, so one step per "
                          "graph is measurably slower)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed work before the warm-up steps and before the prefill "
+                         "sub-measurement (the GPU's clocks rise over the first tenths of a second)")
     ap.add_argument("--fused", action="store_true",
                     help="run each step through the one-call layer (moe_layer_forward) instead of the separate calls")
     ap.add_argument("--ffn-mode", choices=["auto", "stream", "ksplit"], default="auto",
@@ -357,7 +360,8 @@ def main():
             run_step(s)                 # warm every step once eagerly before capture
         torch.cuda.synchronize()
         cap = torch.cuda.Stream()
-        keys = sorted({(s % n_graph, n) for b0, bn in [(0, args.warmup)] + blocks for s, n in chunks(b0, bn)})
+        spans = [(0, n_graph), (0, args.warmup)] + blocks      # settle, warm-up, timed blocks
+        keys = sorted({(s % n_graph, n) for b0, bn in spans for s, n in chunks(b0, bn)})
         for s0, n in keys:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
@@ -375,18 +379,25 @@ def main():
         for s, n in chunks(s_begin, count):
             graphs[(s % n_graph, n)].replay()
 
+    # The GPU's clocks rise over the first tenths of a second of sustained work: untimed
+    # replays of whole rotations bring it to its steady state before the warm-up steps.
+    settle_s = settle(lambda: run_steps(0, n_graph), torch, args.settle)
     run_steps(0, args.warmup)
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed
-    block_s = []
-    for b0, bn in blocks:
-        torch.cuda.synchronize()
-        tb = time.perf_counter()
+    # One region, synchronized on both sides; HIP events between its blocks give the
+    # per-block rates without host synchronizations inside the region.
+    bev = [torch.cuda.Event(enable_timing=True) for _ in range(len(blocks) + 1)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    bev[0].record(stream)
+    for i, (b0, bn) in enumerate(blocks):
         run_steps(b0, bn)
-        torch.cuda.synchronize()
-        block_s.append(time.perf_counter() - tb)
-    elapsed = sum(block_s)
+        bev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    block_s = [bev[i].elapsed_time(bev[i + 1]) * 1e-3 for i in range(len(blocks))]
     ms_per_step = elapsed * 1e3 / K
     tokens_per_s = T * K / elapsed
     block_rates = [T * bn / t for (_, bn), t in zip(blocks, block_s)]
@@ -462,7 +473,7 @@ def main():
     # ---------------------------------------------------------------- prefill, same expert shape
     prefill = None
     if args.config == "olmoe" and not args.no_prefill:
-        prefill = measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev)
+        prefill = measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, args.settle)
 
     workload = f"{cfg.name}_decode_layer_T{T}" if args.config != "prefill" else f"prefill_T{T}"
     out = {
@@ -492,7 +503,9 @@ def main():
         },
         "blocks": {"steps": [bn for _, bn in blocks], "tokens_per_s": block_rates,
                    "spread": block_spread, "pooled_tokens_per_s": tokens_per_s,
-                   "spread_definition": "(max - min) / mean of the blocks' rates"},
+                   "spread_definition": "(max - min) / mean of the blocks' rates",
+                   "timing": "one host-timed region; HIP events on the launch stream between its blocks"},
+        "settle_s": settle_s,
         "roofline": ({
             "bound": "hbm",
             "kernel": "w4a16_ffn_kernel<gate/up> (W4A16 gate/up + SiLU*up)",
@@ -530,6 +543,16 @@ def main():
         out["shared_hbm"] = {"bytes_per_step": shared_bytes,
                              "achieved_gbs": shared_bytes / (mean_us["shared"] * 1e-6) / 1e9}
     print(json.dumps(out))
+
+
+def settle(run_once, torch, seconds: float) -> float:
+    """Repeat run_once (GPU work) until `seconds` of wall time have passed; returns the time spent."""
+    t0 = time.perf_counter()
+    while True:
+        run_once()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return time.perf_counter() - t0
 
 
 def host_threads() -> int:
@@ -585,10 +608,12 @@ def cpu_baselines(args, xs_np, wr_np, rows_np, shared_np, H, I, E, k, T, S, y_gp
     return one, allc
 
 
-def measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, rounds=3):
+def measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, settle_s, rounds=3):
     """Prefill-sized layer on the same expert shape (T = 4096, uniform router init, the
-    grouped-GEMM path): HIP events around back-to-back launches of each phase over the weight
-    replicas, on the launch stream.  Useful FLOPs: gate/up 2*T*k*H*2I, down 2*T*k*I*H."""
+    grouped-GEMM path): each phase captured as one graph of back-to-back launches over the
+    weight replicas, every graph replayed for `settle_s` seconds first (steady clocks), then
+    HIP events around `rounds` replays per phase on the launch stream.  Useful FLOPs: gate/up
+    2*T*k*H*2I, down 2*T*k*I*H."""
     cfg = synth.CONFIGS["prefill"]
     T, H, I, E, k = max(cfg.batches), cfg.H, cfg.I, cfg.E, cfg.k
     router = torch.from_numpy(synth.make_router(cfg)).to(dev)
@@ -611,12 +636,22 @@ def measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, rounds=3)
     for f in phases.values():           # warm each phase (and leave valid routing behind)
         f(0)
     torch.cuda.synchronize()
-    us = {}
+    cap = torch.cuda.Stream()
+    graphs = {}
     for name, f in phases.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(R):
+                f(i)
+        graphs[name] = g
+    torch.cuda.synchronize()
+    settled = settle(lambda: [g.replay() for g in graphs.values()], torch, settle_s)
+    us = {}
+    for name, g in graphs.items():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(rounds * R):
-            f(i % R)
+        for _ in range(rounds):
+            g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         us[name] = e0.elapsed_time(e1) * 1e3 / (rounds * R)
@@ -633,7 +668,9 @@ def measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, rounds=3)
                 "frac": tf(fl_gu + fl_dn, us["gateup"] + us["down"]) / FP16_MFMA_PEAK_TFLOPS},
         "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
         "layer_us": layer_us, "layer_tokens_per_s": T / (layer_us * 1e-6),
-        "timing": f"HIP events around {rounds * R} back-to-back launches of each phase over {R} weight replicas",
+        "settle_s": settled,
+        "timing": f"HIP events around {rounds} replays per phase of a graph of {R} back-to-back launches "
+                  f"over {R} weight replicas",
     }
 
 

@@ -437,12 +437,12 @@ int ffn::cu_count()
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     static int ncu[64];
     if (dev >= 0 && dev < 64) {
-        if (ncu[dev] == 0) {
-            int v = 0;
+        int v = __atomic_load_n(&ncu[dev], __ATOMIC_RELAXED);
+        if (v == 0) {
             if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-            ncu[dev] = v;
+            __atomic_store_n(&ncu[dev], v, __ATOMIC_RELAXED);
         }
-        return ncu[dev];
+        return v;
     }
     return 256;
 }
@@ -453,8 +453,8 @@ template <bool GATEUP, int NT, int S, bool F16W>
 int launch_one(const FfnArgs &a, hipStream_t s, long long max_items, const char *who)
 {
     auto kern = w4a16_ffn_kernel<GATEUP, NT, S, F16W>;
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess || occ <= 0) occ = 1;
+    static int occ_cache[64];
+    const int occ = moe::blocks_per_cu(kern, kThreads, occ_cache);
     long long g = (long long)cu_count() * occ;
     if (g > max_items) g = max_items;
     if (g < 1) g = 1;

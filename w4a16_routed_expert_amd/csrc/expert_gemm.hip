@@ -547,8 +547,8 @@ int launch_gemm(const FfnArgs &a, hipStream_t s, const char *who)
     const long long max_slots = pairs < a.E ? pairs : a.E;
     const long long max_items = (max_slots + pairs / kBM) * nblk;
     auto kern = w4a16_gemm_kernel<GATEUP>;
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kGThreads, 0) != hipSuccess || occ <= 0) occ = 1;
+    static int occ_cache[64];
+    const int occ = moe::blocks_per_cu(kern, kGThreads, occ_cache);
     long long g = (long long)cu_count() * occ;
     if (g > max_items) g = max_items;
     if (g < 1) g = 1;

@@ -254,8 +254,8 @@ template <int NTH, int W>
 int launch_w(const FfnArgs &a, float *planes, hipStream_t s, const char *who)
 {
     auto kern = w4a16_ffn_ksplit_kernel<NTH, W>;
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kKThreads, 0) != hipSuccess || occ <= 0) occ = 1;
+    static int occ_cache[64];
+    const int occ = moe::blocks_per_cu(kern, kKThreads, occ_cache);
     const long long pairs = (long long)a.T * a.k;
     const long long items = (pairs < a.E ? pairs : a.E) * (a.I / W);
     long long g = (long long)cu_count() * occ;

@@ -87,6 +87,22 @@ __device__ inline V sum_phases(V v)
     return v;
 }
 
+// Resident blocks per compute unit of kernel `kern` at `threads` threads on
+// the current device, asked of the runtime once per device and kept in
+// `cache` (one array per kernel: the caller's function-local static).  The
+// query is host work on every launch otherwise.
+template <typename K>
+inline int blocks_per_cu(K kern, int threads, int (&cache)[64])
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int occ = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (occ > 0) return occ;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess || occ <= 0) occ = 1;
+    __atomic_store_n(&cache[dev], occ, __ATOMIC_RELAXED);
+    return occ;
+}
+
 // Data handed between blocks of one launch.  Stores and loads at device
 // scope (relaxed atomics: the sc1 bit, coherent across the XCDs' L2 caches)
 // reach every block without write-back or invalidation of whole L2 caches
