@@ -80,9 +80,9 @@ def parse():
                          "sub-measurement (the GPU's clocks rise over the first tenths of a second)")
     ap.add_argument("--fused", action="store_true",
                     help="run each step through the one-call layer (moe_layer_forward) instead of the separate calls")
-    ap.add_argument("--ffn-mode", choices=["auto", "stream", "ksplit"], default="auto",
-                    help="--fused: the expert-FFN family of the one call (auto: the K-split launch for the "
-                         "smallest batches, else the streaming kernels)")
+    ap.add_argument("--ffn-mode", choices=["auto", "stream", "ksplit", "one"], default="auto",
+                    help="--fused: the expert-FFN family of the one call (auto: the library's choice; one: the "
+                         "whole layer in one persistent launch)")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="olmoe: skip the prefill measurement (T=4096, grouped GEMM) that the line carries")
@@ -289,7 +289,7 @@ def main():
     shared_done = torch.cuda.Event() if Is else None
 
     fused_mode = {"auto": B.MOE_FFN_PATH_AUTO, "stream": B.MOE_FFN_PATH_STREAM,
-                  "ksplit": B.MOE_FFN_PATH_KSPLIT}[args.ffn_mode]
+                  "ksplit": B.MOE_FFN_PATH_KSPLIT, "one": B.MOE_FFN_PATH_ONE_LAUNCH}[args.ffn_mode]
 
     def run_step_fused(s, ev=None):
         """One step through the one-call layer (moe_layer_forward); the shared expert, where

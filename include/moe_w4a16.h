@@ -76,6 +76,7 @@ enum moe_status {
     MOE_ERR_FAULTED = 6,         /* expert table faulted by a failure after publication */
     MOE_ERR_ABSENT_EXPERT = 7,   /* a routed expert has no published device row */
     MOE_ERR_SOURCE = 8,          /* expert table: host source failed its identity or layout check */
+    MOE_ERR_TIMEOUT = 9,         /* one-launch layer: a wait between its blocks gave up (status word) */
 };
 
 #define MOE_MAX_EXPERTS 64
@@ -189,8 +190,15 @@ int moe_route_static(const void *x_dev, const void *w_router_dev, const float *b
  *     (built for prefill batches, bound by the matrix cores);
  *   MOE_FFN_PATH_AUTO: the GEMM when T*k >= 64*E, else the streaming kernels.
  * Any other value returns MOE_ERR_INVALID_ARG. */
-enum moe_ffn_path { MOE_FFN_PATH_AUTO = 0, MOE_FFN_PATH_STREAM = 1, MOE_FFN_PATH_GEMM = 2, MOE_FFN_PATH_KSPLIT = 3 };
-/* MOE_FFN_PATH_KSPLIT: moe_layer_forward only (the FFN calls reject it); see there. */
+enum moe_ffn_path {
+    MOE_FFN_PATH_AUTO = 0,
+    MOE_FFN_PATH_STREAM = 1,
+    MOE_FFN_PATH_GEMM = 2,
+    MOE_FFN_PATH_KSPLIT = 3,
+    MOE_FFN_PATH_ONE_LAUNCH = 4
+};
+/* MOE_FFN_PATH_KSPLIT and MOE_FFN_PATH_ONE_LAUNCH: moe_layer_forward only (the
+ * FFN calls reject them); see there. */
 
 int moe_w4a16_gateup(const void *x_dev, int T, int H, int I, int E, int k,
                      const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,

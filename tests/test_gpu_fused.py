@@ -25,7 +25,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-STREAM, KSPLIT = 1, 3            # MOE_FFN_PATH_STREAM, MOE_FFN_PATH_KSPLIT
+STREAM, KSPLIT, ONE = 1, 3, 4    # MOE_FFN_PATH_STREAM, MOE_FFN_PATH_KSPLIT, MOE_FFN_PATH_ONE_LAUNCH
 
 
 def both(cfg, rows, wr, x, mode=STREAM, **kw):
@@ -38,10 +38,10 @@ def both(cfg, rows, wr, x, mode=STREAM, **kw):
 
 
 def workspace_is_zero(lay, T):
-    """The one-call layer leaves its counter zero (the routing launch's done counter, the first
-    256 bytes of the workspace)."""
+    """The one-call layer leaves its control words zero (the routing launch's done counter and
+    the one-launch layer's counters: the first 1024 bytes of the workspace)."""
     ws = lay.layer_ws.cpu().numpy()
-    return not ws[:256].any()
+    return not ws[:1024].any()
 
 
 @pytest.mark.parametrize("T", [1, 8, 32])
@@ -191,3 +191,114 @@ def test_repeated_calls_and_graph_replay():
         y1 = lay.forward_fused(xs[1])
         torch.cuda.synchronize()
         assert torch.equal(y1.view(torch.int16), want[1].view(torch.int16)), "eager call between replays differs"
+
+
+# ---------------------------------------------------------------- the one-launch layer
+# MOE_FFN_PATH_ONE_LAUNCH: routing, gate/up, down and the combine in one
+# persistent launch whose blocks hand results to each other through
+# device-scope counters.  Same kernels' arithmetic and splits as the separate
+# calls, so y (and h, pair_out, the routing results) must be bit-identical to
+# them, and every stage is checked against the oracle.
+
+def one_vs_separate(cfg, rows, wr, x, **kw):
+    one = gpu_layer(cfg, rows, wr, x, fused=True, mode=ONE, **kw)
+    sep = gpu_layer(cfg, rows, wr, x, mode=STREAM, **kw)
+    for key in ("ids", "w", "offsets", "sorted_pairs", "pair_pos", "active", "h", "pair_out"):
+        assert np.array_equal(one[key], sep[key]), f"one-launch layer: {key} differs from the separate calls"
+    assert np.array_equal(one["y"].view(np.uint16), sep["y"].view(np.uint16)), \
+        "one-launch layer and separate calls differ"
+    assert workspace_is_zero(one["layer"], x.shape[0])
+    return one
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 32])
+def test_one_launch_olmoe_decode(T):
+    # T = 1, 2-4 and 8-32 take the reduction-axis splits 4, 2 and 1
+    cfg = synth.CONFIGS["olmoe"]
+    rows, wr, x = rows_of("olmoe"), synth.make_router(cfg), synth.make_x(cfg, T, step=50 + T)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
+    got = one_vs_separate(cfg, rows, wr, x)
+    assert got["status"] == 0
+    check_full(cfg, got, ref, f"one-launch olmoe T={T}", rows=rows)
+
+
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_one_launch_qwen_decode_with_shared_expert(T):
+    cfg = synth.CONFIGS["qwen"]
+    rows, wr, x = rows_of("qwen"), synth.make_router(cfg), synth.make_x(cfg, T, step=60 + T)
+    shared = synth.make_shared(cfg)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, shared=shared, want_h=True)
+    got = one_vs_separate(cfg, rows, wr, x, shared=shared)
+    assert got["status"] == 0
+    check_full(cfg, got, ref, f"one-launch qwen + shared T={T}", rows=rows)
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 64])
+def test_one_launch_tiny(T):
+    cfg = synth.CONFIGS["tiny"]
+    rows, wr, x = rows_of("tiny"), synth.make_router(cfg), synth.make_x(cfg, T, step=70 + T)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, want_h=True)
+    got = one_vs_separate(cfg, rows, wr, x)
+    check_full(cfg, got, ref, f"one-launch tiny T={T}", rows=rows)
+
+
+def test_one_launch_absent_expert():
+    # an expert without a device row: status word set, its outputs zero, the
+    # rest as the separate calls compute them
+    cfg = synth.CONFIGS["tiny"]
+    T = 8
+    rows, wr, x = rows_of("tiny"), synth.make_router(cfg), synth.make_x(cfg, T, step=15)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k)
+    missing = int(ref["active"][0])
+    slot_map = np.arange(cfg.E, dtype=np.int32)
+    slot_map[missing] = -1
+    got = one_vs_separate(cfg, rows, wr, x, slot_map=slot_map)
+    assert got["status"] == 7
+    lo, hi = ref["offsets"][missing], ref["offsets"][missing + 1]
+    assert np.all(got["pair_out"][lo:hi] == 0)
+
+
+def test_one_launch_rejects_what_it_is_not_built_for():
+    from w4a16_routed_expert_amd import binding as B
+    cfg = synth.CONFIGS["olmoe"]
+    rows, wr = rows_of("olmoe"), synth.make_router(cfg)
+    x = synth.make_x(cfg, 65, step=1)              # T above the one-launch maximum of 64
+    with pytest.raises(B.MoeError) as ei:
+        gpu_layer(cfg, rows, wr, x, fused=True, mode=ONE)
+    assert ei.value.code == B.MOE_ERR_UNSUPPORTED
+
+
+def test_one_launch_repeated_calls_and_graph_replay():
+    # calls of different sizes in a row reuse the workspace (the last block of
+    # each call zeroes the counters); a captured call replays to the same bits
+    # between eager calls
+    cfg = synth.CONFIGS["olmoe"]
+    dev = torch.device("cuda:0")
+    from w4a16_routed_expert_amd.layer import RoutedExpertLayer
+    rows, wr = rows_of("olmoe"), synth.make_router(cfg)
+    lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev), torch.from_numpy(wr).to(dev),
+                            max_T=32, device=dev)
+    xs = {T: torch.from_numpy(synth.make_x(cfg, T, step=80 + T)).to(dev) for T in (32, 1, 8)}
+    want = {T: lay.forward(x, mode=STREAM).clone() for T, x in xs.items()}
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for T, x in xs.items():
+            y = lay.forward_fused(x, mode=ONE)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), want[T].view(torch.int16)), f"T={T}"
+            assert workspace_is_zero(lay, 32)
+            assert int(lay.status.cpu()[0]) == 0
+    y32 = torch.empty((32, cfg.H), dtype=torch.float16, device=dev)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        for _ in range(3):
+            lay.forward_fused(xs[32], y32, mode=ONE)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y32.view(torch.int16), want[32].view(torch.int16)), "graph replay differs"
+        y1 = lay.forward_fused(xs[1], mode=ONE)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), want[1].view(torch.int16)), "eager call between replays differs"
+    assert workspace_is_zero(lay, 32)

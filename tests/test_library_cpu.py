@@ -104,9 +104,16 @@ def test_layer_ksplit_mode_checks_and_workspace(lib):
                                 mode=B.MOE_FFN_PATH_KSPLIT, stream=0)
         assert ei.value.code == B.MOE_ERR_UNSUPPORTED and "K-split" in B.moe_last_error()
     with pytest.raises(B.MoeError) as ei:
-        B.moe_layer_forward(F, F, None, 4, 256, 512, 8, 2, F, 1 << 20, None, None, None, None, F, buf, mode=4,
+        B.moe_layer_forward(F, F, None, 4, 256, 512, 8, 2, F, 1 << 20, None, None, None, None, F, buf, mode=5,
                             stream=0)
     assert ei.value.code == B.MOE_ERR_INVALID_ARG
+    # the one-launch layer: decode batches of the shapes it is built for, rejected on the host otherwise
+    for T, H, I, E, k in ((65, 2048, 1024, 64, 8), (4, 384, 512, 8, 2), (4, 2048, 1024, 63, 8),
+                          (64, 256, 512, 8, 8)):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_layer_forward(F, F, None, T, H, I, E, k, F, 1 << 22, None, None, None, None, F, buf,
+                                mode=B.MOE_FFN_PATH_ONE_LAUNCH, stream=0)
+        assert ei.value.code == B.MOE_ERR_UNSUPPORTED and "one-launch" in B.moe_last_error(), (T, H, I, E, k)
     # a workspace sized for T serves every smaller batch (the planes of the
     # K-split path depend on the batch through the slice width)
     for (H, I, E, k) in ((2048, 1024, 64, 8), (2048, 1408, 60, 4), (256, 512, 8, 2)):

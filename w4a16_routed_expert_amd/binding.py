@@ -24,6 +24,7 @@ MOE_ERR_HIP = 5
 MOE_ERR_FAULTED = 6
 MOE_ERR_ABSENT_EXPERT = 7
 MOE_ERR_SOURCE = 8
+MOE_ERR_TIMEOUT = 9
 
 MOE_SLOT_QPACKED = 0
 MOE_SLOT_FP16 = 1
@@ -32,6 +33,7 @@ MOE_FFN_PATH_AUTO = 0
 MOE_FFN_PATH_STREAM = 1
 MOE_FFN_PATH_GEMM = 2
 MOE_FFN_PATH_KSPLIT = 3
+MOE_FFN_PATH_ONE_LAUNCH = 4
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (

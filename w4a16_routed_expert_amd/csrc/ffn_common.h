@@ -179,6 +179,15 @@ __device__ inline void build_table(SlotTable &tb, const FfnArgs &a, const TableI
 // Compute units of the current device (cached per device).
 int cu_count();
 
+// Split of the reduction axis the streaming launches choose for a batch
+// (expert_ffn.hip), and the argument checks and set-up of those launches
+// (returns -1 for T = 0: nothing to do).
+int stream_split(bool gateup, int T, int H, int I, int E, int k);
+int make_ffn_args(FfnArgs &a, const void *x_dev, int T, int H, int I, int E, int k, const void *rows_dev,
+                  size_t row_stride, const int32_t *slot_map_dev, const int32_t *expert_offsets_dev,
+                  const int32_t *sorted_pairs_dev, const int32_t *active_list_dev, const int32_t *n_active_dev,
+                  void *h_dev, float *pair_out_dev, int32_t *status_dev, const char *who);
+
 // Grouped-GEMM launches for large batches (expert_gemm.hip).
 int launch_gemm_gateup(const FfnArgs &a, hipStream_t s);
 int launch_gemm_down(const FfnArgs &a, hipStream_t s);

@@ -21,7 +21,7 @@
 
 namespace {
 
-constexpr size_t kCtrl = 256;                       // done counter (and padding)
+constexpr size_t kCtrl = 1024;                      // control words: routing counter, one-launch layer counters
 // AUTO never takes the K-split FFN: measured on the MI355X it loses to the
 // streaming pair at every batch (OLMoE shape, one-call layer: T = 1 31.3 us
 // against 28.1 us, the planes' combine costing more than the launch saved;
@@ -71,8 +71,12 @@ int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *
     int rc = moe::check_shape(T, H, I, E, k, true);
     if (rc) return rc;
     if (mode != MOE_FFN_PATH_AUTO && mode != MOE_FFN_PATH_STREAM && mode != MOE_FFN_PATH_GEMM &&
-        mode != MOE_FFN_PATH_KSPLIT)
+        mode != MOE_FFN_PATH_KSPLIT && mode != MOE_FFN_PATH_ONE_LAUNCH)
         return moe::fail(MOE_ERR_INVALID_ARG, "%s: unknown mode %d", who, mode);
+    if (mode == MOE_FFN_PATH_ONE_LAUNCH && T > 0 && !moe::layer_persistent_supported(T, H, I, E, k))
+        return moe::fail(MOE_ERR_UNSUPPORTED, "%s: the one-launch layer takes decode batches (1 <= T <= %d, "
+                         "T*k < 64*E, E even) of the shapes it is built for, H/128 and I/128 in {(2, 4), (16, 8), "
+                         "(16, 11)} (T=%d, H=%d, I=%d, E=%d, k=%d)", who, moe::kPersistentMaxT, T, H, I, E, k);
     const int width = T >= 1 ? moe::ffn_ksplit_width(T, H, I, E, k) : 0;
     if (mode == MOE_FFN_PATH_KSPLIT && T > 0 && width == 0)
         return moe::fail(MOE_ERR_UNSUPPORTED, "%s: the K-split expert FFN needs T <= 16, H <= 2048 with H/128 even "
@@ -93,6 +97,15 @@ int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *
     unsigned int *done = (unsigned int *)ws;
     void *route_ws = ws + kCtrl;
     const size_t route_ws_bytes = moe::route_logits_bytes(T, E);
+    if (mode == MOE_FFN_PATH_ONE_LAUNCH) {
+        if (shared_ready_event) {
+            const hipError_t e = hipStreamWaitEvent(s, (hipEvent_t)shared_ready_event, 0);
+            if (e != hipSuccess) return moe::fail(MOE_ERR_HIP, "%s: waiting for the shared expert: %s", who,
+                                                  hipGetErrorString(e));
+        }
+        return moe::layer_persistent(x_dev, w_router_dev, bias_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev,
+                                     shared_out_dev, shared_gate_dev, y_dev, b, (float *)route_ws, (uint32_t *)ws, s);
+    }
     const bool stream_kernels = mode == MOE_FFN_PATH_STREAM || mode == MOE_FFN_PATH_KSPLIT ||
                                 (mode == MOE_FFN_PATH_AUTO && (long long)T * k < 64LL * E);
     const bool ksplit = mode == MOE_FFN_PATH_KSPLIT ||

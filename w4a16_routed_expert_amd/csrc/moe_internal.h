@@ -113,6 +113,26 @@ inline int blocks_per_cu(K kern, int threads, int (&cache)[64])
 __device__ inline void store_dev(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ inline float load_dev(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ inline void store_dev(int32_t *p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline int32_t load_dev(const int32_t *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline void store_dev(uint32_t *p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline uint32_t load_dev(const uint32_t *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// Store or load plainly, or at device scope when DEV.
+template <bool DEV, typename V>
+__device__ inline void put(V *p, V v)
+{
+    if constexpr (DEV) store_dev(p, v);
+    else *p = v;
+}
+template <bool DEV, typename V>
+__device__ inline V get(const V *p)
+{
+    if constexpr (DEV) return load_dev(p);
+    else return *p;
+}
+// Cache-policy operand of the buffer intrinsics for device-scope accesses
+// (sc1: coherent across the XCDs' L2 caches, like the relaxed atomics above).
+constexpr int kDevScope = 16;
 
 // y[t][c4*4 .. c4*4+3] = RN16( sum_{j<k} topk_w[t][j] * pair_out[pair_pos[t*k+j]][..]
 // (+ shared_gate[t] * shared_out[t][..]) ), FP32 in slot order: the combine of
@@ -210,5 +230,16 @@ int ffn_ksplit(const void *x_dev, int T, int H, int I, int E, int k, const void 
                const int32_t *slot_map_dev, const int32_t *expert_offsets_dev, const int32_t *sorted_pairs_dev,
                const int32_t *active_list_dev, const int32_t *n_active_dev, void *h_dev, int32_t *status_dev,
                float *planes, int width, hipStream_t s);
+
+// layer_persistent.hip: the routed layer of a decode batch in one launch.
+// The control words (layer_persistent_ctl_bytes, at the start of the layer
+// workspace) are zero before and after each call; lbuf: FP32 [T][E].
+constexpr int kPersistentMaxT = 64;
+size_t layer_persistent_ctl_bytes();
+bool layer_persistent_supported(int T, int H, int I, int E, int k);
+int layer_persistent(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int I, int E,
+                     int k, const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                     const float *shared_out_dev, const float *shared_gate_dev, void *y_dev,
+                     const moe_layer_buffers *b, float *lbuf, uint32_t *ctl, hipStream_t s);
 
 }  // namespace moe
