@@ -52,7 +52,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense FP16 matrix peak
-FFN_SOURCE = os.path.join(ROOT, "w4a16_routed_expert_amd", "csrc", "expert_ffn.hip")
+# the sources the streaming gate/up kernel is compiled from (the traffic counters are tied to them)
+FFN_SOURCE = [os.path.join(ROOT, "w4a16_routed_expert_amd", "csrc", f)
+              for f in ("expert_ffn.hip", "ffn_stream.h", "ffn_common.h", "moe_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic.json")
 
 
@@ -141,9 +143,13 @@ def traffic_report(gu_fetch, gu_write, copy_fetch, copy_write, out_path, config_
     print(json.dumps(d))
 
 
-def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(paths) -> str:
+    """sha256 over the files' contents in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(config_name: str, T: int):

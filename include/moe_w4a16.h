@@ -234,6 +234,21 @@ int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
  *     plane order (and writes that sum to pair_out).  Same operation and
  *     rounding points; only the FP32 summation order of the down projection
  *     differs from the streaming kernels.  Three launches in all.
+ *   - mode ONE_LAUNCH (1 <= T <= 64, T*k < 64*E, E even, (H/128, I/128) in
+ *     {(2, 4), (16, 8), (16, 11)}; AUTO does not choose it: measured slower
+ *     than the separate launches, OLMoE shape T = 1 30.6 against 29.2 us,
+ *     T = 32 78.1 against 60.4 us): the routing AND the expert FFN AND the
+ *     combine in ONE launch.  Its grid is exactly the blocks resident at once;
+ *     blocks hand the routing results, h and the pair outputs to each other
+ *     through device-scope counters in the workspace (published by the
+ *     writer after its stores complete, polled by the reader).  y, h,
+ *     pair_out and the routing results are bit-identical to the separate
+ *     calls.  Every wait is bounded: a wait that gives up writes
+ *     MOE_ERR_TIMEOUT to the status word (the call's outputs are then
+ *     undefined) - which needs every block of the launch to be resident,
+ *     so calls that can overlap on one GPU must not share it with other
+ *     long-running kernels.  shared_ready_event is waited for before the
+ *     launch (the shared expert then does not overlap the routed work);
  *   - otherwise the streaming gate/up and down launches and the combine (y
  *     then bit-identical to the separate calls).
  * Other batches run moe_route, moe_w4a16_expert_ffn and moe_combine in order.
@@ -244,6 +259,9 @@ int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
  *     aligned, ZERO-FILLED BEFORE ITS FIRST USE; every call leaves its counter
  *     zero again (a workspace sized for T serves any T' <= T); not shared by
  *     calls that can overlap.
+ * Workspace control words: the first moe_layer_workspace_size bytes hold,
+ * at their start, the counters of the routing launch and of the one-launch
+ * layer (1 KB); every call leaves them zero.
  * shared_out / shared_gate: the shared-expert terms (moe_shared_ffn) or both
  * NULL; shared_ready_event: a hipEvent_t recorded after the shared expert (on
  * another stream), waited for before the combine, or NULL when the shared
