@@ -302,3 +302,32 @@ def test_one_launch_repeated_calls_and_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(y1.view(torch.int16), want[1].view(torch.int16)), "eager call between replays differs"
     assert workspace_is_zero(lay, 32)
+
+
+def test_one_launch_wait_gives_up_on_a_workspace_that_was_not_zeroed():
+    # The routing counter of the one-launch layer starts at a value the
+    # election never reaches, so no block publishes the routing and every
+    # wait for it runs into its poll limit (the kernel still ends: the waits
+    # are bounded): MOE_ERR_TIMEOUT in the status word.  The last block to
+    # leave zeroes the counters, so the next call is correct again.
+    from w4a16_routed_expert_amd import binding as B
+    from w4a16_routed_expert_amd.layer import RoutedExpertLayer
+    cfg = synth.CONFIGS["tiny"]
+    dev = torch.device("cuda:0")
+    T = 4
+    rows, wr, x = rows_of("tiny"), synth.make_router(cfg), synth.make_x(cfg, T, step=90)
+    lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev), torch.from_numpy(wr).to(dev),
+                            max_T=T, device=dev)
+    xd = torch.from_numpy(x).to(dev)
+    want = lay.forward(xd, mode=STREAM).clone()
+    torch.cuda.synchronize()
+    lay.layer_ws[:4].view(torch.int32).fill_(1 << 20)         # logits counter far past any task count
+    lay.forward_fused(xd, mode=ONE)
+    torch.cuda.synchronize()
+    assert int(lay.status.cpu()[0]) == B.MOE_ERR_TIMEOUT
+    assert workspace_is_zero(lay, T)
+    lay.status.zero_()
+    y = lay.forward_fused(xd, mode=ONE)
+    torch.cuda.synchronize()
+    assert int(lay.status.cpu()[0]) == 0
+    assert torch.equal(y.view(torch.int16), want.view(torch.int16))
