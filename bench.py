@@ -614,6 +614,50 @@ def cpu_baselines(args, xs_np, wr_np, rows_np, shared_np, H, I, E, k, T, S, y_gp
     return one, allc
 
 
+def stack_cpu_baselines(args, synth, cfg, host_rows, x_np, T, L):
+    """The oracle on the stack workload: whole layers of one step (layer l's rows, router, bias and
+    shared expert) until about --cpu-seconds of CPU time, scaled to tokens/s of the L-layer stack;
+    then every host thread on the same layers (whole tokens per thread)."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+
+    def args_of(l):
+        return (synth.make_router(cfg, layer=l), host_rows[l],
+                synth.make_zipf_bias(cfg, layer=l) if cfg.zipf_s else None,
+                synth.make_shared(cfg, layer=l) if cfg.shared_I else None)
+    done, cpu_s = [], 0.0
+    while cpu_s < args.cpu_seconds and len(done) < L:
+        l = len(done)
+        wr, rows, bias, shared = args_of(l)
+        tc = time.perf_counter()
+        oracle.layer(x_np, wr, rows, H, I, E, k, bias=bias, shared=shared)
+        cpu_s += time.perf_counter() - tc
+        done.append(l)
+    per_layer = cpu_s / len(done)
+    one = {"value": T / (per_layer * L), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"{len(done)} of the {L} layers of one step, {T} tokens each ({cpu_s:.1f} s, "
+                     f"single-threaded C, fp64), scaled to the {L}-layer stack"}
+    nt = host_threads()
+    per = max(1, -(-T // nt))
+    tasks = [(l, a, min(T, a + per)) for l in done for a in range(0, T, per)]
+    cache = {l: args_of(l) for l in done}
+
+    def run(task):
+        l, a, e = task
+        wr, rows, bias, shared = cache[l]
+        oracle.layer(x_np[a:e], wr, rows, H, I, E, k, bias=bias, shared=shared)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        list(ex.map(run, tasks))
+    wall = time.perf_counter() - t0
+    allc = {"value": T * len(done) / (wall * L), "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"the same {len(done)} layers, {len(tasks)} token chunks on {nt} host threads "
+                      f"({wall:.1f} s wall), scaled to the {L}-layer stack"}
+    return one, allc
+
+
 def measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, settle_s, rounds=3):
     """Prefill-sized layer on the same expert shape (T = 4096, uniform router init, the
     grouped-GEMM path): each phase captured as one graph of back-to-back launches over the
@@ -852,6 +896,9 @@ def run_stack(args, torch, dev):
         lay.check_status()
     h2d_ceiling = pinned_h2d_gbs(torch, dev)
     demand = delta["hits"] + delta["misses"]
+    cpu = cpu_all = None
+    if not args.skip_cpu:
+        cpu, cpu_all = stack_cpu_baselines(args, synth, cfg, host, x0s[0].cpu().numpy(), T, L)
     out = {
         "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode) / MFMA % (prefill)",
         "value": T * K / elapsed,
@@ -883,8 +930,16 @@ def run_stack(args, torch, dev):
             "pinned_h2d_ceiling_gbs": h2d_ceiling,
             "h2d_frac_of_pinned_ceiling": delta["h2d_bytes"] / elapsed / 1e9 / h2d_ceiling,
         },
+        "roofline": {"bound": "hbm", "kernel": "expert FFN (gate/up + down launches of each layer)",
+                     "achieved": ffn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ffn_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": ffn_bytes / (n_ffn * L),
+                     "avg_launch_us": ffn_us / (n_ffn * L),
+                     "timing": f"HIP events around the expert FFN of {n_ffn} steps x {L} layers (eager); the "
+                               "step itself is bound by the host-to-device misses (residency)"},
         "ffn_hbm": {"achieved_gbs": ffn_gbs, "frac": ffn_gbs / HBM_PEAK_GBS,
                     "timing": f"HIP events around the expert FFN of {n_ffn} steps x {L} layers"},
+        "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
         "setup_s": {"generate_inputs": gen_s},
     }
     for t in tables:
