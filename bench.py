@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--ffn-mode", choices=["auto", "stream", "ksplit", "one"], default="auto",
                     help="--fused: the expert-FFN family of the one call (auto: the library's choice; one: the "
                          "whole layer in one persistent launch)")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="--fused with a shared expert: the layer and its shared expert in one call on one stream "
+                         "(moe_layer_forward_shared: the routing launch also runs the shared gate/up pass)")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="olmoe: skip the prefill measurement (T=4096, grouped GEMM) that the line carries")
@@ -305,6 +308,13 @@ def main():
         main = torch.cuda.current_stream()
         if ev is not None:
             ev[0].record(stream)
+        if Is and args.one_stream:
+            Wsg, Wsu, Wsd, wg = shared_reps[r]
+            B.moe_layer_forward_shared(x, router, None, T, H, I, E, k, rows, lay.row_stride, None, Wsg, Wsu, Wsd,
+                                       wg, Is, sh_out, sh_gate, sh_ws, sh_ws_bytes, y, lay._bufs, fused_mode, main)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         if Is:
             side.wait_stream(main)
             Wsg, Wsu, Wsd, wg = shared_reps[r]
@@ -499,7 +509,10 @@ def main():
             "workload": workload,
             "experts": E, "top_k": k, "hidden": H, "intermediate": I, "tokens": T,
             "shared_expert_intermediate": Is,
-            "shared_expert_stream": "second stream, concurrent with routing and the routed experts" if Is else None,
+            "shared_expert_stream": (None if not Is else
+                                     "one stream, gate/up pass in the routing launch"
+                                     if args.fused and args.one_stream else
+                                     "second stream, concurrent with routing and the routed experts"),
             "layer_call": f"moe_layer_forward (one call, expert FFN {args.ffn_mode})" if args.fused else "separate calls",
             "weights": "int4 qpacked, 256-value blocks, fp16 scales; fp16 activations, fp32 accumulation",
             "replicas": R, "input_batches": S, "graph_replay": not args.no_graph,

@@ -288,6 +288,27 @@ int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *
                       const float *shared_out_dev, const float *shared_gate_dev, void *shared_ready_event,
                       void *y_dev, const moe_layer_buffers *buffers, int mode, void *stream);
 
+/* moe_layer_forward_shared: the layer with its FP16 shared expert in one call
+ * (moe_shared_ffn, then moe_layer_forward with the shared terms, and the same
+ * results bit for bit).  For decode batches whose shared gate/up is one pass
+ * of 8-row units over the whole reduction axis (T <= 16 at H = 2048) and that
+ * take the streaming kernels (mode STREAM, or AUTO with T*k < 64*E; E even,
+ * w_router 4-byte aligned), the routing launch also runs the shared expert's
+ * gate/up pass and sigmoid gate as extra blocks (the routing is bound by
+ * latency and leaves HBM idle; a second stream does not overlap the two on
+ * this GPU because each launch's grid takes every CU), then the routed expert
+ * FFN, the shared down projection and the combine follow on `stream`.  Other
+ * batches and modes run moe_shared_ffn and moe_layer_forward in order.
+ * Arguments: those of moe_layer_forward (without shared_ready_event) and of
+ * moe_shared_ffn (shared weights in the tile8 layout, shared_out, shared_gate,
+ * and its workspace of moe_shared_ffn_workspace_size(T, H, Is) bytes). */
+int moe_layer_forward_shared(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int I,
+                             int E, int k, const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
+                             const void *w_sgate_proj_dev, const void *w_sup_dev, const void *w_sdown_dev,
+                             const void *w_sgate_dev, int Is, float *shared_out_dev, float *shared_gate_dev,
+                             void *shared_ws_dev, size_t shared_ws_bytes, void *y_dev,
+                             const moe_layer_buffers *buffers, int mode, void *stream);
+
 /* ------------------------------------------------------------ shared expert
  * moe_shared_ffn: the FP16 shared expert of a layer that has one (non-routed
  * weights stay FP16: "horizonrunmap.com/en", section "08 / Precision &

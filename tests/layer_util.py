@@ -17,11 +17,12 @@ def rows_of(name):
 
 
 def gpu_layer(cfg, rows_np, wr, x, bias=None, slot_map=None, rows_dev=None, mode=None, shared=None, fused=False,
-              fp16_slots=False):
+              fp16_slots=False, one_stream=False):
     """One layer call through the C ABI; mode: None (automatic) or a B.MOE_FFN_PATH_* value;
     shared: None or the FP16 shared expert (Wsg, Wsu, Wsd, wgate) as numpy arrays, run on a
     second stream beside the routed experts; fused: the one-call layer (moe_layer_forward)
-    instead of the separate calls."""
+    instead of the separate calls; one_stream: the layer with its shared expert in one call on
+    one stream (moe_layer_forward_shared)."""
     import torch
     from w4a16_routed_expert_amd import binding as B
     from w4a16_routed_expert_amd.layer import RoutedExpertLayer, SharedExpert
@@ -46,6 +47,8 @@ def gpu_layer(cfg, rows_np, wr, x, bias=None, slot_map=None, rows_dev=None, mode
     xd = torch.from_numpy(x).to(dev)
     if fp16_slots:
         y = lay.forward(xd, shared=sh, fp16_slots=True)
+    elif one_stream:
+        y = lay.forward_shared(xd, sh, mode=B.MOE_FFN_PATH_AUTO if mode is None else mode)
     else:
         fwd = lay.forward_fused if fused else lay.forward
         y = fwd(xd, mode=B.MOE_FFN_PATH_AUTO if mode is None else mode, shared=sh)

@@ -331,3 +331,94 @@ def test_one_launch_wait_gives_up_on_a_workspace_that_was_not_zeroed():
     torch.cuda.synchronize()
     assert int(lay.status.cpu()[0]) == 0
     assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+
+
+# ---------------------------------------------------------------- the layer with its shared expert on one stream
+# moe_layer_forward_shared: for decode batches the routing launch also runs
+# the FP16 shared expert's gate/up pass (extra blocks of the same grid), then
+# the expert FFN, the shared down projection and the combine follow on the
+# same stream.  Every block computes what the separate launches compute, so
+# y, the routing results, h, pair_out and the shared expert's outputs must be
+# bit-identical to the shared expert on a second stream beside the one-call
+# layer; other batches and modes take the separate calls in stream order.
+
+SHARED_KEYS = ("ids", "w", "offsets", "sorted_pairs", "pair_pos", "active", "h", "pair_out", "shared_os",
+               "shared_sigma", "shared_hs")
+
+
+def shared_one_stream(cfg, rows, wr, x, shared, mode=None):
+    one = gpu_layer(cfg, rows, wr, x, shared=shared, one_stream=True, mode=mode)
+    two = gpu_layer(cfg, rows, wr, x, shared=shared, fused=True, mode=mode)
+    for key in SHARED_KEYS:
+        assert np.array_equal(one[key], two[key]), f"one-stream shared layer: {key} differs"
+    assert np.array_equal(one["y"].view(np.uint16), two["y"].view(np.uint16)), \
+        "one-stream shared layer and the two-stream call differ"
+    assert workspace_is_zero(one["layer"], x.shape[0])
+    return one
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 64])
+def test_qwen_layer_with_shared_expert_on_one_stream(T):
+    # T = 1, 5 and 16 take the routing + shared gate/up launch; T = 64 a
+    # shared gate/up plan with wider token tiles, hence the separate calls
+    cfg = synth.CONFIGS["qwen"]
+    rows, wr, x = rows_of("qwen"), synth.make_router(cfg), synth.make_x(cfg, T, step=120 + T)
+    shared = synth.make_shared(cfg)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, shared=shared, want_h=True)
+    got = shared_one_stream(cfg, rows, wr, x, shared)
+    assert got["status"] == 0
+    check_full(cfg, got, ref, f"one-stream qwen + shared T={T}", rows=rows)
+
+
+@pytest.mark.parametrize("T", [1, 7, 16])
+def test_tiny_layer_with_shared_expert_on_one_stream(T):
+    # a small grid: 8 experts, H = 256, a 512-wide shared expert
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], shared_I=512)
+    rows, wr, x = rows_of("tiny"), synth.make_router(cfg), synth.make_x(cfg, T, step=130 + T)
+    shared = synth.make_shared(cfg)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, shared=shared, want_h=True)
+    got = shared_one_stream(cfg, rows, wr, x, shared)
+    check_full(cfg, got, ref, f"one-stream tiny + shared T={T}", rows=rows)
+
+
+@pytest.mark.parametrize("mode", [2, 3, 4])   # GEMM, K-split, one launch: the separate calls
+def test_shared_on_one_stream_other_modes(mode):
+    cfg = synth.CONFIGS["qwen"]
+    T = 4
+    rows, wr, x = rows_of("qwen"), synth.make_router(cfg), synth.make_x(cfg, T, step=140 + mode)
+    shared = synth.make_shared(cfg)
+    shared_one_stream(cfg, rows, wr, x, shared, mode=mode)
+
+
+def test_shared_on_one_stream_repeated_calls_and_graph_replay():
+    from w4a16_routed_expert_amd.layer import RoutedExpertLayer, SharedExpert
+    cfg = synth.CONFIGS["qwen"]
+    dev = torch.device("cuda:0")
+    rows, wr = rows_of("qwen"), synth.make_router(cfg)
+    lay = RoutedExpertLayer(cfg.H, cfg.I, cfg.E, cfg.k, torch.from_numpy(rows).to(dev), torch.from_numpy(wr).to(dev),
+                            max_T=16, device=dev)
+    sh = SharedExpert(*(torch.from_numpy(np.ascontiguousarray(m)).to(dev) for m in synth.make_shared(cfg)),
+                      max_T=16, device=dev)
+    xs = {T: torch.from_numpy(synth.make_x(cfg, T, step=150 + T)).to(dev) for T in (16, 1, 9)}
+    want = {T: lay.forward_fused(x, shared=sh).clone() for T, x in xs.items()}
+    torch.cuda.synchronize()
+    for _ in range(2):
+        for T, x in xs.items():
+            y = lay.forward_shared(x, sh)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), want[T].view(torch.int16)), f"T={T}"
+            assert workspace_is_zero(lay, 16)
+    y16 = torch.empty((16, cfg.H), dtype=torch.float16, device=dev)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        lay.forward_shared(xs[16], sh, y16)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y16.view(torch.int16), want[16].view(torch.int16)), "graph replay differs"
+        y1 = lay.forward_shared(xs[1], sh)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), want[1].view(torch.int16)), "eager call between replays differs"
+    assert workspace_is_zero(lay, 16)

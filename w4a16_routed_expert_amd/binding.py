@@ -41,7 +41,7 @@ EXPORTS = (
     "moe_route_workspace_size", "moe_route", "moe_route_exact", "moe_route_static_max_bytes", "moe_route_static",
     "moe_w4a16_gateup", "moe_w4a16_down", "moe_w4a16_expert_ffn",
     "moe_combine", "moe_shared_ffn_workspace_size", "moe_shared_ffn", "moe_pack_fp16_tile8",
-    "moe_layer_workspace_size", "moe_layer_forward", "moe_residual_add",
+    "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_shared", "moe_residual_add",
     "moe_expert_row_bytes_fp16", "moe_dequant_expert_rows", "moe_fp16_expert_ffn",
     "moe_row_digest", "moe_table_create", "moe_table_destroy", "moe_table_device", "moe_table_misses",
     "moe_upload_expert_rows", "moe_table_prefetch", "moe_table_acquire", "moe_table_release", "moe_table_verify_source",
@@ -136,6 +136,9 @@ def load(path: str = LIB_PATH):
     L.moe_layer_forward.restype = _i
     L.moe_layer_forward.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp,
                                     ctypes.POINTER(LayerBuffers), _i, _vp]
+    L.moe_layer_forward_shared.restype = _i
+    L.moe_layer_forward_shared.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp, _vp, _vp,
+                                           _i, _vp, _vp, _vp, _sz, _vp, ctypes.POINTER(LayerBuffers), _i, _vp]
     L.moe_expert_row_bytes_fp16.restype = _sz
     L.moe_expert_row_bytes_fp16.argtypes = [_i, _i]
     L.moe_dequant_expert_rows.restype = _i
@@ -308,6 +311,15 @@ def moe_layer_forward(x, w_router, bias, T, H, I, E, k, rows, row_stride, slot_m
     _check(load().moe_layer_forward(_p(x), _p(w_router), _p(bias), T, H, I, E, k, _p(rows), row_stride,
                                     _p(slot_map), _p(shared_out), _p(shared_gate), ev, _p(y),
                                     ctypes.byref(buffers), mode, _s(stream)))
+
+
+def moe_layer_forward_shared(x, w_router, bias, T, H, I, E, k, rows, row_stride, slot_map, w_sgate_proj, w_sup,
+                             w_sdown, w_sgate, Is, shared_out, shared_gate, shared_ws, shared_ws_bytes, y,
+                             buffers: LayerBuffers, mode=MOE_FFN_PATH_AUTO, stream=None):
+    _check(load().moe_layer_forward_shared(_p(x), _p(w_router), _p(bias), T, H, I, E, k, _p(rows), row_stride,
+                                           _p(slot_map), _p(w_sgate_proj), _p(w_sup), _p(w_sdown), _p(w_sgate), Is,
+                                           _p(shared_out), _p(shared_gate), _p(shared_ws), shared_ws_bytes, _p(y),
+                                           ctypes.byref(buffers), mode, _s(stream)))
 
 
 def moe_expert_row_bytes_fp16(H: int, I: int) -> int:

@@ -21,7 +21,7 @@
 
 namespace {
 
-constexpr size_t kCtrl = 1024;                      // control words: routing counter, one-launch layer counters
+constexpr size_t kCtrl = moe::kLayerCtrlBytes;      // control words: routing counter, one-launch layer counters
 // AUTO never takes the K-split FFN: measured on the MI355X it loses to the
 // streaming pair at every batch (OLMoE shape, one-call layer: T = 1 31.3 us
 // against 28.1 us, the planes' combine costing more than the launch saved;

@@ -205,6 +205,10 @@ int dequant_rows(const void *q_rows, size_t q_stride, void *f_rows, size_t f_str
 
 // Pieces of the fused layer (moe_layer_forward).
 constexpr int kFusedMaxT = 256;        // largest batch routed in one launch
+// The layer workspace starts with this many bytes of control words (the
+// routing launch's counter first, then the one-launch layer's counters); the
+// routing logits follow.
+constexpr size_t kLayerCtrlBytes = 1024;
 
 // route.hip: logits, top-k and grouping of 1 <= T <= kFusedMaxT tokens in one
 // launch.  lbuf: FP32 [T][E] (route_logits_bytes); done: a counter that is 0

@@ -213,34 +213,14 @@ __global__ __launch_bounds__(kGrpThreads) void route_group_kernel(RouteArgs a)
     group_phase<kGrpWaves, TOPK>(a, s_grp);
 }
 
-// Small batches in one launch (the fused layer, moe_layer_forward): every
-// block computes its (token, expert group) logits as route_logits_kernel
-// does, stored at device scope; once they are complete the block counts
-// itself in the workspace, and the block that counts last (no block ever
-// waits for another) runs the top-k and the grouping over all logits, read
-// at device scope, and resets the counter for the next call.
-union FusedRouteLds {
-    LogitsLds lg;
-    GroupLds<kSelWaves, true> gr;
-};
-
+// Small batches in one launch (the fused layer, moe_layer_forward): block b
+// runs logits task b (fused_route_task in route_dev.h).
 template <int VEC>
 __global__ __launch_bounds__(kSelThreads) void route_fused_kernel(RouteArgs a, unsigned int *done)
 {
     __shared__ FusedRouteLds S;
     __shared__ int s_last;
-    const int G = (a.E + kGroupE - 1) / kGroupE;
-    logits_block<VEC, true>(a, S.lg, blockIdx.x / G, blockIdx.x % G);
-    moe::wait_stores();                                     // this wave's logits are complete
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned int before = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = before == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    group_phase<kSelWaves, true, true>(a, S.gr);
-    if (threadIdx.x == 0) *done = 0u;
+    fused_route_task<VEC>(a, S, s_last, done, blockIdx.x, gridDim.x);
 }
 
 // Large batches: the stable counting sort runs on many blocks (one single

@@ -400,7 +400,10 @@ __device__ void logits_block(const RouteArgs &a, LogitsLds &S, int t, int g)
 {
     constexpr int EQ = kGroupE / VEC;
     constexpr int RPW = 64 / EQ;
-    constexpr int U = VEC >= 8 ? 8 : 32;     // rows in flight per thread (all of H = 2048 in one batch)
+    // rows in flight per thread: 16 (two batches for H = 2048; 32 in one
+    // batch measured no faster and needs 152 VGPRs instead of 96, too many
+    // for a routing block to share a CU with another kernel's block)
+    constexpr int U = VEC >= 8 ? 8 : 16;
     typedef WLoad<VEC> L;
     constexpr int kPath = kMaxH / (RPW * kSelWaves) + ilog2_ceil(RPW) + kSelWaves;
     constexpr int kErrExp = ilog2_ceil(kPath) + 1 - 53;
@@ -523,6 +526,36 @@ __device__ void logits_block(const RouteArgs &a, LogitsLds &S, int t, int g)
             else a.lbuf[(size_t)t * E + e] = lv;
         }
     }
+}
+
+// Small batches in one launch: every logits task (token, expert group) is
+// computed as route_logits_kernel does and stored at device scope; once it
+// is complete its block counts itself in `done`, and the block that counts
+// last (no block ever waits for another) runs the top-k and the grouping over
+// all logits, read at device scope, and resets the counter for the next call.
+union FusedRouteLds {
+    LogitsLds lg;
+    GroupLds<kSelWaves, true> gr;
+};
+
+// Logits task `task` of `ntask` (token task / G, expert group task % G, G
+// groups of kGroupE experts).
+template <int VEC>
+__device__ inline void fused_route_task(const RouteArgs &a, FusedRouteLds &S, int &s_last, unsigned int *done, int task,
+                                        int ntask)
+{
+    const int G = (a.E + kGroupE - 1) / kGroupE;
+    logits_block<VEC, true>(a, S.lg, task / G, task % G);
+    moe::wait_stores();                                     // this wave's logits are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned int before = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = before == (unsigned int)ntask - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    group_phase<kSelWaves, true, true>(a, S.gr);
+    if (threadIdx.x == 0) *done = 0u;
 }
 
 }  // namespace

@@ -164,6 +164,27 @@ class RoutedExpertLayer:
             main.wait_stream(shared.side_stream())   # the side stream's work is joined before reuse
         return y
 
+    def forward_shared(self, x: torch.Tensor, shared: "SharedExpert", y: torch.Tensor | None = None, stream=None,
+                       rows=None, lease=None, mode: int = B.MOE_FFN_PATH_AUTO) -> torch.Tensor:
+        """y = layer(x) with the shared expert, all on one stream (moe_layer_forward_shared): for
+        decode batches the routing launch also runs the shared expert's gate/up pass; the
+        result equals forward_fused's with the same shared expert."""
+        T = x.shape[0]
+        if T > self.max_T:
+            self._alloc(T)
+        if y is None:
+            y = torch.empty((T, self.H), dtype=torch.float16, device=self.device)
+        shared.ensure(T)
+        if lease is not None:
+            rows_dev, stride, smap = lease.rows_dev, lease.row_stride, lease.slot_map_dev
+        else:
+            rows_dev, stride, smap = self._rows(rows)
+        B.moe_layer_forward_shared(x, self.router, self.bias, T, self.H, self.I, self.E, self.k, rows_dev, stride,
+                                   smap, shared.wg, shared.wu, shared.wd, shared.wgate, shared.Is, shared.out,
+                                   shared.gate, shared.ws, shared.ws.numel(), y, self._bufs, mode,
+                                   _torch_stream(stream))
+        return y
+
     def active_experts(self, stream=None):
         """Active expert ids of the last route, on the host.  The copies are ordered after
         the work already enqueued on `stream` (the stream the route ran on; None = the
@@ -245,13 +266,17 @@ class SharedExpert:
             self._side = torch.cuda.Stream(device=self.device)
         return self._side
 
-    def run(self, x: torch.Tensor, stream=None):
-        T = x.shape[0]
+    def ensure(self, T: int):
+        """Output buffers and workspace for a batch of T tokens (grown, never shrunk)."""
         if T > self.max_T:
             self._alloc(T)
         need = B.moe_shared_ffn_workspace_size(T, self.H, self.Is)
         if need > self.ws.numel():
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def run(self, x: torch.Tensor, stream=None):
+        T = x.shape[0]
+        self.ensure(T)
         B.moe_shared_ffn(x, self.wg, self.wu, self.wd, self.wgate, T, self.H, self.Is, self.out, self.gate,
                          self.ws, self.ws.numel(), stream)
 
