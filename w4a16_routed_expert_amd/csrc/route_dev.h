@@ -287,6 +287,7 @@ __device__ inline unsigned long long same_expert_lanes(int e)
 
 constexpr int kGrpLdsIds = 4096;           // pairs whose ids the grouping keeps in LDS
 constexpr int kTopkBatch = 2;              // tokens a wave routes together
+constexpr int kTopkChunk = 8;              // tokens whose logits a wave requests together
 
 template <int NW, bool TOPK>
 struct GroupLds {
@@ -309,23 +310,36 @@ __device__ void group_phase(const RouteArgs &a, GroupLds<NW, TOPK> &S)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.T * a.k, E = a.E;
     if (TOPK) {
-        // kTopkBatch tokens per wave at a time: logits loaded, then routed together
-        for (int t0 = wave; t0 < a.T; t0 += NW * kTopkBatch) {
-            int tok[kTopkBatch];
-            float lv[kTopkBatch];
+        // A wave routes tokens wave, wave + NW, ...: the logit rows of kTopkChunk of
+        // them are requested together (one memory round trip per chunk, not one
+        // per pair of tokens), then routed kTopkBatch at a time.
+        for (int c0 = wave; c0 < a.T; c0 += NW * kTopkChunk) {
+            int tok[kTopkChunk];
+            float lv[kTopkChunk];
 #pragma unroll
-            for (int i = 0; i < kTopkBatch; ++i) {
-                tok[i] = t0 + i * NW;
+            for (int i = 0; i < kTopkChunk; ++i) {
+                tok[i] = c0 + i * NW;
                 // clamped (always valid) addresses: the loads issue back to back
                 const float *src = a.lbuf + (size_t)min(tok[i], a.T - 1) * E + min(lane, E - 1);
                 lv[i] = DEV ? moe::load_dev(src) : *src;
             }
             if (a.logits && a.logits != a.lbuf && lane < E) {
 #pragma unroll
-                for (int i = 0; i < kTopkBatch; ++i)
+                for (int i = 0; i < kTopkChunk; ++i)
                     if (tok[i] < a.T) a.logits[(size_t)tok[i] * E + lane] = lv[i];
             }
-            topk_softmax_wave<kTopkBatch, DEV>(a, tok, lane, lv, S.ids);
+#pragma unroll
+            for (int i = 0; i < kTopkChunk; i += kTopkBatch) {
+                if (tok[i] >= a.T) break;                   // the rest of the chunk is past the batch
+                int tb[kTopkBatch];
+                float lb[kTopkBatch];
+#pragma unroll
+                for (int j = 0; j < kTopkBatch; ++j) {
+                    tb[j] = tok[i + j];
+                    lb[j] = lv[i + j];
+                }
+                topk_softmax_wave<kTopkBatch, DEV>(a, tb, lane, lb, S.ids);
+            }
         }
         __syncthreads();
     }
