@@ -125,6 +125,35 @@ def test_layer_ksplit_mode_checks_and_workspace(lib):
     assert B.moe_layer_workspace_size(4, 2048, 1024, 64, 9) == 0
 
 
+def test_layer_with_shared_expert_checks(lib):
+    # moe_layer_forward_shared validates the shared expert's arguments, the
+    # layer shape and (on its routing + shared gate/up path) the layer buffers
+    # before any device call
+    F = 0x1000
+    buf = B.LayerBuffers(F, F, F, F, F, F, F, F, F, F, F, F, 1 << 30)
+    qwen = (2048, 1408, 60, 4)
+
+    def call(T=1, H=2048, I=1408, E=60, k=4, Is=5632, wsg=F, sh_out=F, sh_ws_bytes=1 << 30, bufs=buf):
+        B.moe_layer_forward_shared(F, F, None, T, H, I, E, k, F, 1 << 23, None, wsg, F, F, F, Is, sh_out, F, F,
+                                   sh_ws_bytes, F, bufs, stream=0)
+
+    for kw, code, word in ((dict(Is=5600), B.MOE_ERR_UNSUPPORTED, "multiples of 128"),
+                           (dict(wsg=None), B.MOE_ERR_INVALID_ARG, "null"),
+                           (dict(sh_out=F + 8), B.MOE_ERR_INVALID_ARG, "aligned"),
+                           (dict(sh_ws_bytes=256), B.MOE_ERR_WORKSPACE, "shared-expert workspace"),
+                           (dict(E=65, k=4), B.MOE_ERR_UNSUPPORTED, None),
+                           (dict(bufs=B.LayerBuffers(F, F, F, F, F, F, F, F, F, F, F, F, 4096)),
+                            B.MOE_ERR_WORKSPACE, "layer workspace")):
+        with pytest.raises(B.MoeError) as ei:
+            call(**kw)
+        assert ei.value.code == code, kw
+        if word:
+            assert word in B.moe_last_error(), (kw, B.moe_last_error())
+    assert B.moe_layer_workspace_size(1, *qwen) > 4096
+    # T = 0: nothing to do
+    call(T=0)
+
+
 def test_table_create_rejects_before_touching_the_gpu(lib):
     # moe_table_create validates the descriptor and the host source's identity
     # and layout before any device call, so these run without a GPU.
