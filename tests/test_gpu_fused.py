@@ -336,7 +336,7 @@ def test_one_launch_wait_gives_up_on_a_workspace_that_was_not_zeroed():
 # ---------------------------------------------------------------- the layer with its shared expert on one stream
 # moe_layer_forward_shared: for decode batches the routing launch also runs
 # the FP16 shared expert's gate/up pass (extra blocks of the same grid), then
-# the expert FFN, the shared down projection and the combine follow on the
+# the expert FFN, the rest of the shared expert and the combine follow on the
 # same stream.  Every block computes what the separate launches compute, so
 # y, the routing results, h, pair_out and the shared expert's outputs must be
 # bit-identical to the shared expert on a second stream beside the one-call
@@ -357,10 +357,11 @@ def shared_one_stream(cfg, rows, wr, x, shared, mode=None):
     return one
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 64])
+@pytest.mark.parametrize("T", [1, 5, 16, 24, 64, 100])
 def test_qwen_layer_with_shared_expert_on_one_stream(T):
-    # T = 1, 5 and 16 take the routing + shared gate/up launch; T = 64 a
-    # shared gate/up plan with wider token tiles, hence the separate calls
+    # T = 1, 5 and 16 take the routing + shared gate/up launch (8-row units
+    # over the whole axis); T = 24, 64 and 100 (16-row units with 2 or 4 token
+    # tiles) the separate calls in stream order
     cfg = synth.CONFIGS["qwen"]
     rows, wr, x = rows_of("qwen"), synth.make_router(cfg), synth.make_x(cfg, T, step=120 + T)
     shared = synth.make_shared(cfg)

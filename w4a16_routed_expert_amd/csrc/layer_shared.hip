@@ -12,10 +12,11 @@
 // extra blocks: blocks below the routing task count run the fused routing
 // (logits of one (token, expert group) task, the last one also the top-k and
 // the grouping), the others the gate/up units of the shared expert and its
-// sigmoid gate.  With 96 (routing) and at most 125 (gate/up) VGPRs two such
-// blocks share a CU, so the routing and the gate/up pass run together.  Then
-// the routed expert FFN, the shared expert's down projection and the combine
-// follow on the same stream.  Every block computes exactly what the
+// sigmoid gate.  For the one-token-tile plans fused here the kernel needs
+// 103-245 VGPRs, and routing blocks run beside the pass's blocks, so the
+// shared weights stream while the logits and the top-k run.  Then the
+// routed expert FFN, the rest of the shared expert and the combine follow on
+// the same stream.  Every block computes exactly what the
 // separate launches compute (the same units with the same block stride), so
 // the outputs are bit-identical to moe_shared_ffn followed by
 // moe_layer_forward.
@@ -28,39 +29,61 @@ int cu_count();   // compute units of the current device (expert_ffn.hip)
 
 namespace {
 
-template <int NTW>
+template <int MT>
 union RouteSharedLds {
     FusedRouteLds r;
-    shx::StreamLds<true, 1> s;
+    shx::StreamLds<true, MT> s;
 };
 
 // Blocks [0, ntask): fused routing task blockIdx.x.  Blocks from ntask on:
-// block b - ntask of the shared expert's gate/up pass (8-row units over the
-// whole reduction axis, one token tile, n_main unit blocks then the
-// sigmoid-gate blocks).
-template <int NTW>
+// block b - ntask of the shared expert's gate/up pass as planned (RU-row
+// units, MT token tiles per pass, NTW tiles per wavefront, nkc chunks of the
+// reduction axis: with more than one, FP32 partial sums to the workspace;
+// n_main unit blocks, then the sigmoid-gate blocks).
+template <int MT, int NTW, int RU>
 __global__ __launch_bounds__(kSelThreads) void route_shared_kernel(RouteArgs ra, unsigned int *done, int ntask,
-                                                                  shx::SArgs sa, int n_main)
+                                                                  shx::SArgs sa, int nkc, int n_main)
 {
-    __shared__ RouteSharedLds<NTW> L;
+    __shared__ RouteSharedLds<MT> L;
     __shared__ int s_last;
     if ((int)blockIdx.x < ntask) {
         fused_route_task<2>(ra, L.r, s_last, done, blockIdx.x, ntask);
         return;
     }
-    shx::fp16_stream_block<true, 1, NTW, 8>(sa, 1, n_main, nullptr, (int)blockIdx.x - ntask,
-                                            (int)gridDim.x - ntask, L.s);
+    shx::fp16_stream_block<true, MT, NTW, RU>(sa, nkc, n_main, sa.part, (int)blockIdx.x - ntask,
+                                              (int)gridDim.x - ntask, L.s);
 }
 
-template <int NTW>
-int launch_route_shared(const RouteArgs &ra, unsigned int *done, const shx::SArgs &sa, hipStream_t s)
+template <int MT, int NTW, int RU>
+int launch_route_shared(const RouteArgs &ra, unsigned int *done, const shx::SArgs &sa, int nkc, hipStream_t s)
 {
     const int ntask = ra.T * ((ra.E + kGroupE - 1) / kGroupE);
     int n_main = 0, n_sig = 0;
     shx::gateup_blocks(sa, &n_main, &n_sig);
     const unsigned int grid = (unsigned int)(ntask + n_main + n_sig);
-    hipLaunchKernelGGL(route_shared_kernel<NTW>, dim3(grid), dim3(kSelThreads), 0, s, ra, done, ntask, sa, n_main);
+    hipLaunchKernelGGL((route_shared_kernel<MT, NTW, RU>), dim3(grid), dim3(kSelThreads), 0, s, ra, done, ntask, sa,
+                       nkc, n_main);
     return moe::check_launch("moe_layer_forward_shared (routing + shared gate/up)");
+}
+
+// The batches that take the fused launch: those whose gate/up pass is one
+// token tile in 8-row units over the whole reduction axis (1-4 tiles per
+// wavefront), where the routing occupies a few CUs and the pass streams on
+// the rest.  Wider plans (16-row units, 2 or 4 token tiles, split axis) were
+// measured no faster fused (Qwen shape T = 32 95.6 against 94.8 us per step,
+// T = 64 111.9 against 111.8): the routing then has a block on most CUs, and
+// the pass, planned for one block per CU, shares them.
+bool plan_fused(const shx::GateupPlan &p) { return p.ru == 8 && p.mt == 1 && p.ntw >= 1 && p.ntw <= 4; }
+
+int launch_planned(const shx::GateupPlan &p, const RouteArgs &ra, unsigned int *done, const shx::SArgs &sa,
+                   hipStream_t s)
+{
+    switch (p.ntw) {
+    case 1: return launch_route_shared<1, 1, 8>(ra, done, sa, p.nkc, s);
+    case 2: return launch_route_shared<1, 2, 8>(ra, done, sa, p.nkc, s);
+    case 3: return launch_route_shared<1, 3, 8>(ra, done, sa, p.nkc, s);
+    default: return launch_route_shared<1, 4, 8>(ra, done, sa, p.nkc, s);
+    }
 }
 
 }  // namespace
@@ -83,9 +106,9 @@ int moe_layer_forward_shared(const void *x_dev, const void *w_router_dev, const 
     if (rc) return rc < 0 ? MOE_OK : rc;
     rc = moe::check_shape(T, H, I, E, k, true);
     if (rc) return rc;
-    const int ntw = shx::fused_gateup_ntw(T, H, Is);
+    const shx::GateupPlan plan = shx::gateup_plan(T, H, Is);
     const bool stream_kernels = mode == MOE_FFN_PATH_STREAM || (mode == MOE_FFN_PATH_AUTO && (long long)T * k < 64LL * E);
-    const bool fused = ntw >= 1 && ntw <= 4 && stream_kernels && T <= moe::kFusedMaxT && H <= kMaxH && E % 2 == 0 &&
+    const bool fused = plan_fused(plan) && stream_kernels && T <= moe::kFusedMaxT && H <= kMaxH && E % 2 == 0 &&
                        moe::aligned(w_router_dev, 4) && moe::aligned(x_dev, 8);
     if (!fused) {
         // any other batch or mode: the shared expert, then the one-call layer, in stream order
@@ -120,12 +143,7 @@ int moe_layer_forward_shared(const void *x_dev, const void *w_router_dev, const 
     // the layer workspace: control words (the routing counter first), then the logits
     a.lbuf = (float *)((uint8_t *)b->ws + moe::kLayerCtrlBytes);
     unsigned int *done = (unsigned int *)b->ws;
-    switch (ntw) {
-    case 1: rc = launch_route_shared<1>(a, done, sa, s); break;
-    case 2: rc = launch_route_shared<2>(a, done, sa, s); break;
-    case 3: rc = launch_route_shared<3>(a, done, sa, s); break;
-    default: rc = launch_route_shared<4>(a, done, sa, s); break;
-    }
+    rc = launch_planned(plan, a, done, sa, s);
     if (rc) return rc;
     rc = moe_w4a16_expert_ffn(x_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev, b->expert_offsets,
                               b->sorted_pairs, b->active_list, b->n_active, b->h, b->pair_out, b->status, mode, stream);

@@ -294,16 +294,20 @@ __device__ void fp16_stream_block(const SArgs &a, int nkc, int n_main, float *ds
 
 // Host side (shared_ffn.hip).  make_args: the checks and set-up of
 // moe_shared_ffn (MOE_OK, an error code, or -1 for T = 0: nothing to do).
-// fused_gateup_ntw: when the gate/up projection of a batch is one pass of
-// 8-row units over the whole reduction axis (no partial sums: T <= 16 for
-// the shapes here), its tiles per wavefront; else 0.  gateup_blocks: the
-// blocks of that pass (without the sigmoid-gate blocks), and the
-// sigmoid-gate blocks.  launch_rest: everything of the shared expert after
-// that gate/up pass (the down projection, with its chunk sums if any).
+// gateup_plan: how the gate/up pass of a batch is cut (rows per unit, token
+// tiles per pass, tiles per wavefront per unit, chunks of the reduction axis;
+// with more than one chunk the pass writes FP32 partial sums to the
+// workspace).  gateup_blocks: the blocks of that pass (without the
+// sigmoid-gate blocks), and the sigmoid-gate blocks.  launch_rest:
+// everything of the shared expert after that pass (the SwiGLU of the summed
+// chunks if any, the down projection, its chunk sums if any).
+struct GateupPlan {
+    int ru, mt, ntw, nkc;
+};
 int make_args(SArgs &a, const void *x_dev, const void *w_gate_dev, const void *w_up_dev, const void *w_down_dev,
               const void *w_sgate_dev, int T, int H, int Is, float *shared_out_dev, float *shared_gate_dev,
               void *ws_dev, size_t ws_bytes, const char *who);
-int fused_gateup_ntw(int T, int H, int Is);
+GateupPlan gateup_plan(int T, int H, int Is);
 void gateup_blocks(const SArgs &a, int *n_main, int *n_sig);
 int launch_rest(const SArgs &a, hipStream_t s, const char *who);
 

@@ -216,10 +216,10 @@ int shx::make_args(SArgs &a, const void *x_dev, const void *w_gate_dev, const vo
     return MOE_OK;
 }
 
-int shx::fused_gateup_ntw(int T, int H, int Is)
+shx::GateupPlan shx::gateup_plan(int T, int H, int Is)
 {
     const Plan pg = plan_of(true, T, Is, H);
-    return (pg.ru == 8 && pg.nkc == 1 && pg.mt == 1) ? pg.ntw : 0;
+    return GateupPlan{pg.ru, pg.mt, pg.ntw, pg.nkc};
 }
 
 void shx::gateup_blocks(const SArgs &a, int *n_main, int *n_sig)
@@ -234,6 +234,14 @@ void shx::gateup_blocks(const SArgs &a, int *n_main, int *n_sig)
 
 int shx::launch_rest(const SArgs &a, hipStream_t s, const char *who)
 {
+    const Plan pg = plan_of(true, a.T, a.Is, a.H);
+    if (pg.nkc > 1) {
+        // SwiGLU of the summed chunks, about 4 columns per thread
+        hipLaunchKernelGGL(shared_gateup_finish, dim3(finish_grid((long long)a.T * (a.Is / 4))), dim3(kThreads), 0,
+                           s, a, pg.nkc);
+        const int rc = moe::check_launch(who);
+        if (rc) return rc;
+    }
     const Plan pd = plan_of(false, a.T, a.H, a.Is);
     int rc = launch_proj<false>(a, pd, pd.nkc > 1 ? a.part : a.out, s, who);
     if (rc || pd.nkc == 1) return rc;
@@ -263,13 +271,6 @@ int moe_shared_ffn(const void *x_dev, const void *w_gate_dev, const void *w_up_d
     const Plan pg = plan_of(true, T, Is, H);
     rc = launch_proj<true>(a, pg, a.part, s, "moe_shared_ffn (gate/up)");
     if (rc) return rc;
-    if (pg.nkc > 1) {
-        // SwiGLU of the summed chunks, about 4 columns per thread
-        hipLaunchKernelGGL(shared_gateup_finish, dim3(finish_grid((long long)T * (Is / 4))), dim3(kThreads), 0, s, a,
-                           pg.nkc);
-        rc = moe::check_launch("moe_shared_ffn (SwiGLU)");
-        if (rc) return rc;
-    }
     return shx::launch_rest(a, s, "moe_shared_ffn");
 }
 
