@@ -30,7 +30,9 @@ steps); the line reports the pooled rate (all tokens over all block time) and
 the blocks' spread.  For the OLMoE-shaped layer the line also carries the
 prefill-sized layer on the same expert shape (T = 4096, grouped GEMM): each
 phase timed with HIP events over back-to-back launches, the FFN's useful FLOPs
-against the FP16 MFMA peak.
+against the FP16 MFMA peak - and what vendor code reaches on the same GPU
+(`practical_ceilings`: a 1 GiB device copy, an 8192^3 FP16 matrix product),
+beside the published peaks the fractions are taken against.
 
 The CPU baseline times the oracle (C, fp64) on a bounded sample of the same
 workload, on one thread and on every host thread (at most 16).
@@ -491,6 +493,10 @@ def main():
     if args.config == "olmoe" and not args.no_prefill:
         prefill = measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, args.settle)
 
+    ceilings = None
+    if args.config == "olmoe" and not args.no_prefill:
+        ceilings = measure_ceilings(torch, dev)
+
     workload = f"{cfg.name}_decode_layer_T{T}" if args.config != "prefill" else f"prefill_T{T}"
     out = {
         "metric": "W4A16 MoE layer tokens/s + HBM GB/s on qpacked bytes (decode) / MFMA % (prefill)",
@@ -556,6 +562,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
         "prefill": prefill,
+        "practical_ceilings": ceilings,
         "setup_s": {"generate_inputs": gen_s},
     }
     if Is and not args.fused:
@@ -669,6 +676,40 @@ def stack_cpu_baselines(args, synth, cfg, host_rows, x_np, T, L):
             "sample": f"the same {len(done)} layers, {len(tasks)} token chunks on {nt} host threads "
                       f"({wall:.1f} s wall), scaled to the {L}-layer stack"}
     return one, allc
+
+
+def measure_ceilings(torch, dev, settle_s=0.3):
+    """What vendor code reaches on this GPU, beside the published peaks the fractions use: a
+    1 GiB device-to-device copy (torch copy_, HBM read + write bytes per second) and an
+    8192^3 FP16 matrix product (torch.mm, the ROCm BLAS libraries), each timed with HIP events
+    around 10 calls after a settle."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    a = torch.randn((8192, 8192), dtype=torch.float16, device=dev)
+    b = torch.randn((8192, 8192), dtype=torch.float16, device=dev)
+    c = torch.empty((8192, 8192), dtype=torch.float16, device=dev)
+
+    def timed(f, reps=10):
+        settle(f, torch, settle_s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_copy = timed(lambda: dst.copy_(src))
+    t_mm = timed(lambda: torch.mm(a, b, out=c))
+    copy_gbs = 2 * n / t_copy / 1e9
+    mm_tflops = 2 * 8192 ** 3 / t_mm / 1e12
+    del src, dst, a, b, c
+    return {"hbm_copy_gbs": copy_gbs, "hbm_copy_frac": copy_gbs / HBM_PEAK_GBS,
+            "fp16_gemm_tflops": mm_tflops, "fp16_gemm_frac": mm_tflops / FP16_MFMA_PEAK_TFLOPS,
+            "what": "torch copy_ of 1 GiB (read + write bytes) and torch.mm of 8192^3 FP16, HIP events "
+                    "around 10 calls after a settle"}
 
 
 def measure_prefill(torch, B, synth, RoutedExpertLayer, replicas, dev, settle_s, rounds=3):

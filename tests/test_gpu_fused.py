@@ -383,6 +383,18 @@ def test_tiny_layer_with_shared_expert_on_one_stream(T):
     check_full(cfg, got, ref, f"one-stream tiny + shared T={T}", rows=rows)
 
 
+@pytest.mark.parametrize("E,k,T", [(37, 5, 3), (8, 2, 9)])
+def test_shared_on_one_stream_shapes_off_the_fused_path(E, k, T):
+    # an odd expert count (37) takes the separate calls; H = 384 (three
+    # 128-column tiles) and a 640-wide shared expert exercise other plans
+    cfg = synth.LayerConfig(f"edge{E}x{k}s", 11, E=E, k=k, H=384, I=256, batches=(T,), resident=E, shared_I=640)
+    rows, wr, x = synth.make_expert_rows(cfg), synth.make_router(cfg), synth.make_x(cfg, T)
+    shared = synth.make_shared(cfg)
+    ref = oracle.layer(x, wr, rows, cfg.H, cfg.I, cfg.E, cfg.k, shared=shared, want_h=True)
+    got = shared_one_stream(cfg, rows, wr, x, shared)
+    check_full(cfg, got, ref, f"one-stream E={E} k={k} T={T} + shared", rows=rows)
+
+
 @pytest.mark.parametrize("mode", [2, 3, 4])   # GEMM, K-split, one launch: the separate calls
 def test_shared_on_one_stream_other_modes(mode):
     cfg = synth.CONFIGS["qwen"]
