@@ -301,7 +301,11 @@ int moe_layer_forward(const void *x_dev, const void *w_router_dev, const float *
  * batches and modes run moe_shared_ffn and moe_layer_forward in order.
  * Arguments: those of moe_layer_forward (without shared_ready_event) and of
  * moe_shared_ffn (shared weights in the tile8 layout, shared_out, shared_gate,
- * and its workspace of moe_shared_ffn_workspace_size(T, H, Is) bytes). */
+ * and its workspace of moe_shared_ffn_workspace_size(T, H, Is) bytes).
+ * Errors: both calls' argument checks (shapes, nulls, alignment, both
+ * workspaces, the mode) run before anything is launched; only a shape that
+ * mode KSPLIT or ONE_LAUNCH does not take is reported after the shared expert
+ * has run (by the moe_layer_forward it then calls). */
 int moe_layer_forward_shared(const void *x_dev, const void *w_router_dev, const float *bias_dev, int T, int H, int I,
                              int E, int k, const void *rows_dev, size_t row_stride, const int32_t *slot_map_dev,
                              const void *w_sgate_proj_dev, const void *w_sup_dev, const void *w_sdown_dev,

@@ -149,6 +149,10 @@ def test_layer_with_shared_expert_checks(lib):
         assert ei.value.code == code, kw
         if word:
             assert word in B.moe_last_error(), (kw, B.moe_last_error())
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_layer_forward_shared(F, F, None, 1, 2048, 1408, 60, 4, F, 1 << 23, None, F, F, F, F, 5632, F, F, F,
+                                   1 << 30, F, buf, mode=9, stream=0)
+    assert ei.value.code == B.MOE_ERR_INVALID_ARG and "mode" in B.moe_last_error()
     assert B.moe_layer_workspace_size(1, *qwen) > 4096
     # T = 0: nothing to do
     call(T=0)

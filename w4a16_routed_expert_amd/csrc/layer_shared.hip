@@ -106,18 +106,10 @@ int moe_layer_forward_shared(const void *x_dev, const void *w_router_dev, const 
     if (rc) return rc < 0 ? MOE_OK : rc;
     rc = moe::check_shape(T, H, I, E, k, true);
     if (rc) return rc;
-    const shx::GateupPlan plan = shx::gateup_plan(T, H, Is);
-    const bool stream_kernels = mode == MOE_FFN_PATH_STREAM || (mode == MOE_FFN_PATH_AUTO && (long long)T * k < 64LL * E);
-    const bool fused = plan_fused(plan) && stream_kernels && T <= moe::kFusedMaxT && H <= kMaxH && E % 2 == 0 &&
-                       moe::aligned(w_router_dev, 4) && moe::aligned(x_dev, 8);
-    if (!fused) {
-        // any other batch or mode: the shared expert, then the one-call layer, in stream order
-        rc = moe_shared_ffn(x_dev, w_sgate_proj_dev, w_sup_dev, w_sdown_dev, w_sgate_dev, T, H, Is, shared_out_dev,
-                            shared_gate_dev, shared_ws_dev, shared_ws_bytes, stream);
-        if (rc) return rc;
-        return moe_layer_forward(x_dev, w_router_dev, bias_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev,
-                                 shared_out_dev, shared_gate_dev, nullptr, y_dev, b, mode, stream);
-    }
+    // the layer's own arguments first, so that a rejected call launches nothing
+    if (mode != MOE_FFN_PATH_AUTO && mode != MOE_FFN_PATH_STREAM && mode != MOE_FFN_PATH_GEMM &&
+        mode != MOE_FFN_PATH_KSPLIT && mode != MOE_FFN_PATH_ONE_LAUNCH)
+        return moe::fail(MOE_ERR_INVALID_ARG, "%s: unknown mode %d", who, mode);
     if (!b || !w_router_dev || !rows_dev || !y_dev || !b->topk_ids || !b->topk_w || !b->expert_offsets ||
         !b->sorted_pairs || !b->pair_pos || !b->active_list || !b->n_active || !b->h || !b->pair_out)
         return moe::fail(MOE_ERR_INVALID_ARG, "%s: null pointer argument", who);
@@ -126,6 +118,19 @@ int moe_layer_forward_shared(const void *x_dev, const void *w_router_dev, const 
     const size_t need = moe_layer_workspace_size(T, H, I, E, k);
     if (!b->ws || b->ws_bytes < need || !moe::aligned(b->ws, 256))
         return moe::fail(MOE_ERR_WORKSPACE, "%s: the layer workspace needs %zu bytes, 256-byte aligned", who, need);
+    const shx::GateupPlan plan = shx::gateup_plan(T, H, Is);
+    const bool stream_kernels = mode == MOE_FFN_PATH_STREAM || (mode == MOE_FFN_PATH_AUTO && (long long)T * k < 64LL * E);
+    const bool fused = plan_fused(plan) && stream_kernels && T <= moe::kFusedMaxT && H <= kMaxH && E % 2 == 0 &&
+                       moe::aligned(w_router_dev, 4) && moe::aligned(x_dev, 8);
+    if (!fused) {
+        // any other batch or mode: the shared expert, then the one-call layer, in stream order (a
+        // shape that mode rejects is reported by moe_layer_forward, after the shared expert ran)
+        rc = moe_shared_ffn(x_dev, w_sgate_proj_dev, w_sup_dev, w_sdown_dev, w_sgate_dev, T, H, Is, shared_out_dev,
+                            shared_gate_dev, shared_ws_dev, shared_ws_bytes, stream);
+        if (rc) return rc;
+        return moe_layer_forward(x_dev, w_router_dev, bias_dev, T, H, I, E, k, rows_dev, row_stride, slot_map_dev,
+                                 shared_out_dev, shared_gate_dev, nullptr, y_dev, b, mode, stream);
+    }
     RouteArgs a;
     a.x = (const uint16_t *)x_dev;
     a.wr = (const uint16_t *)w_router_dev;
