@@ -181,6 +181,10 @@ def main():
               "(the layer is single-GPU; multi-GPU sharding is described in the design notes, not built).",
               file=sys.stderr)
         sys.exit(2)
+    if args.one_stream and not args.fused:
+        print("--one-stream selects the one-call layer with its shared expert: use it with --fused",
+              file=sys.stderr)
+        sys.exit(2)
 
     import torch
     from w4a16_routed_expert_amd import binding as B
