@@ -236,8 +236,8 @@ int moe_w4a16_expert_ffn(const void *x_dev, int T, int H, int I, int E, int k,
  *     differs from the streaming kernels.  Three launches in all.
  *   - mode ONE_LAUNCH (1 <= T <= 64, T*k < 64*E, E even, (H/128, I/128) in
  *     {(2, 4), (16, 8), (16, 11)}; AUTO does not choose it: measured slower
- *     than the separate launches, OLMoE shape T = 1 30.6 against 29.2 us,
- *     T = 32 78.1 against 60.4 us): the routing AND the expert FFN AND the
+ *     than the four launches, OLMoE shape T = 1 29.4 against 26.7 us per
+ *     step, T = 32 74.8 against 59.8 us): the routing AND the expert FFN AND the
  *     combine in ONE launch.  Its grid is exactly the blocks resident at once;
  *     blocks hand the routing results, h and the pair outputs to each other
  *     through device-scope counters in the workspace (published by the
