@@ -23,10 +23,6 @@
 #include "route_dev.h"
 #include "shared_dev.h"
 
-namespace ffn {
-int cu_count();   // compute units of the current device (expert_ffn.hip)
-}
-
 namespace {
 
 template <int MT>
