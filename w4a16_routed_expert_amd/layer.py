@@ -139,7 +139,10 @@ class RoutedExpertLayer:
         """y = layer(x) through the one-call layer (moe_layer_forward: three or four launches for
         decode batches, no host round trip; mode B.MOE_FFN_PATH_KSPLIT forces the one-launch expert
         FFN of small batches).  rows/lease as for ffn().  With a SharedExpert its FFN runs
-        on a second stream beside the routed work and the combine waits for its event."""
+        on a second stream beside the routed work and the combine waits for its event (for
+        decode batches forward_shared, which runs both on one stream with the shared gate/up
+        pass inside the routing launch, was measured faster: Qwen shape T = 1 40.6 against
+        48.9 us, T = 16 72.5 against 80.4)."""
         T = x.shape[0]
         if T > self.max_T:
             self._alloc(T)
